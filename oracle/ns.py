@@ -1,0 +1,63 @@
+"""Oracle Newton-Schulz: the quintic iteration in float64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+owner_planning page, ``ns_cost_fn``: view the tensor as (rows, cols) =
+(shape[0], product of shape[1:]); normalise it; work on its transpose if rows
+> cols so that rows <= cols; then each step is
+    A = X X^T,   X = a X + (b A + c A A) X
+with scalar coefficients (a, b, c).
+
+Readings taken where the page is silent (each also listed with its reason in
+the design notes):
+  * the normalisation is by the Frobenius norm plus a small epsilon:
+    X0 = X / (||X||_F + eps), so the largest singular value of X0 is <= 1 and a
+    zero matrix stays zero;
+  * the result is transposed back, so the output has the input's shape;
+  * the number of steps defaults to five (``assign_owner_work``'s default
+    cost is Newton-Schulz with five iterations).
+
+Pinned by (tests/test_oracle_ns.py): the SVD closed form X_k = U p^k(S) V^T
+with p(s) = a s + b s^3 + c s^5; rank-1 and orthonormal-rows special cases;
+tall == transpose of wide; zero in, zero out; the cubic (1.5, -0.5, 0)
+converging to the polar factor U V^T; singular values bounded by max p on
+[0, 1].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16), as float64.
+
+    A bf16 value is the top 16 bits of an IEEE binary32 value.
+    Pinned by: hand bit patterns in tests/test_oracle_ns.py.
+    """
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def newton_schulz(g, steps: int, a: float, b: float, c: float, eps: float) -> np.ndarray:
+    """Newton-Schulz orthogonalisation of one tensor, in float64.
+
+    g: array of any shape with ndim >= 2 (values already in float64).
+    Returns a float64 array of g's shape.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    if g.ndim < 2:
+        raise ValueError("Newton-Schulz needs a tensor with at least 2 dims")
+    shape = g.shape
+    x = g.reshape(shape[0], -1)
+    transposed = x.shape[0] > x.shape[1]
+    if transposed:
+        x = x.T
+    x = x / (np.sqrt(np.sum(x * x)) + eps)
+    for _ in range(steps):
+        A = x @ x.T
+        B = b * A + c * (A @ A)
+        x = a * x + B @ x
+    if transposed:
+        x = x.T
+    return np.ascontiguousarray(x).reshape(shape)
