@@ -1,0 +1,261 @@
+"""Throughput of the Newton-Schulz hot path on one MI355X.
+
+One step = the whole path over one batch: select / cost / LPT homes (ns_plan,
+host), pack the row shards into their homes (one HIP launch; the route plan is
+built once and reused, as the pages' cached `plan` dict is), batched 5-step
+quintic Newton-Schulz on the home buffers (norm + 15 product launches), and
+unpack the results into result shards (one HIP launch). Inputs are resident in
+HBM before the timed region.
+
+Default workload: 16 bf16 1024x1024 matrices, N(0, 0.02), stored as 4 uneven
+row shards (one home empty). Other workloads: --workload dense-transformer
+(224 matrices, 32 layers, hidden 4096, ffn 14336) or many-small (3000 random +
+192 MoE matrices).
+
+Prints ONE JSON line. `value` is matrices per second for the whole step.
+`roofline` covers the dominant kernel (the MFMA product kernel): algorithmic
+flops per launch over its average launch time, from HIP events recorded around
+its launches on the launch stream during the timed region.
+`cpu_baseline` times the CPU oracle (plan, pack, fp64 Newton-Schulz, unpack) on
+a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NS matrices/sec + achieved TFLOP/s (% bf16 MFMA peak), 5-step quintic NS"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def alg_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
+    """Algorithmic flops of one matrix: per step SYRK(X) m(m+1)n, SYRK(A) m^2(m+1)
+    (skipped when c == 0), GEMM(B X) 2 m^2 n; symmetric products counted once."""
+    per = m * (m + 1) * n + (m * m * (m + 1) if c_nonzero else 0) + 2 * m * m * n
+    return float(steps) * per
+
+
+def oriented(shape):
+    rows, cols = shape[0], 1
+    for d in shape[1:]:
+        cols *= d
+    return min(rows, cols), max(rows, cols)
+
+
+def build_workload(name: str):
+    from workloads import dense_transformer, even_split_rows, many_small, routed_square_batch
+    if name == "routed-square":
+        ms = routed_square_batch(uneven=True)
+    elif name == "dense-transformer":
+        ms = dense_transformer()
+        ms.split_rows = [even_split_rows(s[0], 4) for s in ms.shapes]
+        ms.num_shards = 4
+    elif name == "many-small":
+        ms = many_small()
+        ms.split_rows = [even_split_rows(s[0], 4) for s in ms.shapes]
+        ms.num_shards = 4
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return ms
+
+
+def make_shards(ms, device_gen: bool):
+    """Shard buffers (device) holding every matrix's row pieces, end to end."""
+    import numpy as np
+    import torch
+    from workloads import device_matrix, host_matrix
+    S = ms.num_shards
+    parts = [[] for _ in range(S)]
+    for i, shape in enumerate(ms.shapes):
+        if device_gen:
+            full = device_matrix(ms.seed, i, shape, std=ms.std)
+        else:
+            bits = host_matrix(ms.seed, i, shape, std=ms.std)
+            full = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        r0 = 0
+        for s in range(S):
+            r = ms.split_rows[i][s]
+            parts[s].append(full[r0:r0 + r].reshape(-1))
+            r0 += r
+    shards = []
+    for s in range(S):
+        shards.append(torch.cat(parts[s]) if parts[s] and sum(p.numel() for p in parts[s]) else None)
+    torch.cuda.synchronize()
+    return shards
+
+
+def cpu_baseline(ms, budget_s: float):
+    """The oracle on a bounded sample: plan, pack, fp64 NS and unpack of the
+    first k matrices (k grows until about budget_s of work)."""
+    import numpy as np
+    from oracle import ns as ons
+    from oracle import planner, route
+    from workloads import host_matrix
+    import threadpoolctl
+
+    a, b, c = (float(np.float32(x)) for x in ms.coeffs)
+    # warm the BLAS so threadpoolctl sees it
+    np.ones((64, 64)) @ np.ones((64, 64))
+    threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()
+                  if p.get("user_api") == "blas") or 1
+    S = ms.num_shards
+    done, t0 = 0, time.perf_counter()
+    elapsed = 0.0
+    while done < ms.n and (elapsed < budget_s or done == 0):
+        i = done
+        shape = ms.shapes[i]
+        split = [ms.split_rows[i]]
+        full = host_matrix(ms.seed, i, shape, std=ms.std)
+        shards = np.split(full, np.cumsum(split[0])[:-1], axis=0)
+        shards = [x.ravel() for x in shards]
+        t_start = time.perf_counter()
+        p = planner.plan([shape], ms.steps, S, split)
+        homes = route.pack(shards, [shape], split, p["home"], S)
+        x = ons.bf16_bits_to_f64(homes[p["home"][0]]).reshape(shape)
+        y = ons.newton_schulz(x, ms.steps, a, b, c, 1e-7)
+        res = [np.zeros(0)] * S
+        res[p["home"][0]] = y.ravel()
+        route.unpack(res, [shape], split, p["home"], S)
+        elapsed += time.perf_counter() - t_start
+        done += 1
+    total = time.perf_counter() - t0
+    return {"value": done / elapsed, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {ms.n} matrices of the workload through oracle plan + pack + "
+                      f"fp64 NS ({ms.steps} steps) + unpack, {elapsed:.1f} s of work ({total:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="routed-square",
+                    choices=["routed-square", "dense-transformer", "many-small"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the HIP-event timing of the product kernel")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no cross-GPU "
+              "part in this build; how it would shard is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_quintic_amd as nsq
+
+    if not os.path.exists(nsq.LIB_PATH):
+        from newton_schulz_quintic_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms = build_workload(args.workload)
+    S = ms.num_shards
+    big = args.workload != "routed-square"
+    shards_in = make_shards(ms, device_gen=big)
+
+    # route plan: built once, reused every step
+    p = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
+    plan = nsq.ns_route_plan_create(ms.shapes, S, ms.split_rows, p["home"], 2)
+    q = nsq.ns_route_plan_query(plan)
+    nsq.ns_route_plan_upload(plan)
+    homes = [torch.empty(n, dtype=torch.bfloat16, device=dev) if n else None for n in q["home_elems"]]
+    shards_out = [torch.empty(n, dtype=torch.bfloat16, device=dev) if n else None
+                  for n in q["shard_elems"]]
+    views = []
+    for i, shape in enumerate(ms.shapes):
+        h, off = p["home"][i], q["home_offset"][i]
+        numel = 1
+        for d in shape:
+            numel *= d
+        views.append(homes[h][off:off + numel].view(shape))
+    need, _ = nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        pl = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
+        nsq.ns_pack_shards(plan, shards_in, homes, stream)
+        nsq.ns_orthogonalize_batched(views, views, steps=ms.steps, coeffs=ms.coeffs, order=pl["order"],
+                                     workspace=workspace, stream=stream)
+        nsq.ns_unpack_shards(plan, homes, shards_out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for k in range(3):
+        nsq.ns_timing_read(k)           # drop anything recorded before the timed region
+    if not args.no_kernel_timing:
+        nsq.ns_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nsq.ns_timing_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    flops = sum(alg_flops(*oriented(s), ms.steps, ms.coeffs[2] != 0.0) for s in ms.shapes)
+    dense = sum(ms.steps * (4 * m * m * n + 2 * m ** 3) for m, n in (oriented(s) for s in ms.shapes))
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(ms.n / (ms_step * 1e-3), 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ms.name, "matrices": ms.n, "distinct_shapes": len(set(ms.shapes)),
+                   "shards": S, "ns_steps": ms.steps, "coeffs": list(ms.coeffs),
+                   "homes_used": len(set(p["home"]))},
+        "tflops": round(tflops, 2),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "alg_flops_per_step": flops,
+        "dense_equiv_flops_per_step": float(dense),
+    }
+    if not args.no_kernel_timing:
+        kms, kn, kwork = nsq.ns_timing_read(0)
+        rms, rn, rwork = nsq.ns_timing_read(1)
+        nms, nn, nwork = nsq.ns_timing_read(2)
+        if kn:
+            achieved = (kwork / kn) / (kms / kn * 1e-3) / 1e12
+            out["roofline"] = {"kernel": "ns_product_kernel<bf16>", "bound": "mfma",
+                               "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                               "traffic": None, "avg_launch_us": round(kms / kn * 1e3, 2),
+                               "alg_flops_per_launch": kwork / kn, "launches": kn}
+        if rn:
+            gbs = (rwork / rn) / (rms / rn * 1e-3) / 1e9
+            out["route_kernel"] = {"kernel": "route_copy_kernel", "bound": "hbm",
+                                   "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "avg_launch_us": round(rms / rn * 1e3, 2),
+                                   "bytes_per_launch": rwork / rn,
+                                   "note": "working set fits the 256 MB MALL" if rwork / rn < 256e6
+                                   else "working set exceeds the MALL"}
+        if nn:
+            out["norm_kernels"] = {"avg_us": round(nms / nn * 1e3, 2), "bytes": nwork / nn}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(ms, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

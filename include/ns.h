@@ -1,0 +1,224 @@
+/*
+ * ns.h -- C ABI of the MI355X (gfx950) Newton-Schulz library.
+ *
+ * One GPU. Plain pointers and sizes; no C++ or torch types. Every call returns
+ * an ns_status (0 = NS_OK, negative = error). On error nothing has been
+ * enqueued on the stream and no output has been written; ns_last_error()
+ * returns a message for the calling thread's last failure.
+ *
+ * Memory: the library never allocates device memory. Every device buffer (shard
+ * buffers, home buffers, the route plan's device table, the Newton-Schulz
+ * workspace, inputs and outputs) belongs to the caller. Device pointers must
+ * stay valid until the work enqueued on the stream has finished.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * Work is enqueued asynchronously in stream order; calls do not synchronise
+ * the host unless stated.
+ *
+ * Pages cited (by title, then section):
+ *   [owner_planning] "core.distributed.fsdp.src.megatron_fsdp.experimental.
+ *                     owner_planning" (Megatron-FSDP API docs)
+ *   [layer_sharded]  "core.optimizer.layer_sharded_a2a" (Megatron Core API docs)
+ *   [issue]          "[GTP][Muon] Optimize Muon step performance" (GitHub issue)
+ */
+#ifndef NS_MI355X_NS_H
+#define NS_MI355X_NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ns_status;
+
+#define NS_OK                 0
+#define NS_ERR_INVALID_ARG   -1  /* null pointer, negative size, bad shape, bad order, ...   */
+#define NS_ERR_NO_CANDIDATE  -2  /* a participating tensor has no rows in any shard          */
+#define NS_ERR_HOME_RANGE    -3  /* a home index outside [0, num_shards)                     */
+#define NS_ERR_SPLIT_SUM     -4  /* a tensor's split rows do not sum to its first dimension  */
+#define NS_ERR_OVERFLOW      -5  /* a size, offset or cost does not fit in 63 / 64 bits      */
+#define NS_ERR_PLAN_MISMATCH -6  /* a route plan used with buffers it was not built for      */
+#define NS_ERR_WORKSPACE     -7  /* workspace too small (or its table not uploaded)          */
+#define NS_ERR_DTYPE         -8  /* unsupported dtype or element size                        */
+#define NS_ERR_HIP           -9  /* a HIP runtime call failed (message names it)             */
+
+#define NS_MAX_DIMS   8
+#define NS_MAX_SHARDS 64
+
+/* Thread-local message describing the calling thread's last failed call.
+ * Never NULL; empty if no call on this thread has failed. */
+const char *ns_last_error(void);
+
+/* A tensor's full shape. It is viewed as a matrix (rows, cols) =
+ * (dims[0], dims[1] * ... * dims[ndim-1]), row-major and contiguous
+ * [owner_planning, ns_cost_fn]. Tensors with ndim < 2 do not take part
+ * [owner_planning, select_ge_2d_params]. */
+typedef struct ns_shape {
+    int32_t ndim;                 /* 0 .. NS_MAX_DIMS */
+    int64_t dims[NS_MAX_DIMS];    /* dims[d] >= 0 for d < ndim; the rest ignored */
+} ns_shape;
+
+typedef enum ns_dtype { NS_BF16 = 0, NS_F32 = 1 } ns_dtype;
+
+/* ------------------------------------------------------------------------ *
+ * Planning (host only; no GPU needed)
+ * ------------------------------------------------------------------------ */
+
+/* Cost estimate and owner ("home") assignment for n tensors over num_homes
+ * homes [owner_planning, ns_cost_fn and assign_owner_work].
+ *
+ * cost[i]  = rows * cols * (min(rows, cols) * steps + 1), exact in uint64
+ *            (NS_ERR_OVERFLOW if it does not fit).
+ * Candidates of tensor i: the homes s with split_rows[i*num_homes + s] > 0, in
+ * ascending s (buffer order); every home if split_rows is NULL.
+ * Assignment (LPT): tensors with a single candidate first, in index order; then
+ * the others by descending cost (ties: ascending index); each goes to its
+ * least-loaded candidate, ties to the first candidate in buffer order.
+ *
+ * n            number of tensors (>= 0); shapes: [n] (may be NULL iff n == 0).
+ * steps        Newton-Schulz steps in the cost (>= 0).
+ * num_homes    1 .. NS_MAX_SHARDS.
+ * split_rows   [n * num_homes] rows of tensor i held by shard s, each row of the
+ *              table summing to dims[0]; or NULL.
+ * cost_out     [n] or NULL: cost per tensor (0 for tensors with ndim < 2).
+ * home_out     [n] (required): home per tensor, -1 for tensors with ndim < 2.
+ * load_out     [num_homes] or NULL: summed cost per home.
+ * order_out    [n] or NULL: participating tensors in assignment order, then -1
+ *              for the entries left over.
+ * Errors: INVALID_ARG, SPLIT_SUM, NO_CANDIDATE, OVERFLOW. Outputs untouched on error. */
+ns_status ns_plan(int32_t n, const ns_shape *shapes, int32_t steps, int32_t num_homes,
+                  const int64_t *split_rows, uint64_t *cost_out, int32_t *home_out,
+                  uint64_t *load_out, int32_t *order_out);
+
+/* ------------------------------------------------------------------------ *
+ * Routing: S simulated row-shard buffers <-> S home buffers on one GPU
+ * [layer_sharded, route_to_ns_home / route_from_ns_home / params_by_home;
+ *  owner_planning, OwnerGatherPlan / OwnerScatterPlan]
+ * ------------------------------------------------------------------------ */
+
+/* Immutable, host-side description of one routing: the offsets of every piece
+ * in the shard and home buffers. It is a pure function of (shapes, split_rows,
+ * home, num_shards, elem_bytes), built once and reused while those are unchanged
+ * [layer_sharded, route_to_ns_home `plan` argument]. The caller owns it.
+ *
+ * Layouts (flat, row-major, contiguous, in elements):
+ *  - shard buffer s: for every tensor i in increasing index order, the
+ *    split_rows[i][s] rows of tensor i that shard s holds, end to end. Shard s
+ *    holds the rows starting at sum_{s' < s} split_rows[i][s'] (shards split a
+ *    tensor in buffer order).
+ *  - home buffer h: the complete tensors i with home[i] == h, in increasing
+ *    index order [layer_sharded, params_by_home]; empty homes hold nothing.
+ * Tensors must have ndim >= 2 (view (rows, cols) as above); zero-size tensors
+ * and zero-row splits are allowed. */
+typedef struct ns_route_plan ns_route_plan;
+
+/* n >= 0 tensors; num_shards 1 .. NS_MAX_SHARDS; split_rows [n * num_shards]
+ * (each row sums to dims[0]); home [n] in [0, num_shards); elem_bytes 2 or 4.
+ * *out receives a new plan (release with ns_route_plan_destroy).
+ * Errors: INVALID_ARG, SPLIT_SUM, HOME_RANGE, OVERFLOW, DTYPE. */
+ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int32_t num_shards,
+                               const int64_t *split_rows, const int32_t *home,
+                               int32_t elem_bytes, ns_route_plan **out);
+
+/* Any output pointer may be NULL.
+ * shard_elems [S], home_elems [S]: buffer sizes in elements.
+ * home_offset [n]: element offset of tensor i in its home buffer.
+ * shard_offset [n * S]: element offset of tensor i's piece in shard buffer s.
+ * device_table_bytes: size of the device table ns_route_plan_upload writes.
+ * fingerprint: 64-bit hash of everything the plan was built from. */
+ns_status ns_route_plan_query(const ns_route_plan *plan, int64_t *shard_elems,
+                              int64_t *home_elems, int64_t *home_offset,
+                              int64_t *shard_offset, size_t *device_table_bytes,
+                              uint64_t *fingerprint);
+
+/* Copy the plan's segment table to caller-owned device memory of at least
+ * device_table_bytes (16-byte aligned), on `stream`, and wait for the copy.
+ * Must be called once before pack/unpack; the plan remembers the address. */
+ns_status ns_route_plan_upload(ns_route_plan *plan, void *device_table, void *stream);
+
+/* Release a plan (NULL is a no-op). Work already enqueued keeps running. */
+void ns_route_plan_destroy(ns_route_plan *plan);
+
+/* Forward routing (gather): for every tensor i, concatenate its row pieces from
+ * shard buffers 0..S-1 (buffer order) into its slot in home buffer home[i]
+ * [owner_planning, OwnerGatherPlan.reconstruct_full; layer_sharded,
+ * route_to_ns_home]. Bit copy. shard_bufs [S] and home_bufs [S] are arrays of
+ * device pointers of num_shards entries; an entry may be NULL only if that
+ * buffer has zero elements. Buffers must not overlap. One kernel launch.
+ * Errors: INVALID_ARG, PLAN_MISMATCH (plan not uploaded), HIP. */
+ns_status ns_pack_shards(const ns_route_plan *plan, const void *const *shard_bufs,
+                         void *const *home_bufs, void *stream);
+
+/* Backward routing (scatter): the inverse of ns_pack_shards on the same plan;
+ * every shard buffer receives its rows of every tensor back from the home
+ * buffers [owner_planning, OwnerScatterPlan.unpack; layer_sharded,
+ * route_from_ns_home]. Same conventions as ns_pack_shards. */
+ns_status ns_unpack_shards(const ns_route_plan *plan, const void *const *home_bufs,
+                           void *const *shard_bufs, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Newton-Schulz orthogonalisation [owner_planning, ns_cost_fn;
+ * issue, "Current Progress": shape-batched NS, SYRK symmetric kernels]
+ * ------------------------------------------------------------------------ */
+
+/* Device workspace (bytes) that lets ns_orthogonalize_batched run all n
+ * tensors at once. A smaller workspace is accepted down to the amount needed
+ * for the largest single tensor; tensors are then processed in consecutive
+ * groups that fit (results are identical). *min_bytes (may be NULL) receives
+ * that minimum. Errors: INVALID_ARG, DTYPE, OVERFLOW. */
+ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
+                             size_t *bytes, size_t *min_bytes);
+
+/* For every tensor i with ndim >= 2 and numel > 0: view it as (rows, cols);
+ * if rows > cols work on its transpose so that m = min <= n = max; normalise
+ * X0 = G / (||G||_F + eps); run `steps` steps of
+ *     A = X X^T,  B = b A + c A A,  X = a X + B X
+ * and write X (transposed back if it was transposed) to out[i] in the input's
+ * shape and dtype [owner_planning, ns_cost_fn].
+ *
+ * Precision: bf16 tensors keep X, A and B in bf16 between products; every
+ * product runs on bf16 MFMA with fp32 accumulation, and the norm and the
+ * epilogues (b A + c (A A), a X + B X) are computed in fp32 and rounded once
+ * (round to nearest even). f32 tensors keep everything in fp32 (f32 MFMA).
+ *
+ * in[i], out[i]   device pointers, contiguous row-major, 2-byte (bf16) or
+ *                 4-byte (f32) aligned; out[i] may equal in[i]; distinct outputs
+ *                 must not overlap. Entries of tensors with numel == 0 or
+ *                 ndim < 2 are ignored (and may be NULL).
+ * steps >= 0; a, b, c: coefficients (quintic 3.4445, -4.7750, 2.0315); eps >= 0.
+ * order   [n] permutation of 0..n-1 giving the dispatch order (e.g. ns_plan's
+ *         order), or NULL for descending cost. Results do not depend on it.
+ * workspace/workspace_bytes  device memory, 256-byte aligned, at least the
+ *         minimum from ns_workspace_bytes.
+ * Errors: INVALID_ARG, DTYPE, WORKSPACE, OVERFLOW, HIP. */
+ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
+                                   const void *const *in, void *const *out, ns_dtype dtype,
+                                   int32_t steps, float a, float b, float c, float eps,
+                                   const int32_t *order, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Measurement support
+ * ------------------------------------------------------------------------ */
+
+/* Kernel timing: while enabled, the library records a HIP event pair on the
+ * launch stream around every launch of its matrix-product kernel, and of its
+ * pack/unpack kernel. ns_timing_read waits for those events, returns the sums
+ * and clears them. Not thread-safe against concurrent batched calls.
+ * kind: 0 = matrix-product kernel, 1 = pack/unpack kernel, 2 = norm kernels.
+ * total_ms: summed durations; launches: number of launches; work: summed
+ * algorithmic work of those launches (flops for kind 0, bytes moved for kind 1,
+ * bytes read + written for kind 2). */
+ns_status ns_timing_enable(int32_t enable);
+ns_status ns_timing_read(int32_t kind, double *total_ms, int64_t *launches, double *work);
+
+/* Library version string. */
+const char *ns_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NS_MI355X_NS_H */

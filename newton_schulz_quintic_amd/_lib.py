@@ -1,0 +1,291 @@
+"""ctypes binding of ``include/ns.h``: argument marshalling only.
+
+Python functions carry the C entry points' names. Torch supplies device memory
+(tensors) and streams; every step of the path runs in the HIP library. The
+library is loaded on first use and a missing build raises ``NSLibraryMissing``
+(there is no fallback of any kind).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsq.so")
+
+NS_BF16, NS_F32 = 0, 1
+NS_MAX_DIMS, NS_MAX_SHARDS = 8, 64
+STATUS = {
+    0: "NS_OK", -1: "NS_ERR_INVALID_ARG", -2: "NS_ERR_NO_CANDIDATE", -3: "NS_ERR_HOME_RANGE",
+    -4: "NS_ERR_SPLIT_SUM", -5: "NS_ERR_OVERFLOW", -6: "NS_ERR_PLAN_MISMATCH",
+    -7: "NS_ERR_WORKSPACE", -8: "NS_ERR_DTYPE", -9: "NS_ERR_HIP",
+}
+EXPORTS = [
+    "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_query",
+    "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
+    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_timing_enable", "ns_timing_read",
+]
+
+
+class NSLibraryMissing(ImportError):
+    pass
+
+
+class NSError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class ns_shape(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("dims", ctypes.c_int64 * NS_MAX_DIMS)]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _U64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "ns_last_error": (ctypes.c_char_p, []),
+    "ns_version": (ctypes.c_char_p, []),
+    "ns_plan": (_I32, [_I32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "ns_route_plan_create": (_I32, [_I32, _P, _I32, _P, _P, _I32, ctypes.POINTER(_P)]),
+    "ns_route_plan_query": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
+    "ns_route_plan_upload": (_I32, [_P, _P, _P]),
+    "ns_route_plan_destroy": (None, [_P]),
+    "ns_pack_shards": (_I32, [_P, _P, _P, _P]),
+    "ns_unpack_shards": (_I32, [_P, _P, _P, _P]),
+    "ns_workspace_bytes": (_I32, [_I32, _P, _I32, _P, _P]),
+    "ns_orthogonalize_batched": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P,
+                                        _SZ, _P]),
+    "ns_timing_enable": (_I32, [_I32]),
+    "ns_timing_read": (_I32, [_I32, _P, _P, _P]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises NSLibraryMissing if it was never built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise NSLibraryMissing(
+                    f"{LIB_PATH} not found: build it with `python -m newton_schulz_quintic_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+        return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise NSError(status, lib().ns_last_error().decode())
+
+
+def _shapes(shapes):
+    arr = (ns_shape * max(1, len(shapes)))()
+    for i, s in enumerate(shapes):
+        s = tuple(int(d) for d in s)
+        if len(s) > NS_MAX_DIMS:
+            raise ValueError(f"shape {s} has more than {NS_MAX_DIMS} dims")
+        arr[i].ndim = len(s)
+        for d, v in enumerate(s):
+            arr[i].dims[d] = v
+    return arr
+
+
+def _arr(ctype, values):
+    values = list(values)
+    return (ctype * max(1, len(values)))(*values)
+
+
+def _addr(x) -> int:
+    return ctypes.addressof(x)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def ns_last_error() -> str:
+    return lib().ns_last_error().decode()
+
+
+def ns_version() -> str:
+    return lib().ns_version().decode()
+
+
+def ns_plan(shapes, steps: int = 5, num_homes: int = 1, split_rows=None) -> dict:
+    """Costs and LPT homes; see ns.h. Returns dict(cost, home, load, order)."""
+    n = len(shapes)
+    sh = _shapes(shapes)
+    split = None
+    if split_rows is not None:
+        flat = [int(r) for row in split_rows for r in row]
+        if len(flat) != n * num_homes:
+            raise ValueError("split_rows must be n x num_homes")
+        split = _arr(_I64, flat)
+    cost, home, load, order = (_arr(_U64, [0] * n), _arr(_I32, [0] * n), _arr(_U64, [0] * num_homes),
+                               _arr(_I32, [0] * n))
+    _check(lib().ns_plan(n, _addr(sh), steps, num_homes, None if split is None else _addr(split),
+                         _addr(cost), _addr(home), _addr(load), _addr(order)))
+    return {"cost": list(cost)[:n], "home": list(home)[:n], "load": list(load)[:num_homes],
+            "order": [i for i in list(order)[:n] if i >= 0]}
+
+
+class RoutePlan:
+    """Owns an ns_route_plan handle (destroyed with the object)."""
+
+    def __init__(self, handle: int, n: int, num_shards: int, elem_bytes: int):
+        self.handle = handle
+        self.n, self.num_shards, self.elem_bytes = n, num_shards, elem_bytes
+        self.device_table = None
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.ns_route_plan_destroy(self.handle)
+            self.handle = None
+
+
+def ns_route_plan_create(shapes, num_shards: int, split_rows, home, elem_bytes: int) -> RoutePlan:
+    n = len(shapes)
+    sh = _shapes(shapes)
+    flat = [int(r) for row in split_rows for r in row]
+    if len(flat) != n * num_shards:
+        raise ValueError("split_rows must be n x num_shards")
+    out = _P()
+    split, homes = _arr(_I64, flat), _arr(_I32, home)     # held alive across the call
+    _check(lib().ns_route_plan_create(n, _addr(sh), num_shards, _addr(split), _addr(homes),
+                                      elem_bytes, ctypes.byref(out)))
+    return RoutePlan(out.value, n, num_shards, elem_bytes)
+
+
+def ns_route_plan_query(plan: RoutePlan) -> dict:
+    S, n = plan.num_shards, plan.n
+    se, he = _arr(_I64, [0] * S), _arr(_I64, [0] * S)
+    ho, so = _arr(_I64, [0] * n), _arr(_I64, [0] * (n * S))
+    tb, fp = _SZ(0), _U64(0)
+    _check(lib().ns_route_plan_query(plan.handle, _addr(se), _addr(he), _addr(ho), _addr(so),
+                                     ctypes.addressof(tb), ctypes.addressof(fp)))
+    so_l = list(so)[:n * S]
+    return {"shard_elems": list(se)[:S], "home_elems": list(he)[:S], "home_offset": list(ho)[:n],
+            "shard_offset": [so_l[i * S:(i + 1) * S] for i in range(n)],
+            "device_table_bytes": tb.value, "fingerprint": fp.value}
+
+
+def ns_route_plan_upload(plan: RoutePlan, device_table=None, stream=None):
+    """Upload the plan's table. Allocates a torch uint8 device tensor if none is given."""
+    if device_table is None:
+        import torch
+        nbytes = ns_route_plan_query(plan)["device_table_bytes"]
+        device_table = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    _check(lib().ns_route_plan_upload(plan.handle, device_table.data_ptr(), _stream(stream)))
+    plan.device_table = device_table     # keep the memory alive with the plan
+    return device_table
+
+
+def ns_route_plan_destroy(plan: RoutePlan) -> None:
+    if plan.handle:
+        lib().ns_route_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def _ptr_array(bufs, S):
+    if len(bufs) != S:
+        raise ValueError(f"expected {S} buffers")
+    return _arr(_P, [_ptr(b) for b in bufs])
+
+
+def ns_pack_shards(plan: RoutePlan, shard_bufs, home_bufs, stream=None) -> None:
+    src, dst = _ptr_array(shard_bufs, plan.num_shards), _ptr_array(home_bufs, plan.num_shards)
+    _check(lib().ns_pack_shards(plan.handle, _addr(src), _addr(dst), _stream(stream)))
+
+
+def ns_unpack_shards(plan: RoutePlan, home_bufs, shard_bufs, stream=None) -> None:
+    src, dst = _ptr_array(home_bufs, plan.num_shards), _ptr_array(shard_bufs, plan.num_shards)
+    _check(lib().ns_unpack_shards(plan.handle, _addr(src), _addr(dst), _stream(stream)))
+
+
+def ns_workspace_bytes(shapes, dtype: int) -> tuple[int, int]:
+    sh = _shapes(shapes)
+    b, mb = _SZ(0), _SZ(0)
+    _check(lib().ns_workspace_bytes(len(shapes), _addr(sh), dtype, ctypes.addressof(b),
+                                    ctypes.addressof(mb)))
+    return b.value, mb.value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return NS_BF16
+    if t.dtype == torch.float32:
+        return NS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315),
+                             eps: float = 1e-7, order=None, workspace=None, stream=None):
+    """Newton-Schulz on every tensor of ``inputs`` into ``outputs`` (see ns.h).
+
+    Tensors: contiguous, same dtype (bf16 or f32), on the current GPU. The
+    workspace (uint8 device tensor) is allocated with torch if not given.
+    Returns the workspace so callers can reuse it.
+    """
+    n = len(inputs)
+    if len(outputs) != n:
+        raise ValueError("inputs and outputs differ in length")
+    if n == 0:
+        return workspace
+    dtype = _dtype_code(inputs[0])
+    for x, y in zip(inputs, outputs):
+        if _dtype_code(x) != dtype or _dtype_code(y) != dtype:
+            raise TypeError("all tensors must share one dtype")
+        if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+            raise ValueError("tensors must be contiguous and outputs shaped like inputs")
+    shapes = [tuple(x.shape) for x in inputs]
+    if workspace is None:
+        import torch
+        need, _ = ns_workspace_bytes(shapes, dtype)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+    a, b, c = coeffs
+    sh = _shapes(shapes)
+    ins = _arr(_P, [x.data_ptr() for x in inputs])
+    outs = _arr(_P, [y.data_ptr() for y in outputs])
+    ord_arr = None if order is None else _arr(_I32, order)   # held alive across the call
+    _check(lib().ns_orthogonalize_batched(n, _addr(sh), _addr(ins), _addr(outs), dtype, steps,
+                                          float(a), float(b), float(c), float(eps),
+                                          None if ord_arr is None else _addr(ord_arr),
+                                          workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ns_timing_enable(enable: bool) -> None:
+    _check(lib().ns_timing_enable(1 if enable else 0))
+
+
+def ns_timing_read(kind: int) -> tuple[float, int, float]:
+    """(total_ms, launches, work) for kind 0 = products, 1 = pack/unpack, 2 = norm."""
+    ms, cnt, work = ctypes.c_double(0), _I64(0), ctypes.c_double(0)
+    _check(lib().ns_timing_read(kind, ctypes.addressof(ms), ctypes.addressof(cnt),
+                                ctypes.addressof(work)))
+    return ms.value, cnt.value, work.value

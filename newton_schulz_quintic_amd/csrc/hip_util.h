@@ -1,0 +1,34 @@
+// HIP helpers shared by the library's kernels and entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace nsq {
+
+#define NSQ_HIP(call)                                                                    \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess)                                                            \
+            return ::nsq::fail(NS_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// Kernel timing (see ns_timing_enable): a scope that records a HIP event pair
+// around the launches made while it is alive, when timing is enabled.
+enum TimingKind { kTimeProduct = 0, kTimeRoute = 1, kTimeNorm = 2, kTimeKinds = 3 };
+
+bool timing_enabled();
+// Returns an opaque slot (or -1 when timing is off). `work` is the algorithmic
+// work the bracketed launches perform (flops or bytes).
+int timing_start(int kind, hipStream_t stream, double work);
+void timing_stop(int slot, hipStream_t stream);
+
+struct TimedScope {
+    int slot;
+    hipStream_t stream;
+    TimedScope(int kind, hipStream_t s, double work) : slot(timing_start(kind, s, work)), stream(s) {}
+    ~TimedScope() { timing_stop(slot, stream); }
+};
+
+}  // namespace nsq

@@ -1,0 +1,49 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "ns.h"
+
+namespace nsq {
+
+// Records a message for ns_last_error() and returns `code`.
+ns_status fail(ns_status code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// (rows, cols) view of a shape, with overflow and sign checks.
+// Returns NS_OK, NS_ERR_INVALID_ARG or NS_ERR_OVERFLOW (message set).
+ns_status matrix_view(const ns_shape &s, int64_t idx, int64_t *rows, int64_t *cols);
+
+// One contiguous piece moved by pack/unpack: `len` bytes between shard buffer
+// `shard` at byte `shard_off` and home buffer `home` at byte `home_off`.
+// Chunks of kRouteChunkBytes are numbered globally; this piece owns chunks
+// [chunk_begin, chunk_begin + ceil(len / kRouteChunkBytes)).
+struct RouteSeg {
+    int64_t shard_off;
+    int64_t home_off;
+    int64_t len;
+    int64_t chunk_begin;
+    int32_t shard;
+    int32_t home;
+    int64_t pad;
+};
+static_assert(sizeof(RouteSeg) == 48, "RouteSeg layout");
+
+constexpr int64_t kRouteChunkBytes = 16384;
+
+}  // namespace nsq
+
+struct ns_route_plan {
+    int32_t n = 0;
+    int32_t num_shards = 0;
+    int32_t elem_bytes = 0;
+    std::vector<int64_t> shard_elems, home_elems, home_offset, shard_offset;
+    std::vector<nsq::RouteSeg> segs;
+    int64_t total_chunks = 0;
+    int64_t total_bytes = 0;
+    uint64_t fingerprint = 0;
+    void *device_table = nullptr;
+};

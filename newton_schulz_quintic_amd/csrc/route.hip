@@ -1,0 +1,150 @@
+// Pack / unpack: move the row pieces of every tensor between the S shard
+// buffers and the S home buffers of one GPU, as laid out by the route plan.
+//
+// "core.optimizer.layer_sharded_a2a": route_to_ns_home gathers each param's
+// row shards into the complete matrix at its home, route_from_ns_home scatters
+// the results back. "...owner_planning": OwnerGatherPlan.reconstruct_full
+// concatenates per-rank shards in buffer order; OwnerScatterPlan.unpack
+// extracts each rank's flat result shard.
+//
+// One launch moves every piece. The pieces are cut into 16 KiB chunks numbered
+// globally; a workgroup takes chunks in a grid-stride loop, finds the piece by
+// binary search over the pieces' first chunk numbers, and copies the chunk with
+// 16-byte loads and stores when both ends are 16-byte aligned (narrower
+// accesses otherwise). HBM-bound: every byte is read once and written once.
+
+#include "hip_util.h"
+
+namespace nsq {
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteMaxGrid = 8192;
+
+struct PtrSet {
+    char *p[NS_MAX_SHARDS];
+};
+
+__device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict__ dst, int64_t len) {
+    const int t = threadIdx.x;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+    if ((mis & 15) == 0) {
+        const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+        uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+        const int64_t n16 = len >> 4;
+        if (n16 == kRouteChunkBytes / 16) {
+            // full chunk: 4 loads in flight per thread before the stores
+            uint4 v0 = s4[t], v1 = s4[t + 256], v2 = s4[t + 512], v3 = s4[t + 768];
+            d4[t] = v0;
+            d4[t + 256] = v1;
+            d4[t + 512] = v2;
+            d4[t + 768] = v3;
+        } else {
+            for (int64_t i = t; i < n16; i += kRouteThreads) d4[i] = s4[i];
+        }
+        for (int64_t i = (n16 << 4) + 2 * t; i < len; i += 2 * kRouteThreads)
+            *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
+    } else if ((mis & 3) == 0) {
+        const int64_t n4 = len >> 2;
+        for (int64_t i = t; i < n4; i += kRouteThreads)
+            reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(src)[i];
+        for (int64_t i = (n4 << 2) + 2 * t; i < len; i += 2 * kRouteThreads)
+            *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
+    } else {
+        for (int64_t i = 2 * t; i < len; i += 2 * kRouteThreads)
+            *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
+    }
+}
+
+// to_home = 1: shard -> home (pack); 0: home -> shard (unpack).
+__global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSeg *__restrict__ segs,
+                                                                   int32_t nseg, int64_t total_chunks,
+                                                                   PtrSet shard, PtrSet home,
+                                                                   int32_t to_home) {
+    for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
+        int32_t lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (segs[mid].chunk_begin <= c)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const RouteSeg g = segs[lo];
+        const int64_t off = (c - g.chunk_begin) * kRouteChunkBytes;
+        const int64_t rem = g.len - off;
+        const int64_t len = rem < kRouteChunkBytes ? rem : kRouteChunkBytes;
+        char *sp = shard.p[g.shard] + g.shard_off + off;
+        char *hp = home.p[g.home] + g.home_off + off;
+        if (to_home)
+            copy_chunk(sp, hp, len);
+        else
+            copy_chunk(hp, sp, len);
+    }
+}
+
+ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
+                       const void *const *home_bufs, int32_t to_home, void *stream) {
+    if (!plan) return fail(NS_ERR_INVALID_ARG, "plan is NULL");
+    if (!plan->device_table && !plan->segs.empty())
+        return fail(NS_ERR_PLAN_MISMATCH, "route plan not uploaded (call ns_route_plan_upload)");
+    const int32_t S = plan->num_shards;
+    if (S > 0 && (!shard_bufs || !home_bufs))
+        return fail(NS_ERR_INVALID_ARG, "buffer pointer arrays are required");
+    PtrSet sh{}, ho{};
+    for (int32_t s = 0; s < S; ++s) {
+        if (!shard_bufs[s] && plan->shard_elems[s] > 0)
+            return fail(NS_ERR_INVALID_ARG, "shard buffer %d is NULL but holds %lld elements", s,
+                        (long long)plan->shard_elems[s]);
+        if (!home_bufs[s] && plan->home_elems[s] > 0)
+            return fail(NS_ERR_INVALID_ARG, "home buffer %d is NULL but holds %lld elements", s,
+                        (long long)plan->home_elems[s]);
+        const uintptr_t align = (uintptr_t)shard_bufs[s] | (uintptr_t)home_bufs[s];
+        if (align % plan->elem_bytes)
+            return fail(NS_ERR_INVALID_ARG, "buffers of shard/home %d not %d-byte aligned", s,
+                        plan->elem_bytes);
+        sh.p[s] = (char *)shard_bufs[s];
+        ho.p[s] = (char *)home_bufs[s];
+    }
+    if (plan->segs.empty()) return NS_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t grid = plan->total_chunks < kRouteMaxGrid ? plan->total_chunks : kRouteMaxGrid;
+    {
+        TimedScope ts(kTimeRoute, st, 2.0 * (double)plan->total_bytes);
+        hipLaunchKernelGGL(route_copy_kernel, dim3((unsigned)grid), dim3(kRouteThreads), 0, st,
+                           reinterpret_cast<const RouteSeg *>(plan->device_table),
+                           (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
+    }
+    NSQ_HIP(hipGetLastError());
+    return NS_OK;
+}
+
+}  // namespace
+}  // namespace nsq
+
+using namespace nsq;
+
+extern "C" ns_status ns_route_plan_upload(ns_route_plan *plan, void *device_table, void *stream) {
+    if (!plan) return fail(NS_ERR_INVALID_ARG, "plan is NULL");
+    if (!device_table) return fail(NS_ERR_INVALID_ARG, "device_table is NULL");
+    if (reinterpret_cast<uintptr_t>(device_table) % 16)
+        return fail(NS_ERR_INVALID_ARG, "device_table must be 16-byte aligned");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!plan->segs.empty()) {
+        NSQ_HIP(hipMemcpyAsync(device_table, plan->segs.data(), plan->segs.size() * sizeof(RouteSeg),
+                               hipMemcpyHostToDevice, st));
+        NSQ_HIP(hipStreamSynchronize(st));
+    }
+    plan->device_table = device_table;
+    return NS_OK;
+}
+
+extern "C" ns_status ns_pack_shards(const ns_route_plan *plan, const void *const *shard_bufs,
+                                    void *const *home_bufs, void *stream) {
+    return route_launch(plan, shard_bufs, const_cast<const void *const *>(home_bufs), 1, stream);
+}
+
+extern "C" ns_status ns_unpack_shards(const ns_route_plan *plan, const void *const *home_bufs,
+                                      void *const *shard_bufs, void *stream) {
+    return route_launch(plan, const_cast<const void *const *>(shard_bufs), home_bufs, 0, stream);
+}

@@ -1,0 +1,96 @@
+// Kernel timing hooks (ns_timing_enable / ns_timing_read): HIP event pairs
+// recorded on the launch stream around the library's own kernel launches.
+
+#include <mutex>
+#include <vector>
+
+#include "hip_util.h"
+
+namespace nsq {
+
+namespace {
+struct Rec {
+    hipEvent_t start, stop;
+    int kind;
+    double work;
+    bool closed;
+};
+std::mutex g_mu;
+bool g_enabled = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+bool timing_enabled() {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return g_enabled;
+}
+
+int timing_start(int kind, hipStream_t stream, double work) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_enabled) return -1;
+    Rec r{take_event(), take_event(), kind, work, false};
+    if (!r.start || !r.stop) return -1;
+    if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
+    g_recs.push_back(r);
+    return (int)g_recs.size() - 1;
+}
+
+void timing_stop(int slot, hipStream_t stream) {
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (slot >= (int)g_recs.size()) return;
+    if (hipEventRecord(g_recs[slot].stop, stream) == hipSuccess) g_recs[slot].closed = true;
+}
+
+}  // namespace nsq
+
+using namespace nsq;
+
+extern "C" ns_status ns_timing_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_enabled = enable != 0;
+    return NS_OK;
+}
+
+extern "C" ns_status ns_timing_read(int32_t kind, double *total_ms, int64_t *launches,
+                                    double *work) {
+    if (kind < 0 || kind >= kTimeKinds) return fail(NS_ERR_INVALID_ARG, "timing kind %d", kind);
+    std::lock_guard<std::mutex> lk(g_mu);
+    double ms_sum = 0.0, work_sum = 0.0;
+    int64_t count = 0;
+    std::vector<Rec> keep;
+    for (Rec &r : g_recs) {
+        if (r.kind != kind) {
+            keep.push_back(r);
+            continue;
+        }
+        if (r.closed) {
+            hipError_t e = hipEventSynchronize(r.stop);
+            float ms = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+            if (e != hipSuccess) return fail(NS_ERR_HIP, "timing event: %s", hipGetErrorString(e));
+            ms_sum += ms;
+            work_sum += r.work;
+            ++count;
+        }
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
+    }
+    g_recs.swap(keep);
+    if (total_ms) *total_ms = ms_sum;
+    if (launches) *launches = count;
+    if (work) *work = work_sum;
+    return NS_OK;
+}

@@ -1,0 +1,208 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/ns.h declares;
+* ns_plan and the route plan's offsets are bit-exact against the oracle;
+* argument errors are reported before anything touches the GPU.
+"""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import newton_schulz_quintic_amd as nsq
+from newton_schulz_quintic_amd import _lib
+from oracle import planner
+from workloads import dense_transformer, many_small, routed_square_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "ns.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ns_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = nsq.lib()
+    names = _declared()
+    assert "ns_orthogonalize_batched" in names and "ns_pack_shards" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.EXPORTS)
+    assert "gfx950" in nsq.ns_version()
+
+
+def _compare_plan(shapes, steps, S, split):
+    got = nsq.ns_plan(shapes, steps=steps, num_homes=S, split_rows=split)
+    want = planner.plan(shapes, steps, S, split)
+    assert got["cost"] == want["cost"]
+    assert got["home"] == want["home"]
+    assert got["load"] == want["load"]
+    assert got["order"] == want["order"]
+    return got
+
+
+def test_plan_matches_oracle_hand_and_example():
+    _compare_plan([(6, 4), (4, 4)], 5, 2, [[5, 1], [0, 4]])
+    _compare_plan([(1, 10), (1, 7), (1, 6), (1, 5)], 1, 2, None)
+    _compare_plan([(2, 50), (2, 3)], 1, 2, [[1, 1], [2, 0]])
+    _compare_plan([(5,), (2, 3), (7,), (2, 3, 4)], 5, 3, None)
+
+
+def test_plan_routed_uneven_set():
+    ms = routed_square_batch(uneven=True)
+    got = _compare_plan(ms.shapes, 5, 4, ms.split_rows)
+    # 6 / 5 / 5 / 0 matrices per home; home 3 is empty
+    assert [got["home"].count(h) for h in range(4)] == [6, 5, 5, 0]
+    ms = routed_square_batch(uneven=False)
+    got = _compare_plan(ms.shapes, 5, 4, ms.split_rows)
+    assert got["home"] == [0, 1, 2, 3] * 4
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_plan_random_matches_oracle(seed):
+    rng = random.Random(seed)
+    S = rng.randint(1, 9)
+    n = rng.randint(0, 40)
+    shapes = []
+    for _ in range(n):
+        nd = rng.choice([1, 2, 2, 2, 3])
+        shapes.append(tuple(rng.randint(1, 300) for _ in range(nd)))
+    split = None
+    if rng.random() < 0.6 and n:
+        split = []
+        for s in shapes:
+            rows = s[0]
+            cuts = sorted(rng.randint(0, rows) for _ in range(S - 1))
+            split.append([b - a for a, b in zip([0] + cuts, cuts + [rows])])
+        # tensors of fewer than 2 dims take no part; give them any valid split
+    steps = rng.randint(0, 6)
+    _compare_plan(shapes, steps, S, split)
+
+
+def test_plan_large_sets_match_oracle():
+    _compare_plan(dense_transformer().shapes, 5, 8, None)
+    _compare_plan(many_small().shapes, 5, 8, None)
+
+
+def _compare_offsets(shapes, split, home, S, elem):
+    plan = nsq.ns_route_plan_create(shapes, S, split, home, elem)
+    q = nsq.ns_route_plan_query(plan)
+    want = planner.route_offsets(shapes, split, home, S)
+    assert q["shard_elems"] == want["shard_elems"]
+    assert q["home_elems"] == want["home_elems"]
+    assert q["home_offset"] == want["home_offset"]
+    assert q["shard_offset"] == want["shard_offset"]
+    return q
+
+
+def test_route_offsets_worked_example():
+    q = _compare_offsets([(6, 4), (4, 4)], [[5, 1], [0, 4]], [1, 1], 2, 4)
+    assert q["home_elems"] == [0, 40] and q["shard_elems"] == [20, 20]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_route_offsets_random(seed):
+    rng = random.Random(100 + seed)
+    S = rng.randint(1, 8)
+    n = rng.randint(0, 30)
+    shapes, split = [], []
+    for _ in range(n):
+        nd = rng.randint(2, 4)
+        s = tuple([rng.randint(0, 50)] + [rng.randint(0, 7) for _ in range(nd - 1)])
+        shapes.append(s)
+        cuts = sorted(rng.randint(0, s[0]) for _ in range(S - 1))
+        split.append([b - a for a, b in zip([0] + cuts, cuts + [s[0]])])
+    home = [rng.randrange(S) for _ in range(n)]
+    _compare_offsets(shapes, split, home, S, rng.choice([2, 4]))
+
+
+def test_route_plan_fingerprint_tracks_inputs():
+    a = nsq.ns_route_plan_query(nsq.ns_route_plan_create([(4, 4)], 2, [[2, 2]], [0], 2))
+    b = nsq.ns_route_plan_query(nsq.ns_route_plan_create([(4, 4)], 2, [[2, 2]], [0], 2))
+    c = nsq.ns_route_plan_query(nsq.ns_route_plan_create([(4, 4)], 2, [[2, 2]], [1], 2))
+    d = nsq.ns_route_plan_query(nsq.ns_route_plan_create([(4, 4)], 2, [[1, 3]], [0], 2))
+    assert a["fingerprint"] == b["fingerprint"]
+    assert len({a["fingerprint"], c["fingerprint"], d["fingerprint"]}) == 3
+
+
+def _status(fn, *args):
+    with pytest.raises(nsq.NSError) as e:
+        fn(*args)
+    return e.value.name
+
+
+def test_plan_errors():
+    assert _status(nsq.ns_plan, [(4, 5)], 5, 2, [[1, 2]]) == "NS_ERR_SPLIT_SUM"
+    assert _status(nsq.ns_plan, [(0, 5)], 5, 2, [[0, 0]]) == "NS_ERR_NO_CANDIDATE"
+    assert _status(nsq.ns_plan, [(4, 5)], 5, 2, [[-1, 5]]) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_plan, [(4, 5)], -1, 2) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_plan, [(4, 5)], 5, 0) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_plan, [(4, 5)], 5, 65) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_plan, [(2 ** 31, 2 ** 31)], 5, 1) == "NS_ERR_OVERFLOW"
+    assert _status(nsq.ns_plan, [(2 ** 40, 2 ** 40)], 5, 1) == "NS_ERR_OVERFLOW"
+    assert "overflow" in nsq.ns_last_error()
+    lib = nsq.lib()
+    assert lib.ns_plan(1, None, 5, 1, None, None, None, None, None) == -1
+    assert lib.ns_plan(-1, None, 5, 1, None, None, None, None, None) == -1
+    assert lib.ns_plan(0, None, 5, 1, None, None, None, None, None) == 0
+
+
+def test_route_plan_errors():
+    assert _status(nsq.ns_route_plan_create, [(4, 4)], 2, [[2, 2]], [2], 2) == "NS_ERR_HOME_RANGE"
+    assert _status(nsq.ns_route_plan_create, [(4, 4)], 2, [[2, 2]], [-1], 2) == "NS_ERR_HOME_RANGE"
+    assert _status(nsq.ns_route_plan_create, [(4, 4)], 2, [[2, 1]], [0], 2) == "NS_ERR_SPLIT_SUM"
+    assert _status(nsq.ns_route_plan_create, [(4, 4)], 2, [[2, 2]], [0], 3) == "NS_ERR_DTYPE"
+    assert _status(nsq.ns_route_plan_create, [(4,)], 1, [[4]], [0], 2) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_route_plan_create, [(4, 4)], 0, [], [0], 2) == "NS_ERR_INVALID_ARG"
+    big = 2 ** 62
+    assert _status(nsq.ns_route_plan_create, [(big, 2)], 1, [[big]], [0], 2) == "NS_ERR_OVERFLOW"
+    lib = nsq.lib()
+    out = ctypes.c_void_p()
+    assert lib.ns_route_plan_create(1, None, 1, None, None, 2, ctypes.byref(out)) == -1
+    assert lib.ns_route_plan_create(0, None, 1, None, None, 2, None) == -1
+    # an empty plan is fine
+    p = nsq.ns_route_plan_create([], 3, [], [], 2)
+    assert nsq.ns_route_plan_query(p)["shard_elems"] == [0, 0, 0]
+    # pack before upload: plan mismatch (checked on the host, nothing launched)
+    p = nsq.ns_route_plan_create([(4, 4)], 1, [[4]], [0], 2)
+    assert lib.ns_pack_shards(p.handle, None, None, None) in (-1, -6)
+    assert lib.ns_pack_shards(None, None, None, None) == -1
+
+
+def test_workspace_and_batched_errors():
+    b, mb = nsq.ns_workspace_bytes([(1024, 1024)] * 3 + [(5,)], nsq.NS_BF16)
+    assert b > mb > 0
+    one, _ = nsq.ns_workspace_bytes([(1024, 1024)], nsq.NS_BF16)
+    assert b > 2 * (one - 4096)
+    # f32 needs about twice the buffers
+    b32, _ = nsq.ns_workspace_bytes([(1024, 1024)], nsq.NS_F32)
+    assert b32 > 1.9 * one
+    assert _status(nsq.ns_workspace_bytes, [(4, 4)], 7) == "NS_ERR_DTYPE"
+    lib = nsq.lib()
+    # n == 0 is a no-op; these all fail in host validation, before any HIP call
+    assert lib.ns_orthogonalize_batched(0, None, None, None, 0, 5, 1.0, 0.0, 0.0, 1e-7, None, None, 0,
+                                        None) == 0
+    sh = _lib._shapes([(4, 4)])
+    ptrs = _lib._arr(ctypes.c_void_p, [256])
+    args = lambda dtype=0, steps=5, eps=1e-7, order=None, ws=None, wsb=0: (  # noqa: E731
+        1, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs), dtype, steps, 3.4, -4.7,
+        2.0, eps, order, ws, wsb, None)
+    assert lib.ns_orthogonalize_batched(*args(dtype=5)) == -8
+    assert lib.ns_orthogonalize_batched(*args(steps=-1)) == -1
+    assert lib.ns_orthogonalize_batched(*args(eps=-1.0)) == -1
+    bad_order = _lib._arr(ctypes.c_int32, [3])
+    assert lib.ns_orthogonalize_batched(*args(order=ctypes.addressof(bad_order))) == -1
+    assert lib.ns_orthogonalize_batched(*args()) == -7          # no workspace
+    assert lib.ns_orthogonalize_batched(*args(ws=4096, wsb=16)) == -7   # too small
+    assert lib.ns_orthogonalize_batched(*args(ws=4100, wsb=1 << 30)) == -7  # misaligned
+    odd = _lib._arr(ctypes.c_void_p, [257])
+    assert lib.ns_orthogonalize_batched(1, ctypes.addressof(sh), ctypes.addressof(odd),
+                                        ctypes.addressof(odd), 0, 5, 3.4, -4.7, 2.0, 1e-7, None, 4096,
+                                        1 << 30, None) == -1
+    assert "aligned" in nsq.ns_last_error()

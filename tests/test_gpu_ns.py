@@ -1,0 +1,187 @@
+"""GPU parity of ns_orthogonalize_batched against the fp64 oracle.
+
+Bar: max abs error <= 2e-2 for bf16 tensors and <= 1e-4 for fp32 tensors,
+element by element, on the same seeded inputs. Sizes span several 128x128
+tiles with ragged tails, tall and wide orientations, 3-D tensors, and the
+method's degenerate cases (zero matrix, a single row or column, zero-size
+tensors, zero steps, c = 0). Also: run-to-run determinism, batch invariance
+(order and company do not change a matrix's bits), and identical results with a
+workspace too small for the whole batch.
+"""
+
+import numpy as np
+import pytest
+
+import newton_schulz_quintic_amd as nsq
+from tests.helpers import TOL, log, oracle_ns, to_device, to_host
+from workloads import CUBIC, DEFAULT_EPS, QUINTIC, host_matrix, single_fp32, square_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(hosts, dtype, steps=5, coeffs=QUINTIC, eps=DEFAULT_EPS, order=None, workspace=None):
+    import torch
+    ins = [to_device(h, dtype) for h in hosts]
+    outs = [torch.empty_like(x) for x in ins]
+    nsq.ns_orthogonalize_batched(ins, outs, steps=steps, coeffs=coeffs, eps=eps, order=order,
+                                 workspace=workspace)
+    torch.cuda.synchronize()
+    return [to_host(o, dtype) for o in outs]
+
+
+def _check(hosts, dtype, outs, steps=5, coeffs=QUINTIC, eps=DEFAULT_EPS, tol=None):
+    tol = TOL[dtype] if tol is None else tol
+    worst = 0.0
+    for h, o in zip(hosts, outs):
+        want = oracle_ns(h, dtype, steps, coeffs, eps)
+        got = (o.astype(np.uint32) << 16).view(np.float32) if dtype == "bf16" else o
+        assert got.shape == want.shape
+        err = float(np.max(np.abs(got.astype(np.float64) - want))) if want.size else 0.0
+        worst = max(worst, err)
+        assert err <= tol, f"shape {h.shape}: max abs err {err} > {tol}"
+    return worst
+
+
+def test_fp32_single_matrix_quintic_and_tall():
+    ms = single_fp32()
+    g = host_matrix(ms.seed, 0, ms.shapes[0], std=1.0, dtype="f32")
+    log("ns: fp32 64x128 quintic, and its transpose")
+    hosts = [g, np.ascontiguousarray(g.T)]
+    _check(hosts, "f32", _run_gpu(hosts, "f32"))
+
+
+def test_fp32_cubic_thirty_steps_is_polar_factor():
+    g = host_matrix(0, 0, (64, 128), std=1.0, dtype="f32")
+    log("ns: fp32 64x128 cubic x30")
+    out = _run_gpu([g, np.ascontiguousarray(g.T)], "f32", steps=30, coeffs=CUBIC)
+    u, s, vt = np.linalg.svd(g.astype(np.float64), full_matrices=False)
+    polar = u @ vt
+    assert np.max(np.abs(out[0] - polar)) <= 1e-4
+    assert np.max(np.abs(out[1] - polar.T)) <= 1e-4
+
+
+def test_bf16_square_set_full():
+    ms = square_batch()
+    hosts = [host_matrix(ms.seed, i, s) for i, s in enumerate(ms.shapes)]
+    log("ns: bf16 16 x 1024^2")
+    worst = _check(hosts, "bf16", _run_gpu(hosts, "bf16"))
+    log(f"   worst abs err {worst:.3e}")
+
+
+RAGGED = [(200, 333), (333, 200), (129, 257), (1, 5), (5, 1), (64, 64), (300, 128), (3, 40, 5),
+          (1000, 130), (2, 2), (127, 1025)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_batch(dtype):
+    std = 0.02 if dtype == "bf16" else 1.0
+    hosts = [host_matrix(11, i, s, std=std, dtype=dtype) for i, s in enumerate(RAGGED)]
+    log(f"ns: ragged batch {dtype}")
+    _check(hosts, dtype, _run_gpu(hosts, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_cases(dtype):
+    import torch
+    log(f"ns: degenerate cases {dtype}")
+    zero = np.zeros((70, 90), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    small = host_matrix(12, 0, (20, 30), dtype=dtype)
+    outs = _run_gpu([zero, small], dtype)
+    assert not np.any(outs[0])                           # zero in, zero out (+0.0 bits)
+    _check([small], dtype, outs[1:])
+    # zero steps: the normalised input, transposed back
+    _check([small, np.ascontiguousarray(small.T)], dtype,
+           _run_gpu([small, np.ascontiguousarray(small.T)], dtype, steps=0), steps=0)
+    # c = 0 (the cubic) skips the A A product
+    _check([small], dtype, _run_gpu([small], dtype, steps=7, coeffs=CUBIC), steps=7, coeffs=CUBIC)
+    # zero-size tensors and 1-D tensors in a batch are left alone
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ins = [torch.empty((0, 7), dtype=tdt, device="cuda"), to_device(small, dtype),
+           torch.ones((5,), dtype=tdt, device="cuda")]
+    outs = [torch.empty_like(x) for x in ins]
+    outs[2].fill_(3.0)
+    nsq.ns_orthogonalize_batched(ins, outs)
+    torch.cuda.synchronize()
+    _check([small], dtype, [to_host(outs[1], dtype)])
+    assert torch.all(outs[2] == 3.0)
+
+
+def test_in_place_output():
+    import torch
+    h = host_matrix(13, 0, (256, 384))
+    x = to_device(h, "bf16")
+    log("ns: in place")
+    nsq.ns_orthogonalize_batched([x], [x])
+    torch.cuda.synchronize()
+    _check([h], "bf16", [to_host(x, "bf16")])
+
+
+def test_deterministic_and_batch_invariant():
+    shapes = [(512, 700), (700, 512), (256, 256), (96, 1000)]
+    hosts = [host_matrix(14, i, s) for i, s in enumerate(shapes)]
+    log("ns: determinism / batch invariance")
+    a = _run_gpu(hosts, "bf16")
+    b = _run_gpu(hosts, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    rev = _run_gpu(hosts[::-1], "bf16", order=[3, 1, 2, 0])[::-1]
+    for x, y in zip(a, rev):
+        assert np.array_equal(x, y)
+    for i, h in enumerate(hosts):
+        alone = _run_gpu([h], "bf16")[0]
+        assert np.array_equal(alone, a[i])
+
+
+def test_small_workspace_gives_same_bits():
+    import torch
+    shapes = [(384, 640), (256, 256), (640, 384), (128, 1024)]
+    hosts = [host_matrix(15, i, s) for i, s in enumerate(shapes)]
+    full = _run_gpu(hosts, "bf16")
+    need, minimum = nsq.ns_workspace_bytes(shapes, nsq.NS_BF16)
+    assert minimum < need
+    ws = torch.empty(minimum, dtype=torch.uint8, device="cuda")
+    log("ns: minimum workspace (one matrix at a time)")
+    small = _run_gpu(hosts, "bf16", workspace=ws)
+    for x, y in zip(full, small):
+        assert np.array_equal(x, y)
+    _check(hosts, "bf16", small)
+
+
+def test_routed_equals_unrouted_bitwise():
+    """pack -> NS on the home buffers -> unpack gives each shard exactly its rows of NS(full)."""
+    import torch
+    from workloads import routed_square_batch
+    ms = routed_square_batch(True)
+    fulls = [host_matrix(ms.seed, i, s) for i, s in enumerate(ms.shapes)]
+    S = ms.num_shards
+    p = nsq.ns_plan(ms.shapes, 5, S, ms.split_rows)
+    plan = nsq.ns_route_plan_create(ms.shapes, S, ms.split_rows, p["home"], 2)
+    q = nsq.ns_route_plan_query(plan)
+    nsq.ns_route_plan_upload(plan)
+    parts = [[] for _ in range(S)]
+    for f, split in zip(fulls, ms.split_rows):
+        for s, blk in enumerate(np.split(f, np.cumsum(split)[:-1], axis=0)):
+            parts[s].append(blk.ravel())
+    shards = [to_device(np.concatenate(x), "bf16") if q["shard_elems"][s] else None
+              for s, x in enumerate(parts)]
+    homes = [torch.empty(n, dtype=torch.bfloat16, device="cuda") if n else None for n in q["home_elems"]]
+    log("ns: routed vs unrouted")
+    nsq.ns_pack_shards(plan, shards, homes)
+    views_in, views_out, res = [], [], []
+    for i, s in enumerate(ms.shapes):
+        h, off = p["home"][i], q["home_offset"][i]
+        views_in.append(homes[h][off:off + s[0] * s[1]].view(s))
+    res = [torch.empty_like(v) for v in views_in]
+    nsq.ns_orthogonalize_batched(views_in, res, order=p["order"])
+    for i, s in enumerate(ms.shapes):
+        views_in[i].copy_(res[i])
+    nsq.ns_unpack_shards(plan, homes, shards)
+    torch.cuda.synchronize()
+    direct = _run_gpu(fulls, "bf16")
+    for s in range(S):
+        if not q["shard_elems"][s]:
+            continue
+        want = []
+        for i, split in enumerate(ms.split_rows):
+            want.append(np.split(direct[i], np.cumsum(split)[:-1], axis=0)[s].ravel())
+        assert np.array_equal(to_host(shards[s], "bf16"), np.concatenate(want))
