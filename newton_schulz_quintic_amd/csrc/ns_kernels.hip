@@ -23,7 +23,7 @@
 //    store each off-diagonal tile twice (itself and its mirror), so A and B are
 //    exactly symmetric.
 //  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X
-//    (written as X' and X'^T, or on the last step straight to the output in the
+//    (written as X' and X'^T; a final copy kernel moves X or X^T to the output in the
 //    input's orientation, shape and dtype).
 //  * Norm: per-chunk fp32 sums of squares in a fixed order (no atomics), then a
 //    tile pass that reduces the partials, scales, and writes X0 and X0^T
@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -45,28 +46,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 128;          // product output tile (rows and cols); padding unit
-constexpr int kThreads = 256;       // 4 waves
-constexpr int kPanelBytes = 128;    // K bytes per LDS row per stage
-constexpr int kLdsStride = 144;     // padded LDS row stride in bytes (conflict-free fragment reads)
-constexpr int kOperandLds = kTile * kLdsStride;
-constexpr int kStageLds = 2 * kOperandLds;
-constexpr int kLdsBytes = 2 * kStageLds;  // double-buffered P and Q panels: 73728 B
+constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
+constexpr int kThreads = 256;       // 4 waves, 2 x 2 over the output tile
+constexpr int kRowBytes = 128;      // K bytes per LDS panel row per stage (64 bf16 / 32 f32)
 constexpr int kNormChunk = 16384;   // elements per norm partial
 constexpr int kNormTile = 64;       // norm apply tile edge
 constexpr int kNumXcd = 8;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
-    char *x[2];        // X ping/pong: mp x np (ld np)
-    char *xt[2];       // X^T ping/pong: np x mp (ld mp)
+    char *x0, *x1;     // X ping/pong: mp x np (ld np)
+    char *xt0, *xt1;   // X^T ping/pong: np x mp (ld mp)
     char *a;           // mp x mp
     char *b;           // mp x mp
     const char *in;    // input, rows x cols
     char *out;         // output, rows x cols
-    float *partials;   // nparts fp32 partial sums of squares
+    float *partials;   // nparts fp32 partial sums of squares, then the scale
     int32_t m, n;      // oriented sizes (m <= n)
-    int32_t mp, np;    // padded to kTile
+    int32_t mp, np;    // padded to kPad
     int32_t tall;      // input had rows > cols
     int32_t nparts;
 };
@@ -100,6 +97,14 @@ template <> struct Mfma<float> {
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }
 
+#define NSQ_GLOBAL __attribute__((address_space(1)))
+#define NSQ_LDS __attribute__((address_space(3)))
+template <typename T> __device__ __forceinline__ NSQ_GLOBAL T *gp(const char *p) {
+    return (NSQ_GLOBAL T *)(p);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Bijection from hardware workgroup id to logical tile id such that the
 // workgroups of one XCD (hardware ids congruent mod 8) get a contiguous range.
 __device__ __forceinline__ int xcd_remap(int b, int g) {
@@ -110,199 +115,239 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 
 enum Mode { kSyrkX = 0, kSyrkA = 1, kGemmBX = 2 };
 
-// C = P Q^T over K (elements) for one 128x128 tile; P rows [row0, row0+128),
-// Q rows [col0, col0+128). ld in bytes. Every access is in bounds by padding.
-template <typename T>
-__device__ __forceinline__ void tile_product(const char *__restrict__ P, const char *__restrict__ Q,
-                                             int64_t ldp, int64_t ldq, int K, char *lds,
-                                             f32x16 (&acc)[2][2]) {
+// Output tile of BM x BM, 4 waves in 2 x 2, each wave (BM/2)^2 as (BM/64)^2
+// blocks of 32x32 MFMA output. K is staged in panels of kRowBytes per row.
+template <int BM> struct TileCfg {
+    static constexpr int WT = BM / 2;           // wave tile edge
+    static constexpr int NB = WT / 32;          // 32x32 blocks per wave edge
+    static constexpr int PANEL = BM * kRowBytes;
+    static constexpr int STAGE = 2 * PANEL;     // P panel then Q panel
+    static constexpr int LDS = 2 * STAGE;       // two stages
+    static constexpr int LOADS = BM / 32;       // 1 KiB direct-to-LDS loads per wave per panel
+};
+
+// LDS panel layout: row r of the panel at r * 128 bytes; its 16-byte chunk c
+// (8 bf16 / 4 f32 consecutive k) sits in slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// The MFMA fragment reads (32 consecutive rows, one chunk) then hit distinct
+// banks in every group of 8 lanes (32-bank view) and of 16 lanes (64-bank view).
+//
+// Global -> LDS: each wave instruction moves 1 KiB = 8 panel rows straight into
+// LDS (buffer_load ... lds writes lane l's 16 bytes at M0 + 16 l), so lane l
+// fetches row 8 g + l/8, logical chunk (l % 8) ^ f(row).
+template <typename T, int BM>
+__device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int nk,
+                                             char *lds, f32x16 (&acc)[TileCfg<BM>::NB][TileCfg<BM>::NB]) {
+    typedef TileCfg<BM> C;
     typedef typename Mfma<T>::frag frag;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = t >> 3, lc16 = (t & 7) * 16;
-    const int nk = (int)((int64_t)K * sizeof(T) / kPanelBytes);
 
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < C::NB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    uint4 pr[4], qr[4];
-    auto gload = [&](int kb) {
-        const int64_t kbyte = (int64_t)kb * kPanelBytes + lc16;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, BM * ldp, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, BM * ldq, 0x00020000);
+    // per-lane part of the load offsets; instruction i adds 32 i rows
+    const int lrow = wave * 8 + (lane >> 3);
+    const int lchunk = ((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4;
+    const int voff_p = lrow * ldp + lchunk, voff_q = lrow * ldq + lchunk;
+
+    auto issue = [&](int stage, int kb) __attribute__((always_inline)) {
+        char *sb = lds + stage * C::STAGE + wave * 1024;
+        const int kbyte = kb * kRowBytes;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = it * 32 + lrow;
-            pr[it] = *reinterpret_cast<const uint4 *>(P + row * ldp + kbyte);
-            qr[it] = *reinterpret_cast<const uint4 *>(Q + row * ldq + kbyte);
-        }
-    };
-    auto lstore = [&](int buf) {
-        char *base = lds + buf * kStageLds;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = it * 32 + lrow;
-            *reinterpret_cast<uint4 *>(base + row * kLdsStride + lc16) = pr[it];
-            *reinterpret_cast<uint4 *>(base + kOperandLds + row * kLdsStride + lc16) = qr[it];
+        for (int i = 0; i < C::LOADS; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sb + i * 4096), 16, voff_p,
+                                                     kbyte + i * 32 * ldp, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sb + C::PANEL + i * 4096), 16,
+                                                     voff_q, kbyte + i * 32 * ldq, 0, 0);
         }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    const int frow_a = (wm * 64 + (lane & 31)) * kLdsStride + (lane >> 5) * 16;
-    const int frow_b = (wn * 64 + (lane & 31)) * kLdsStride + (lane >> 5) * 16;
+    const int hi = lane >> 5;
+    const int xl = (lane & 7) ^ ((lane >> 3) & 1);
+    const int a_row = (wm * C::WT + (lane & 31)) * kRowBytes;
+    const int b_row = C::PANEL + (wn * C::WT + (lane & 31)) * kRowBytes;
+    int kg_off[4];
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) kg_off[kg] = ((2 * kg + hi) ^ xl) << 4;
+
+    if (nk > 0) issue(0, 0);
     for (int kb = 0; kb < nk; ++kb) {
-        const bool more = kb + 1 < nk;
-        if (more) gload(kb + 1);
-        const char *sp = lds + (kb & 1) * kStageLds;
-        const char *sq = sp + kOperandLds;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's panel loads have landed
+        __syncthreads();                       // ... and everyone's; stage (kb+1)&1 is free again
+        if (kb + 1 < nk) issue((kb + 1) & 1, kb + 1);
+        const char *sb = lds + (kb & 1) * C::STAGE;
+        // fragments for k-group kg + 1 are read while the MFMAs of kg run
+        frag fa[2][C::NB], fb[2][C::NB];
 #pragma unroll
-        for (int kg = 0; kg < kPanelBytes / 32; ++kg) {
-            frag fa[2], fb[2];
+        for (int i = 0; i < C::NB; ++i)
+            fa[0][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[0]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                fa[i] = *reinterpret_cast<const frag *>(sp + frow_a + i * 32 * kLdsStride + kg * 32);
+        for (int j = 0; j < C::NB; ++j)
+            fb[0][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[0]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                fb[j] = *reinterpret_cast<const frag *>(sq + frow_b + j * 32 * kLdsStride + kg * 32);
+        for (int kg = 0; kg < 4; ++kg) {
+            const int cb = kg & 1, nb = cb ^ 1;
+            if (kg < 3) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < C::NB; ++i)
+                    fa[nb][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[kg + 1]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < C::NB; ++j)
+                    fb[nb][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[kg + 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
+#pragma unroll
+            for (int i = 0; i < C::NB; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NB; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
         }
-        if (more) lstore((kb + 1) & 1);
-        __syncthreads();
     }
 }
 
 // Store 4 consecutive-row values of one column into a row-major array at
 // [col][row..row+3] (the mirror / transposed copy), as one vector store.
 template <typename T>
-__device__ __forceinline__ void store4(char *base, int64_t ld_elems, int col, int row, const T v[4]) {
-    T *p = reinterpret_cast<T *>(base) + (int64_t)col * ld_elems + row;
+__device__ __forceinline__ void store4(char *base, int ld, int col, int row, const T v[4]) {
+    NSQ_GLOBAL T *p = gp<T>(base) + (int64_t)col * ld + row;
     if constexpr (sizeof(T) == 2) {
         typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-        b4 w = {v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<b4 *>(p) = w;
+        *(NSQ_GLOBAL b4 *)p = b4{v[0], v[1], v[2], v[3]};
     } else {
-        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        *(NSQ_GLOBAL f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
     }
 }
 
+// Load [col][row..row+3] of a row-major array as 4 floats.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void ns_product_kernel(const NsProb *__restrict__ probs,
+__device__ __forceinline__ void load4(const char *base, int ld, int col, int row, float o[4]) {
+    const NSQ_GLOBAL T *p = gp<T>(base) + (int64_t)col * ld + row;
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        const b4 w = *(const NSQ_GLOBAL b4 *)p;
+        o[0] = (float)w[0], o[1] = (float)w[1], o[2] = (float)w[2], o[3] = (float)w[3];
+    } else {
+        const f32x4 w = *(const NSQ_GLOBAL f32x4 *)p;
+        o[0] = w[0], o[1] = w[1], o[2] = w[2], o[3] = w[3];
+    }
+}
+
+template <typename T, int BM>
+__global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
                                                                  int32_t ntiles, int32_t mode,
-                                                                 int32_t cur, int32_t last, float ca,
-                                                                 float cb, float cc) {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+                                                                 int32_t cur, float ca, float cb,
+                                                                 float cc) {
+    typedef TileCfg<BM> C;
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
     const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
     if (tile_id >= ntiles) return;
     const TileRef tr = tiles[tile_id];
-    const NsProb pr = probs[tr.prob];
-    const int64_t es = sizeof(T);
-    const int row0 = tr.ti * kTile, col0 = tr.tj * kTile;
+    const NsProb &pr = probs[tr.prob];
+    const int es = sizeof(T);
+    const int mp = pr.mp, np = pr.np;
+    const int row0 = tr.ti * BM, col0 = tr.tj * BM;
+    char *xc = cur ? pr.x1 : pr.x0;
+    char *xn = cur ? pr.x0 : pr.x1;
+    char *xtc = cur ? pr.xt1 : pr.xt0;
+    char *xtn = cur ? pr.xt0 : pr.xt1;
+    char *A = pr.a, *B = pr.b;
 
+    // Operands: C = P Q^T, both row-major along K.
     const char *P, *Q;
-    int64_t ldp, ldq;
-    int K;
-    if (mode == kSyrkX) {
-        P = pr.x[cur] + row0 * (int64_t)pr.np * es;
-        Q = pr.x[cur] + col0 * (int64_t)pr.np * es;
-        ldp = ldq = pr.np * es;
-        K = pr.np;
-    } else if (mode == kSyrkA) {
-        P = pr.a + row0 * (int64_t)pr.mp * es;
-        Q = pr.a + col0 * (int64_t)pr.mp * es;
-        ldp = ldq = pr.mp * es;
-        K = pr.mp;
-    } else {
-        P = pr.b + row0 * (int64_t)pr.mp * es;
-        Q = pr.xt[cur] + col0 * (int64_t)pr.mp * es;
-        ldp = ldq = pr.mp * es;
-        K = pr.mp;
+    int ld, K;
+    if (mode == kSyrkX) {            // A = X X^T
+        ld = np * es;
+        P = xc + (int64_t)row0 * ld;
+        Q = xc + (int64_t)col0 * ld;
+        K = np;
+    } else if (mode == kSyrkA) {     // A A = A A^T (A symmetric)
+        ld = mp * es;
+        P = A + (int64_t)row0 * ld;
+        Q = A + (int64_t)col0 * ld;
+        K = cc == 0.f ? 0 : mp;      // c == 0: B = b A needs no product
+    } else {                         // B X = B (X^T)^T
+        ld = mp * es;
+        P = B + (int64_t)row0 * ld;
+        Q = xtc + (int64_t)col0 * ld;
+        K = mp;
     }
-
-    f32x16 acc[2][2];
-    if (mode == kSyrkA && cc == 0.f) {
-        // c == 0: B = b A; the A A product is not needed.
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    } else {
-        tile_product<T>(P, Q, ldp, ldq, K, lds, acc);
-    }
+    f32x16 acc[C::NB][C::NB];
+    tile_product<T, BM>(P, Q, ld, ld, K * es / kRowBytes, lds, acc);
 
     // Epilogue. Accumulator element (i, j, v) of this lane sits at tile row
-    // wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4 and tile column
-    // wn*64 + j*32 + lane%32.
+    // wm*WT + 32 i + 8 (v/4) + 4 (lane/32) + v%4 and tile column wn*WT + 32 j + lane%32.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const bool mirror = tr.ti != tr.tj;
+    char *dst = mode == kSyrkX ? A : mode == kSyrkA ? B : xn;          // row-major result
+    char *dst_t = mode == kGemmBX ? xtn : dst;                          // transposed copy
+    const int ld_dst = mode == kGemmBX ? np : mp;
+    const char *old_t = mode == kSyrkA ? A : xtc;                       // b A / a X source, transposed
+    const float s_old = mode == kSyrkA ? cb : ca;
+    const float s_acc = mode == kSyrkA ? cc : 1.0f;
+    const bool write_t = mode == kGemmBX || mirror;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::NB; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int gc = col0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < C::NB; ++j) {
+            const int gc = col0 + wn * C::WT + j * 32 + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int gr = row0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+                const int gr = row0 + wm * C::WT + i * 32 + 8 * q + 4 * (lane >> 5);
                 T val[4];
                 if (mode == kSyrkX) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) val[e] = from_f32<T>(acc[i][j][4 * q + e]);
-                    T *A = reinterpret_cast<T *>(pr.a);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) A[(int64_t)(gr + e) * pr.mp + gc] = val[e];
-                    if (mirror) store4<T>(pr.a, pr.mp, gc, gr, val);
-                } else if (mode == kSyrkA) {
-                    const T *A = reinterpret_cast<const T *>(pr.a);
-                    T *B = reinterpret_cast<T *>(pr.b);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float old = to_f32<T>(A[(int64_t)(gr + e) * pr.mp + gc]);
-                        val[e] = from_f32<T>(cb * old + cc * acc[i][j][4 * q + e]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) B[(int64_t)(gr + e) * pr.mp + gc] = val[e];
-                    if (mirror) store4<T>(pr.b, pr.mp, gc, gr, val);
                 } else {
-                    const T *X = reinterpret_cast<const T *>(pr.x[cur]);
+                    // X[gr+e][gc] from X^T; A[gr+e][gc] == A[gc][gr+e] since A is symmetric
+                    float old[4];
+                    load4<T>(old_t, mp, gc, gr, old);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float old = to_f32<T>(X[(int64_t)(gr + e) * pr.np + gc]);
-                        val[e] = from_f32<T>(ca * old + acc[i][j][4 * q + e]);
-                    }
-                    if (!last) {
-                        T *Xn = reinterpret_cast<T *>(pr.x[cur ^ 1]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Xn[(int64_t)(gr + e) * pr.np + gc] = val[e];
-                        store4<T>(pr.xt[cur ^ 1], pr.mp, gc, gr, val);
-                    } else {
-                        T *O = reinterpret_cast<T *>(pr.out);
-                        if (gc < pr.n) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int r = gr + e;
-                                if (r < pr.m) {
-                                    if (pr.tall)
-                                        O[(int64_t)gc * pr.m + r] = val[e];   // out is n x m
-                                    else
-                                        O[(int64_t)r * pr.n + gc] = val[e];   // out is m x n
-                                }
-                            }
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        val[e] = from_f32<T>(s_old * old[e] + s_acc * acc[i][j][4 * q + e]);
                 }
+                NSQ_GLOBAL T *D = gp<T>(dst);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ld_dst + gc] = val[e];
+                if (write_t) store4<T>(dst_t, mp, gc, gr, val);
             }
         }
     }
+}
+
+// Final result to the output in the input's orientation: rows of X (wide
+// input, out is m x n) or rows of X^T (tall input, out is n x m). One
+// workgroup per output row chunk of up to 2048 elements.
+struct OutRow {
+    int32_t prob;
+    int32_t row;
+    int32_t col0;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ns_output_kernel(const NsProb *__restrict__ probs,
+                                                             const OutRow *__restrict__ rows,
+                                                             int32_t count, int32_t cur) {
+    const int bid = blockIdx.x;
+    if (bid >= count) return;
+    const OutRow r = rows[bid];
+    const NsProb &pr = probs[r.prob];
+    const char *src = pr.tall ? (cur ? pr.xt1 : pr.xt0) : (cur ? pr.x1 : pr.x0);
+    const int ld_src = pr.tall ? pr.mp : pr.np;
+    const int width = pr.tall ? pr.m : pr.n;
+    const int end = min(width, r.col0 + 2048);
+    const NSQ_GLOBAL T *s = gp<T>(src) + (int64_t)r.row * ld_src;
+    NSQ_GLOBAL T *d = gp<T>(pr.out) + (int64_t)r.row * width;
+    for (int c = r.col0 + threadIdx.x; c < end; c += kThreads) d[c] = s[c];
 }
 
 // Fixed-order fp32 sum over a workgroup (every thread gets the total).
@@ -420,8 +465,8 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
         }
         return;
     }
-    T *X = reinterpret_cast<T *>(pr.x[0]);
-    T *XT = reinterpret_cast<T *>(pr.xt[0]);
+    T *X = reinterpret_cast<T *>(pr.x0);
+    T *XT = reinterpret_cast<T *>(pr.xt0);
     for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
         const int a = e / kNormTile, b = e % kNormTile;
         X[(int64_t)(i0 + a) * pr.np + (j0 + b)] = from_f32<T>(tile[a][b]);
@@ -435,11 +480,12 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+constexpr int kOutChunk = 2048;   // output copy: elements per workgroup
 
 struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
-    int64_t nparts, syrk_tiles, gemm_tiles, norm_tiles;
+    int64_t nparts, syrk_tiles, gemm_tiles, norm_tiles, out_rows;
     size_t buf_bytes;
 };
 
@@ -448,29 +494,30 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
     if (dtype != NS_BF16 && dtype != NS_F32) return fail(NS_ERR_DTYPE, "dtype %d", (int)dtype);
     const int64_t es = dtype == NS_BF16 ? 2 : 4;
-    info.resize(n);
+    info.assign(n, MatInfo{});
     for (int32_t i = 0; i < n; ++i) {
         MatInfo &mi = info[i];
         ns_status st = matrix_view(shapes[i], i, &mi.rows, &mi.cols);
         if (st) return st;
         mi.active = mi.rows > 0 && mi.cols > 0;
-        if (!mi.active) {
-            mi = MatInfo{mi.rows, mi.cols, 0, 0, 0, 0, false, false, 0, 0, 0, 0, 0};
-            continue;
-        }
+        if (!mi.active) continue;
         mi.tall = mi.rows > mi.cols;
         mi.m = std::min(mi.rows, mi.cols);
         mi.n = std::max(mi.rows, mi.cols);
-        if (mi.n > (int64_t)65535 * kNormTile || mi.m * mi.n > ((int64_t)1 << 40))
+        // tile indices are 16-bit; byte offsets inside one padded matrix are 32-bit
+        if (mi.n > (int64_t)65535 * kNormTile || round_up(mi.m, kPad) * round_up(mi.n, kPad) * es >= (1ll << 31))
             return fail(NS_ERR_OVERFLOW, "tensor %d: %lld x %lld is too large", i,
                         (long long)mi.rows, (long long)mi.cols);
-        mi.mp = round_up(mi.m, kTile);
-        mi.np = round_up(mi.n, kTile);
-        const int64_t tm = mi.mp / kTile, tn = mi.np / kTile;
+        mi.mp = round_up(mi.m, kPad);
+        mi.np = round_up(mi.n, kPad);
+        // table sizing uses the smaller product tile (more tiles)
+        const int64_t tm = mi.mp / 128, tn = mi.np / 128;
         mi.syrk_tiles = tm * (tm + 1) / 2;
         mi.gemm_tiles = tm * tn;
         mi.norm_tiles = (mi.mp / kNormTile) * (mi.np / kNormTile);
         mi.nparts = (mi.m * mi.n + kNormChunk - 1) / kNormChunk;
+        const int64_t width = mi.tall ? mi.m : mi.n;
+        mi.out_rows = (mi.tall ? mi.n : mi.m) * ((width + kOutChunk - 1) / kOutChunk);
         const size_t xb = align256((size_t)(mi.mp * mi.np * es));
         const size_t ab = align256((size_t)(mi.mp * mi.mp * es));
         mi.buf_bytes = 4 * xb + 2 * ab;
@@ -478,12 +525,19 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
     return NS_OK;
 }
 
+// Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, parts, ntiles, partials, total;
+    size_t probs, syrk, gemm, parts, ntiles, outrows, partials, total;
+    size_t o_syrk() const { return probs; }
+    size_t o_gemm() const { return o_syrk() + syrk; }
+    size_t o_parts() const { return o_gemm() + gemm; }
+    size_t o_ntiles() const { return o_parts() + parts; }
+    size_t o_outrows() const { return o_ntiles() + ntiles; }
+    size_t o_partials() const { return o_outrows() + outrows; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, pa = 0, nt = 0, ps = 0;
+    int64_t np = 0, sy = 0, ge = 0, pa = 0, nt = 0, orow = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
@@ -491,7 +545,7 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
         ge += mi.gemm_tiles;
         pa += mi.nparts;
         nt += mi.norm_tiles;
-        ++ps;
+        orow += mi.out_rows;
     }
     TableSizes t;
     t.probs = align256(np * sizeof(NsProb));
@@ -499,33 +553,57 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
     t.gemm = align256(ge * sizeof(TileRef));
     t.parts = align256(pa * sizeof(NormPart));
     t.ntiles = align256(nt * sizeof(TileRef));
-    t.partials = align256((pa + ps) * sizeof(float));  // partials + one scale per matrix
-    t.total = t.probs + t.syrk + t.gemm + t.parts + t.ntiles + t.partials;
+    t.outrows = align256(orow * sizeof(OutRow));
+    t.partials = align256((pa + np) * sizeof(float));  // partials + one scale per matrix
+    t.total = t.o_partials() + t.partials;
     return t;
+}
+
+// Product tile edge for a group: 256 when the big tiles still give the GPU
+// enough workgroups, else 128. NS_TILE=128|256 overrides (tuning).
+int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &info) {
+    if (const char *env = getenv("NS_TILE")) {
+        const int v = atoi(env);
+        if (v == 128 || v == 256) return v;
+    }
+    int64_t big_syrk = 0;
+    for (int32_t idx : group) {
+        const int64_t t = info[idx].mp / 256;
+        big_syrk += t * (t + 1) / 2;
+    }
+    return big_syrk >= 128 ? 256 : 128;
+}
+
+template <typename T, int BM>
+void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
+                    int32_t mode, int32_t cur, float a, float b, float c) {
+    hipLaunchKernelGGL((ns_product_kernel<T, BM>), grid, dim3(kThreads), 0, st, probs, tiles, nt, mode,
+                       cur, a, b, c);
 }
 
 template <typename T>
 ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo> &info,
                     const void *const *in, void *const *out, int32_t steps, float a, float b,
                     float c, float eps, char *ws, const TableSizes &tsz, hipStream_t st) {
-    // Host tables for this group.
+    const int64_t es = sizeof(T);
+    const int bm = pick_tile(group, info);
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, ntiles;
     std::vector<NormPart> parts;
+    std::vector<OutRow> orows;
     char *base = ws + tsz.total;
-    float *partials = reinterpret_cast<float *>(ws + tsz.total - tsz.partials);
+    float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
     int64_t part_off = 0;
     double f_syrk_x = 0, f_syrk_a = 0, f_gemm = 0, norm_bytes = 0;
-    const int64_t es = sizeof(T);
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
         const size_t xb = align256((size_t)(mi.mp * mi.np * es));
         const size_t ab = align256((size_t)(mi.mp * mi.mp * es));
-        p.x[0] = base;
-        p.x[1] = base + xb;
-        p.xt[0] = base + 2 * xb;
-        p.xt[1] = base + 3 * xb;
+        p.x0 = base;
+        p.x1 = base + xb;
+        p.xt0 = base + 2 * xb;
+        p.xt1 = base + 3 * xb;
         p.a = base + 4 * xb;
         p.b = base + 4 * xb + ab;
         base += mi.buf_bytes;
@@ -541,7 +619,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.nparts = (int32_t)mi.nparts;
         const int32_t pid = (int32_t)probs.size();
         probs.push_back(p);
-        const int tm = (int)(mi.mp / kTile), tn = (int)(mi.np / kTile);
+        const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
         for (int ti = 0; ti < tm; ++ti)
             for (int tj = ti; tj < tm; ++tj) syrk.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
         for (int ti = 0; ti < tm; ++ti)
@@ -550,6 +628,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         const int nm = (int)(mi.mp / kNormTile), nn = (int)(mi.np / kNormTile);
         for (int ti = 0; ti < nm; ++ti)
             for (int tj = 0; tj < nn; ++tj) ntiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+        const int64_t out_rows = mi.tall ? mi.n : mi.m, width = mi.tall ? mi.m : mi.n;
+        for (int64_t r = 0; r < out_rows; ++r)
+            for (int64_t c0 = 0; c0 < width; c0 += kOutChunk)
+                orows.push_back(OutRow{pid, (int32_t)r, (int32_t)c0});
         const double m = (double)mi.m, n = (double)mi.n;
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += c != 0.f ? m * m * (m + 1) : 0.0;
@@ -559,24 +641,24 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     if (probs.empty()) return NS_OK;
 
     // One upload of every table (stream-ordered after earlier groups' kernels).
-    std::vector<char> host(tsz.total - tsz.partials, 0);
+    std::vector<char> host(tsz.o_partials(), 0);
     auto put = [&](size_t off, const void *src, size_t bytes) {
         if (bytes) std::memcpy(host.data() + off, src, bytes);
     };
-    const size_t o_syrk = tsz.probs, o_gemm = o_syrk + tsz.syrk, o_parts = o_gemm + tsz.gemm,
-                 o_ntiles = o_parts + tsz.parts;
     put(0, probs.data(), probs.size() * sizeof(NsProb));
-    put(o_syrk, syrk.data(), syrk.size() * sizeof(TileRef));
-    put(o_gemm, gemm.data(), gemm.size() * sizeof(TileRef));
-    put(o_parts, parts.data(), parts.size() * sizeof(NormPart));
-    put(o_ntiles, ntiles.data(), ntiles.size() * sizeof(TileRef));
+    put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
+    put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
+    put(tsz.o_parts(), parts.data(), parts.size() * sizeof(NormPart));
+    put(tsz.o_ntiles(), ntiles.data(), ntiles.size() * sizeof(TileRef));
+    put(tsz.o_outrows(), orows.data(), orows.size() * sizeof(OutRow));
     NSQ_HIP(hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st));
 
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
-    const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + o_syrk);
-    const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + o_gemm);
-    const NormPart *d_parts = reinterpret_cast<const NormPart *>(ws + o_parts);
-    const TileRef *d_ntiles = reinterpret_cast<const TileRef *>(ws + o_ntiles);
+    const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
+    const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
+    const NormPart *d_parts = reinterpret_cast<const NormPart *>(ws + tsz.o_parts());
+    const TileRef *d_ntiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ntiles());
+    const OutRow *d_orows = reinterpret_cast<const OutRow *>(ws + tsz.o_outrows());
 
     {
         TimedScope ts(kTimeNorm, st, norm_bytes);
@@ -589,28 +671,24 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     }
     NSQ_HIP(hipGetLastError());
     int cur = 0;
+    const double work[3] = {f_syrk_x, f_syrk_a, f_gemm};
     for (int32_t s = 0; s < steps; ++s) {
-        const int last = s == steps - 1;
-        {
-            TimedScope ts(kTimeProduct, st, f_syrk_x);
-            hipLaunchKernelGGL(ns_product_kernel<T>, dim3((unsigned)syrk.size()), dim3(kThreads), 0,
-                               st, d_probs, d_syrk, (int32_t)syrk.size(), (int32_t)kSyrkX, cur, last,
-                               a, b, c);
-        }
-        {
-            TimedScope ts(kTimeProduct, st, f_syrk_a);
-            hipLaunchKernelGGL(ns_product_kernel<T>, dim3((unsigned)syrk.size()), dim3(kThreads), 0,
-                               st, d_probs, d_syrk, (int32_t)syrk.size(), (int32_t)kSyrkA, cur, last,
-                               a, b, c);
-        }
-        {
-            TimedScope ts(kTimeProduct, st, f_gemm);
-            hipLaunchKernelGGL(ns_product_kernel<T>, dim3((unsigned)gemm.size()), dim3(kThreads), 0,
-                               st, d_probs, d_gemm, (int32_t)gemm.size(), (int32_t)kGemmBX, cur, last,
-                               a, b, c);
+        for (int mode = kSyrkX; mode <= kGemmBX; ++mode) {
+            const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;
+            const int32_t nt = (int32_t)(mode == kGemmBX ? gemm.size() : syrk.size());
+            TimedScope ts(kTimeProduct, st, work[mode]);
+            if (bm == 256)
+                launch_product<T, 256>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
+            else
+                launch_product<T, 128>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
+    }
+    if (steps > 0) {
+        hipLaunchKernelGGL(ns_output_kernel<T>, dim3((unsigned)orows.size()), dim3(kThreads), 0, st,
+                           d_probs, d_orows, (int32_t)orows.size(), cur);
+        NSQ_HIP(hipGetLastError());
     }
     return NS_OK;
 }
