@@ -48,10 +48,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
 constexpr int kThreads = 256;       // 4 waves, 2 x 2 over the output tile
-constexpr int kRowBytes = 128;      // K bytes per LDS panel row per stage (64 bf16 / 32 f32)
+constexpr int kRowBytes = 64;       // K bytes per LDS panel row per stage (32 bf16 / 16 f32)
+constexpr int kStages = 4;          // LDS pipeline depth (3 panels in flight)
 constexpr int kNormChunk = 16384;   // elements per norm partial
 constexpr int kNormTile = 64;       // norm apply tile edge
 constexpr int kNumXcd = 8;
+#ifndef NSQ_ROW_PAD_BYTES
+#define NSQ_ROW_PAD_BYTES 256
+#endif
+// Every workspace row is padded by this many bytes past its padded width, so
+// the row stride is an odd multiple of 256 bytes: a K panel (the same 64 bytes
+// of 256 consecutive rows) then spreads over all L2 channels instead of
+// landing on one or two of them, as a power-of-two stride makes it do.
+constexpr int kRowPadBytes = NSQ_ROW_PAD_BYTES;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
@@ -64,6 +73,8 @@ struct NsProb {
     float *partials;   // nparts fp32 partial sums of squares, then the scale
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
+    int32_t ldx;       // row stride of X (elements, >= np)
+    int32_t ldt;       // row stride of X^T, A and B (elements, >= mp)
     int32_t tall;      // input had rows > cols
     int32_t nparts;
 };
@@ -115,100 +126,127 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 
 enum Mode { kSyrkX = 0, kSyrkA = 1, kGemmBX = 2 };
 
-// Output tile of BM x BM, 4 waves in 2 x 2, each wave (BM/2)^2 as (BM/64)^2
-// blocks of 32x32 MFMA output. K is staged in panels of kRowBytes per row.
-template <int BM> struct TileCfg {
-    static constexpr int WT = BM / 2;           // wave tile edge
-    static constexpr int NB = WT / 32;          // 32x32 blocks per wave edge
+// Output tile of BM x BM computed by WM x WN waves; each wave owns a
+// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
+// panels of kRowBytes per row, kStages deep.
+template <int BM_, int WM_, int WN_> struct TileCfg {
+    static constexpr int BM = BM_, WM = WM_, WN = WN_;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int NBM = BM / WM / 32;    // 32x32 blocks per wave, row direction
+    static constexpr int NBN = BM / WN / 32;    // ... column direction
     static constexpr int PANEL = BM * kRowBytes;
     static constexpr int STAGE = 2 * PANEL;     // P panel then Q panel
-    static constexpr int LDS = 2 * STAGE;       // two stages
-    static constexpr int LOADS = BM / 32;       // 1 KiB direct-to-LDS loads per wave per panel
+    static constexpr int LDS = kStages * STAGE;
+    static constexpr int RPW = BM / WAVES;      // panel rows each wave loads
+    static constexpr int LOADS = RPW / 16;      // 1 KiB loads per wave per panel
+    static constexpr int KG = kRowBytes / 32;   // k-groups (one MFMA K step each) per stage
+    static_assert(RPW % 16 == 0, "each wave loads whole 16-row groups");
 };
+typedef TileCfg<256, 2, 4> Big;    // 8 waves, 2 per SIMD, 128 x 64 per wave
+typedef TileCfg<128, 2, 2> Small;  // 4 waves, 64 x 64 per wave (two workgroups per CU)
 
-// LDS panel layout: row r of the panel at r * 128 bytes; its 16-byte chunk c
-// (8 bf16 / 4 f32 consecutive k) sits in slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
-// The MFMA fragment reads (32 consecutive rows, one chunk) then hit distinct
-// banks in every group of 8 lanes (32-bank view) and of 16 lanes (64-bank view).
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS panel layout: row r of the panel at r * 64 bytes; its 16-byte chunk c
+// (8 bf16 / 4 f32 consecutive k) sits in slot c ^ f(r), with
+// f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1). The MFMA fragment reads (32
+// consecutive rows, one chunk each) then touch distinct banks in every group
+// of 8 lanes (32 banks of 4 bytes) and of 16 lanes (64 banks).
 //
-// Global -> LDS: each wave instruction moves 1 KiB = 8 panel rows straight into
-// LDS (buffer_load ... lds writes lane l's 16 bytes at M0 + 16 l), so lane l
-// fetches row 8 g + l/8, logical chunk (l % 8) ^ f(row).
-template <typename T, int BM>
+// Global -> LDS: each wave instruction moves 1 KiB = 16 panel rows straight
+// into LDS (buffer_load ... lds writes lane l's 16 bytes at M0 + 16 l), so lane
+// l fetches row 16 g + l/4, logical chunk (l % 4) ^ f(row). Each wave loads a
+// contiguous block of RPW rows of each panel.
+template <typename T, class C>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int nk,
-                                             char *lds, f32x16 (&acc)[TileCfg<BM>::NB][TileCfg<BM>::NB]) {
-    typedef TileCfg<BM> C;
+                                             char *lds, f32x16 (&acc)[C::NBM][C::NBN]) {
     typedef typename Mfma<T>::frag frag;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
 
 #pragma unroll
-    for (int i = 0; i < C::NB; ++i)
+    for (int i = 0; i < C::NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NB; ++j)
+        for (int j = 0; j < C::NBN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const __amdgpu_buffer_rsrc_t rp =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, BM * ldp, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, C::BM * ldp, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, BM * ldq, 0x00020000);
-    // per-lane part of the load offsets; instruction i adds 32 i rows
-    const int lrow = wave * 8 + (lane >> 3);
-    const int lchunk = ((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4;
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, C::BM * ldq, 0x00020000);
+    // per-lane part of the load offsets; instruction i adds 16 i rows
+    const int lrow = wave * C::RPW + (lane >> 2);
+    const int lf = ((lane >> 3) & 3) ^ ((lane >> 5) & 1);          // f(lrow)
+    const int lchunk = ((lane & 3) ^ lf) << 4;
     const int voff_p = lrow * ldp + lchunk, voff_q = lrow * ldq + lchunk;
 
-    auto issue = [&](int stage, int kb) __attribute__((always_inline)) {
-        char *sb = lds + stage * C::STAGE + wave * 1024;
+    auto issue = [&](int kb) __attribute__((always_inline)) {
+        char *sb = lds + (kb % kStages) * C::STAGE + wave * C::RPW * kRowBytes;
         const int kbyte = kb * kRowBytes;
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sb + i * 4096), 16, voff_p,
-                                                     kbyte + i * 32 * ldp, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sb + C::PANEL + i * 4096), 16,
-                                                     voff_q, kbyte + i * 32 * ldq, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sb + i * 1024), 16, voff_p,
+                                                     kbyte + i * 16 * ldp, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sb + C::PANEL + i * 1024), 16,
+                                                     voff_q, kbyte + i * 16 * ldq, 0, 0);
         }
     };
 
     const int hi = lane >> 5;
-    const int xl = (lane & 7) ^ ((lane >> 3) & 1);
-    const int a_row = (wm * C::WT + (lane & 31)) * kRowBytes;
-    const int b_row = C::PANEL + (wn * C::WT + (lane & 31)) * kRowBytes;
-    int kg_off[4];
+    const int xf = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);           // f(row) of this lane's fragment rows
+    const int a_row = (wm * (C::BM / C::WM) + (lane & 31)) * kRowBytes;
+    const int b_row = C::PANEL + (wn * (C::BM / C::WN) + (lane & 31)) * kRowBytes;
+    int kg_off[C::KG];
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kg_off[kg] = ((2 * kg + hi) ^ xl) << 4;
+    for (int kg = 0; kg < C::KG; ++kg) kg_off[kg] = ((2 * kg + hi) ^ xf) << 4;
 
-    if (nk > 0) issue(0, 0);
-    for (int kb = 0; kb < nk; ++kb) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's panel loads have landed
-        __syncthreads();                       // ... and everyone's; stage (kb+1)&1 is free again
-        if (kb + 1 < nk) issue((kb + 1) & 1, kb + 1);
-        const char *sb = lds + (kb & 1) * C::STAGE;
-        // fragments for k-group kg + 1 are read while the MFMAs of kg run
-        frag fa[2][C::NB], fb[2][C::NB];
+    constexpr int L = 2 * C::LOADS;   // loads per wave per stage
 #pragma unroll
-        for (int i = 0; i < C::NB; ++i)
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) issue(s);
+    for (int kb = 0; kb < nk; ++kb) {
+        // this wave's loads for panel kb have landed (later panels may still fly)
+        const int ahead = min(nk - 1 - kb, kStages - 2);
+        if (ahead >= 2)
+            wait_vmcnt<2 * L>();
+        else if (ahead == 1)
+            wait_vmcnt<L>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();   // every wave's panel kb is in LDS; buffer (kb-1) % kStages is free
+        if (kb + kStages - 1 < nk) issue(kb + kStages - 1);
+        const char *sb = lds + (kb % kStages) * C::STAGE;
+        // fragments for k-group kg + 1 are read while the MFMAs of kg run
+        frag fa[2][C::NBM], fb[2][C::NBN];
+#pragma unroll
+        for (int i = 0; i < C::NBM; ++i)
             fa[0][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[0]);
 #pragma unroll
-        for (int j = 0; j < C::NB; ++j)
+        for (int j = 0; j < C::NBN; ++j)
             fb[0][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[0]);
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
+        for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
-            if (kg < 3) {
+            if (kg + 1 < C::KG) {
 #pragma unroll
-                for (int i = 0; i < C::NB; ++i)
+                for (int i = 0; i < C::NBM; ++i)
                     fa[nb][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[kg + 1]);
 #pragma unroll
-                for (int j = 0; j < C::NB; ++j)
+                for (int j = 0; j < C::NBN; ++j)
                     fb[nb][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[kg + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
-            for (int i = 0; i < C::NB; ++i)
+            for (int i = 0; i < C::NBM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::NB; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
+                for (int j = 0; j < C::NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
         }
     }
 }
@@ -240,13 +278,13 @@ __device__ __forceinline__ void load4(const char *base, int ld, int col, int row
     }
 }
 
-template <typename T, int BM>
-__global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
+template <typename T, class C>
+__global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
                                                                  int32_t ntiles, int32_t mode,
                                                                  int32_t cur, float ca, float cb,
                                                                  float cc) {
-    typedef TileCfg<BM> C;
+    constexpr int BM = C::BM;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
     const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
     if (tile_id >= ntiles) return;
@@ -255,6 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *_
     const int es = sizeof(T);
     const int mp = pr.mp, np = pr.np;
     const int row0 = tr.ti * BM, col0 = tr.tj * BM;
+    const int ldx = pr.ldx, ldt = pr.ldt;
     char *xc = cur ? pr.x1 : pr.x0;
     char *xn = cur ? pr.x0 : pr.x1;
     char *xtc = cur ? pr.xt1 : pr.xt0;
@@ -265,44 +304,44 @@ __global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *_
     const char *P, *Q;
     int ld, K;
     if (mode == kSyrkX) {            // A = X X^T
-        ld = np * es;
+        ld = ldx * es;
         P = xc + (int64_t)row0 * ld;
         Q = xc + (int64_t)col0 * ld;
         K = np;
     } else if (mode == kSyrkA) {     // A A = A A^T (A symmetric)
-        ld = mp * es;
+        ld = ldt * es;
         P = A + (int64_t)row0 * ld;
         Q = A + (int64_t)col0 * ld;
         K = cc == 0.f ? 0 : mp;      // c == 0: B = b A needs no product
     } else {                         // B X = B (X^T)^T
-        ld = mp * es;
+        ld = ldt * es;
         P = B + (int64_t)row0 * ld;
         Q = xtc + (int64_t)col0 * ld;
         K = mp;
     }
-    f32x16 acc[C::NB][C::NB];
-    tile_product<T, BM>(P, Q, ld, ld, K * es / kRowBytes, lds, acc);
+    f32x16 acc[C::NBM][C::NBN];
+    tile_product<T, C>(P, Q, ld, ld, K * es / kRowBytes, lds, acc);
 
     // Epilogue. Accumulator element (i, j, v) of this lane sits at tile row
-    // wm*WT + 32 i + 8 (v/4) + 4 (lane/32) + v%4 and tile column wn*WT + 32 j + lane%32.
+    // wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32) + v%4 and tile column wn*BM/WN + 32 j + lane%32.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const bool mirror = tr.ti != tr.tj;
     char *dst = mode == kSyrkX ? A : mode == kSyrkA ? B : xn;          // row-major result
     char *dst_t = mode == kGemmBX ? xtn : dst;                          // transposed copy
-    const int ld_dst = mode == kGemmBX ? np : mp;
+    const int ld_dst = mode == kGemmBX ? ldx : ldt;
     const char *old_t = mode == kSyrkA ? A : xtc;                       // b A / a X source, transposed
     const float s_old = mode == kSyrkA ? cb : ca;
     const float s_acc = mode == kSyrkA ? cc : 1.0f;
     const bool write_t = mode == kGemmBX || mirror;
 #pragma unroll
-    for (int i = 0; i < C::NB; ++i) {
+    for (int i = 0; i < C::NBM; ++i) {
 #pragma unroll
-        for (int j = 0; j < C::NB; ++j) {
-            const int gc = col0 + wn * C::WT + j * 32 + (lane & 31);
+        for (int j = 0; j < C::NBN; ++j) {
+            const int gc = col0 + wn * (BM / C::WN) + j * 32 + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int gr = row0 + wm * C::WT + i * 32 + 8 * q + 4 * (lane >> 5);
+                const int gr = row0 + wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
                 T val[4];
                 if (mode == kSyrkX) {
 #pragma unroll
@@ -310,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *_
                 } else {
                     // X[gr+e][gc] from X^T; A[gr+e][gc] == A[gc][gr+e] since A is symmetric
                     float old[4];
-                    load4<T>(old_t, mp, gc, gr, old);
+                    load4<T>(old_t, ldt, gc, gr, old);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         val[e] = from_f32<T>(s_old * old[e] + s_acc * acc[i][j][4 * q + e]);
@@ -318,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_product_kernel(const NsProb *_
                 NSQ_GLOBAL T *D = gp<T>(dst);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ld_dst + gc] = val[e];
-                if (write_t) store4<T>(dst_t, mp, gc, gr, val);
+                if (write_t) store4<T>(dst_t, ldt, gc, gr, val);
             }
         }
     }
@@ -342,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void ns_output_kernel(const NsProb *__res
     const OutRow r = rows[bid];
     const NsProb &pr = probs[r.prob];
     const char *src = pr.tall ? (cur ? pr.xt1 : pr.xt0) : (cur ? pr.x1 : pr.x0);
-    const int ld_src = pr.tall ? pr.mp : pr.np;
+    const int ld_src = pr.tall ? pr.ldt : pr.ldx;
     const int width = pr.tall ? pr.m : pr.n;
     const int end = min(width, r.col0 + 2048);
     const NSQ_GLOBAL T *s = gp<T>(src) + (int64_t)r.row * ld_src;
@@ -469,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
     T *XT = reinterpret_cast<T *>(pr.xt0);
     for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
         const int a = e / kNormTile, b = e % kNormTile;
-        X[(int64_t)(i0 + a) * pr.np + (j0 + b)] = from_f32<T>(tile[a][b]);
-        XT[(int64_t)(j0 + a) * pr.mp + (i0 + b)] = from_f32<T>(tile[b][a]);
+        X[(int64_t)(i0 + a) * pr.ldx + (j0 + b)] = from_f32<T>(tile[a][b]);
+        XT[(int64_t)(j0 + a) * pr.ldt + (i0 + b)] = from_f32<T>(tile[b][a]);
     }
 }
 
@@ -489,6 +528,13 @@ struct MatInfo {
     size_t buf_bytes;
 };
 
+// Row strides (elements) and array sizes of one matrix's workspace.
+inline int64_t ld_x(const MatInfo &mi, int64_t es) { return mi.np + kRowPadBytes / es; }
+inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }
+inline size_t x_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_x(mi, es) * es)); }
+inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.np * ld_t(mi, es) * es)); }
+inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
+
 ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info) {
     if (n < 0) return fail(NS_ERR_INVALID_ARG, "n = %d < 0", n);
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
@@ -505,7 +551,8 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.m = std::min(mi.rows, mi.cols);
         mi.n = std::max(mi.rows, mi.cols);
         // tile indices are 16-bit; byte offsets inside one padded matrix are 32-bit
-        if (mi.n > (int64_t)65535 * kNormTile || round_up(mi.m, kPad) * round_up(mi.n, kPad) * es >= (1ll << 31))
+        if (mi.n > (int64_t)65535 * kNormTile ||
+            round_up(mi.m, kPad) * (round_up(mi.n, kPad) + kRowPadBytes / es) * es >= (1ll << 31))
             return fail(NS_ERR_OVERFLOW, "tensor %d: %lld x %lld is too large", i,
                         (long long)mi.rows, (long long)mi.cols);
         mi.mp = round_up(mi.m, kPad);
@@ -518,9 +565,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.nparts = (mi.m * mi.n + kNormChunk - 1) / kNormChunk;
         const int64_t width = mi.tall ? mi.m : mi.n;
         mi.out_rows = (mi.tall ? mi.n : mi.m) * ((width + kOutChunk - 1) / kOutChunk);
-        const size_t xb = align256((size_t)(mi.mp * mi.np * es));
-        const size_t ab = align256((size_t)(mi.mp * mi.mp * es));
-        mi.buf_bytes = 4 * xb + 2 * ab;
+        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
 }
@@ -574,10 +619,10 @@ int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &inf
     return big_syrk >= 128 ? 256 : 128;
 }
 
-template <typename T, int BM>
+template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
                     int32_t mode, int32_t cur, float a, float b, float c) {
-    hipLaunchKernelGGL((ns_product_kernel<T, BM>), grid, dim3(kThreads), 0, st, probs, tiles, nt, mode,
+    hipLaunchKernelGGL((ns_product_kernel<T, C>), grid, dim3(C::THREADS), 0, st, probs, tiles, nt, mode,
                        cur, a, b, c);
 }
 
@@ -598,14 +643,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
-        const size_t xb = align256((size_t)(mi.mp * mi.np * es));
-        const size_t ab = align256((size_t)(mi.mp * mi.mp * es));
+        const size_t xb = x_bytes(mi, es), tb = xt_bytes(mi, es), ab = a_bytes(mi, es);
         p.x0 = base;
-        p.x1 = base + xb;
-        p.xt0 = base + 2 * xb;
-        p.xt1 = base + 3 * xb;
-        p.a = base + 4 * xb;
-        p.b = base + 4 * xb + ab;
+        p.x1 = p.x0 + xb;
+        p.xt0 = p.x1 + xb;
+        p.xt1 = p.xt0 + tb;
+        p.a = p.xt1 + tb;
+        p.b = p.a + ab;
         base += mi.buf_bytes;
         p.in = static_cast<const char *>(in[idx]);
         p.out = static_cast<char *>(out[idx]);
@@ -615,6 +659,8 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.n = (int32_t)mi.n;
         p.mp = (int32_t)mi.mp;
         p.np = (int32_t)mi.np;
+        p.ldx = (int32_t)ld_x(mi, es);
+        p.ldt = (int32_t)ld_t(mi, es);
         p.tall = mi.tall;
         p.nparts = (int32_t)mi.nparts;
         const int32_t pid = (int32_t)probs.size();
@@ -678,9 +724,9 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const int32_t nt = (int32_t)(mode == kGemmBX ? gemm.size() : syrk.size());
             TimedScope ts(kTimeProduct, st, work[mode]);
             if (bm == 256)
-                launch_product<T, 256>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
+                launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
             else
-                launch_product<T, 128>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
+                launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
