@@ -182,7 +182,7 @@ def test_workspace_and_batched_errors():
     assert b > 2 * (one - 4096)
     # f32 needs about twice the buffers
     b32, _ = nsq.ns_workspace_bytes([(1024, 1024)], nsq.NS_F32)
-    assert b32 > 1.9 * one
+    assert b32 > 1.8 * one       # fixed 256-byte row pad is not doubled
     assert _status(nsq.ns_workspace_bytes, [(4, 4)], 7) == "NS_ERR_DTYPE"
     lib = nsq.lib()
     # n == 0 is a no-op; these all fail in host validation, before any HIP call
