@@ -49,7 +49,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
 constexpr int kThreads = 256;       // 4 waves, 2 x 2 over the output tile
 constexpr int kRowBytes = 64;       // K bytes per LDS panel row per stage (32 bf16 / 16 f32)
-constexpr int kStages = 4;          // LDS pipeline depth (3 panels in flight)
+#ifndef NSQ_STAGES
+#define NSQ_STAGES 4
+#endif
+constexpr int kStages = NSQ_STAGES; // LDS pipeline depth (kStages - 1 panels in flight)
 constexpr int kNormChunk = 16384;   // elements per norm partial
 constexpr int kNormTile = 64;       // norm apply tile edge
 constexpr int kNumXcd = 8;
@@ -214,7 +217,9 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
     for (int kb = 0; kb < nk; ++kb) {
         // this wave's loads for panel kb have landed (later panels may still fly)
         const int ahead = min(nk - 1 - kb, kStages - 2);
-        if (ahead >= 2)
+        if (ahead >= 3)
+            wait_vmcnt<(kStages >= 5 ? 3 : 0) * L>();
+        else if (ahead == 2)
             wait_vmcnt<2 * L>();
         else if (ahead == 1)
             wait_vmcnt<L>();
@@ -619,6 +624,20 @@ int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &inf
     return big_syrk >= 128 ? 256 : 128;
 }
 
+// Tiles of a tm x tn grid (upper triangle only if `upper`) in groups of
+// kGroupRows x kGroupCols. Consecutive tile ids land on one XCD, whose 32 CUs
+// then work on one group at a time: 4 row panels and 8 column panels shared
+// through that XCD's L2, instead of 2 row panels and 16 column panels for a
+// plain row-major order.
+constexpr int kGroupRows = 4, kGroupCols = 8;
+void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef> &out) {
+    for (int bi = 0; bi < tm; bi += kGroupRows)
+        for (int bj = 0; bj < tn; bj += kGroupCols)
+            for (int ti = bi; ti < std::min(tm, bi + kGroupRows); ++ti)
+                for (int tj = bj; tj < std::min(tn, bj + kGroupCols); ++tj)
+                    if (!upper || tj >= ti) out.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+}
+
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
                     int32_t mode, int32_t cur, float a, float b, float c) {
@@ -666,10 +685,8 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         const int32_t pid = (int32_t)probs.size();
         probs.push_back(p);
         const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
-        for (int ti = 0; ti < tm; ++ti)
-            for (int tj = ti; tj < tm; ++tj) syrk.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
-        for (int ti = 0; ti < tm; ++ti)
-            for (int tj = 0; tj < tn; ++tj) gemm.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+        grouped_tiles(pid, tm, tm, true, syrk);
+        grouped_tiles(pid, tm, tn, false, gemm);
         for (int64_t k = 0; k < mi.nparts; ++k) parts.push_back(NormPart{pid, (int32_t)k});
         const int nm = (int)(mi.mp / kNormTile), nn = (int)(mi.np / kNormTile);
         for (int ti = 0; ti < nm; ++ti)
