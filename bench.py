@@ -193,7 +193,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    for k in range(3):
+    for k in range(4):
         nsq.ns_timing_read(k)           # drop anything recorded before the timed region
     if not args.no_kernel_timing:
         nsq.ns_timing_enable(True)
@@ -234,6 +234,7 @@ def main():
         kms, kn, kwork = nsq.ns_timing_read(0)
         rms, rn, rwork = nsq.ns_timing_read(1)
         nms, nn, nwork = nsq.ns_timing_read(2)
+        fms, fn, fwork = nsq.ns_timing_read(3)
         if kn:
             achieved = (kwork / kn) / (kms / kn * 1e-3) / 1e12
             out["roofline"] = {"kernel": "ns_product_kernel<bf16>", "bound": "mfma",

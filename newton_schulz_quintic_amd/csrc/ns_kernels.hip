@@ -53,7 +53,8 @@ constexpr int kRowBytes = 64;       // K bytes per LDS panel row per stage (32 b
 #define NSQ_STAGES 4
 #endif
 constexpr int kStages = NSQ_STAGES; // LDS pipeline depth (kStages - 1 panels in flight)
-constexpr int kNormChunk = 16384;   // elements per norm partial
+constexpr int kNormChunk = 16384;   // minimum elements per norm partial
+constexpr int kMaxParts = kThreads; // at most one partial per thread of the apply reduction
 constexpr int kNormTile = 64;       // norm apply tile edge
 constexpr int kNumXcd = 8;
 #ifndef NSQ_ROW_PAD_BYTES
@@ -73,13 +74,14 @@ struct NsProb {
     char *b;           // mp x mp
     const char *in;    // input, rows x cols
     char *out;         // output, rows x cols
-    float *partials;   // nparts fp32 partial sums of squares, then the scale
+    float *partials;   // nparts (<= kMaxParts) fp32 partial sums of squares
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
     int32_t ldx;       // row stride of X (elements, >= np)
     int32_t ldt;       // row stride of X^T, A and B (elements, >= mp)
     int32_t tall;      // input had rows > cols
     int32_t nparts;
+    int32_t chunk;     // input elements per partial (a multiple of 8)
 };
 
 struct TileRef {
@@ -283,7 +285,10 @@ __device__ __forceinline__ void load4(const char *base, int ld, int col, int row
     }
 }
 
-template <typename T, class C>
+// LAST: the final B X step of the iteration. It writes a X + B X straight to
+// the caller's output in the input's orientation (rows of X for a wide input,
+// rows of X^T for a tall one) instead of into the workspace.
+template <typename T, class C, bool LAST>
 __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
                                                                  int32_t ntiles, int32_t mode,
@@ -339,6 +344,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb 
     const float s_old = mode == kSyrkA ? cb : ca;
     const float s_acc = mode == kSyrkA ? cc : 1.0f;
     const bool write_t = mode == kGemmBX || mirror;
+    const int m = pr.m, n = pr.n;
+    const bool out_vec = (m & 3) == 0 && (reinterpret_cast<uintptr_t>(pr.out) & (4 * sizeof(T) - 1)) == 0;
 #pragma unroll
     for (int i = 0; i < C::NBM; ++i) {
 #pragma unroll
@@ -359,39 +366,30 @@ __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb 
                     for (int e = 0; e < 4; ++e)
                         val[e] = from_f32<T>(s_old * old[e] + s_acc * acc[i][j][4 * q + e]);
                 }
-                NSQ_GLOBAL T *D = gp<T>(dst);
+                if constexpr (!LAST) {
+                    NSQ_GLOBAL T *D = gp<T>(dst);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ld_dst + gc] = val[e];
-                if (write_t) store4<T>(dst_t, ldt, gc, gr, val);
+                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ld_dst + gc] = val[e];
+                    if (write_t) store4<T>(dst_t, ldt, gc, gr, val);
+                } else if (gc < n) {
+                    NSQ_GLOBAL T *O = gp<T>(pr.out);
+                    if (pr.tall) {                 // out is n x m: row gc, columns gr..gr+3
+                        if (out_vec && gr + 3 < m) {
+                            store4<T>(pr.out, m, gc, gr, val);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (gr + e < m) O[(int64_t)gc * m + gr + e] = val[e];
+                        }
+                    } else {                       // out is m x n
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gr + e < m) O[(int64_t)(gr + e) * n + gc] = val[e];
+                    }
+                }
             }
         }
     }
-}
-
-// Final result to the output in the input's orientation: rows of X (wide
-// input, out is m x n) or rows of X^T (tall input, out is n x m). One
-// workgroup per output row chunk of up to 2048 elements.
-struct OutRow {
-    int32_t prob;
-    int32_t row;
-    int32_t col0;
-};
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void ns_output_kernel(const NsProb *__restrict__ probs,
-                                                             const OutRow *__restrict__ rows,
-                                                             int32_t count, int32_t cur) {
-    const int bid = blockIdx.x;
-    if (bid >= count) return;
-    const OutRow r = rows[bid];
-    const NsProb &pr = probs[r.prob];
-    const char *src = pr.tall ? (cur ? pr.xt1 : pr.xt0) : (cur ? pr.x1 : pr.x0);
-    const int ld_src = pr.tall ? pr.ldt : pr.ldx;
-    const int width = pr.tall ? pr.m : pr.n;
-    const int end = min(width, r.col0 + 2048);
-    const NSQ_GLOBAL T *s = gp<T>(src) + (int64_t)r.row * ld_src;
-    NSQ_GLOBAL T *d = gp<T>(pr.out) + (int64_t)r.row * width;
-    for (int c = r.col0 + threadIdx.x; c < end; c += kThreads) d[c] = s[c];
 }
 
 // Fixed-order fp32 sum over a workgroup (every thread gets the total).
@@ -413,7 +411,7 @@ struct NormPart {
     int32_t part;
 };
 
-// Sum of squares of one kNormChunk-element chunk of one input, in fp32.
+// Sum of squares of one chunk of one input, in fp32, in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb *__restrict__ probs,
                                                                    const NormPart *__restrict__ list,
@@ -422,16 +420,18 @@ __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb 
     const int bid = blockIdx.x;
     if (bid >= count) return;
     const NormPart np_ = list[bid];
-    const NsProb pr = probs[np_.prob];
+    const NsProb &pr = probs[np_.prob];
     const int64_t numel = (int64_t)pr.m * pr.n;
-    const int64_t start = (int64_t)np_.part * kNormChunk;
-    const int64_t end = min(numel, start + (int64_t)kNormChunk);
+    const int64_t start = (int64_t)np_.part * pr.chunk;
+    const int64_t end = min(numel, start + (int64_t)pr.chunk);
     const T *in = reinterpret_cast<const T *>(pr.in);
     float s = 0.f;
     constexpr int kVec = 16 / sizeof(T);
-    if ((reinterpret_cast<uintptr_t>(in) & 15) == 0 && end - start == kNormChunk) {
+    if ((reinterpret_cast<uintptr_t>(in) & 15) == 0) {
+        // start is a multiple of 8 elements, so in + start stays 16-byte aligned
         const uint4 *v4 = reinterpret_cast<const uint4 *>(in + start);
-        for (int k = threadIdx.x; k < kNormChunk / kVec; k += kThreads) {
+        const int64_t nvec = (end - start) / kVec;
+        for (int64_t k = threadIdx.x; k < nvec; k += kThreads) {
             uint4 raw = v4[k];
             const T *e = reinterpret_cast<const T *>(&raw);
 #pragma unroll
@@ -439,6 +439,10 @@ __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb 
                 const float f = to_f32<T>(e[u]);
                 s += f * f;
             }
+        }
+        for (int64_t k = start + nvec * kVec + threadIdx.x; k < end; k += kThreads) {
+            const float f = to_f32<T>(in[k]);
+            s += f * f;
         }
     } else {
         for (int64_t k = start + threadIdx.x; k < end; k += kThreads) {
@@ -450,33 +454,23 @@ __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb 
     if (threadIdx.x == 0) pr.partials[np_.part] = total;
 }
 
-// One workgroup per matrix: reduce its partial sums in a fixed order and store
-// the scale 1 / (||G||_F + eps) after the partials.
-__global__ __launch_bounds__(kThreads) void ns_norm_finish_kernel(const NsProb *__restrict__ probs,
-                                                                  int32_t count, float eps) {
-    __shared__ float red[kThreads];
-    const int bid = blockIdx.x;
-    if (bid >= count) return;
-    const NsProb pr = probs[bid];
-    float s = 0.f;
-    for (int p = threadIdx.x; p < pr.nparts; p += kThreads) s += pr.partials[p];
-    const float nrm = sqrtf(block_sum(s, red));
-    if (threadIdx.x == 0) pr.partials[pr.nparts] = 1.0f / (nrm + eps);
-}
-
 // Scale and write one 64x64 tile of X0 (mp x np) and
 // X0^T, zero in the padding. With write_out (steps == 0) the scaled input goes
 // straight to the output instead.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
-                                                                 int32_t count, int32_t write_out) {
+                                                                 int32_t count, float eps,
+                                                                 int32_t write_out) {
+    __shared__ float red[kThreads];
     __shared__ float tile[kNormTile][kNormTile + 1];
     const int bid = blockIdx.x;
     if (bid >= count) return;
     const TileRef tr = tiles[bid];
     const NsProb pr = probs[tr.prob];
-    const float scale = pr.partials[pr.nparts];
+    // ||G||_F from the matrix's partials: the same fixed-order sum in every workgroup
+    const float part = (int)threadIdx.x < pr.nparts ? pr.partials[threadIdx.x] : 0.f;
+    const float scale = 1.0f / (sqrtf(block_sum(part, red)) + eps);
 
     const T *in = reinterpret_cast<const T *>(pr.in);
     const int i0 = tr.ti * kNormTile, j0 = tr.tj * kNormTile;  // X rows / cols
@@ -524,12 +518,11 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-constexpr int kOutChunk = 2048;   // output copy: elements per workgroup
 
 struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
-    int64_t nparts, syrk_tiles, gemm_tiles, norm_tiles, out_rows;
+    int64_t nparts, chunk, syrk_tiles, gemm_tiles, norm_tiles;
     size_t buf_bytes;
 };
 
@@ -567,9 +560,8 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.syrk_tiles = tm * (tm + 1) / 2;
         mi.gemm_tiles = tm * tn;
         mi.norm_tiles = (mi.mp / kNormTile) * (mi.np / kNormTile);
-        mi.nparts = (mi.m * mi.n + kNormChunk - 1) / kNormChunk;
-        const int64_t width = mi.tall ? mi.m : mi.n;
-        mi.out_rows = (mi.tall ? mi.n : mi.m) * ((width + kOutChunk - 1) / kOutChunk);
+        mi.chunk = std::max<int64_t>(kNormChunk, round_up((mi.m * mi.n + kMaxParts - 1) / kMaxParts, 8));
+        mi.nparts = (mi.m * mi.n + mi.chunk - 1) / mi.chunk;
         mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
@@ -577,17 +569,16 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
 
 // Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, parts, ntiles, outrows, partials, total;
+    size_t probs, syrk, gemm, parts, ntiles, partials, total;
     size_t o_syrk() const { return probs; }
     size_t o_gemm() const { return o_syrk() + syrk; }
     size_t o_parts() const { return o_gemm() + gemm; }
     size_t o_ntiles() const { return o_parts() + parts; }
-    size_t o_outrows() const { return o_ntiles() + ntiles; }
-    size_t o_partials() const { return o_outrows() + outrows; }
+    size_t o_partials() const { return o_ntiles() + ntiles; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, pa = 0, nt = 0, orow = 0;
+    int64_t np = 0, sy = 0, ge = 0, pa = 0, nt = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
@@ -595,7 +586,6 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
         ge += mi.gemm_tiles;
         pa += mi.nparts;
         nt += mi.norm_tiles;
-        orow += mi.out_rows;
     }
     TableSizes t;
     t.probs = align256(np * sizeof(NsProb));
@@ -603,8 +593,7 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
     t.gemm = align256(ge * sizeof(TileRef));
     t.parts = align256(pa * sizeof(NormPart));
     t.ntiles = align256(nt * sizeof(TileRef));
-    t.outrows = align256(orow * sizeof(OutRow));
-    t.partials = align256((pa + np) * sizeof(float));  // partials + one scale per matrix
+    t.partials = align256(pa * sizeof(float));
     t.total = t.o_partials() + t.partials;
     return t;
 }
@@ -640,9 +629,13 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
-                    int32_t mode, int32_t cur, float a, float b, float c) {
-    hipLaunchKernelGGL((ns_product_kernel<T, C>), grid, dim3(C::THREADS), 0, st, probs, tiles, nt, mode,
-                       cur, a, b, c);
+                    int32_t mode, int32_t cur, bool last, float a, float b, float c) {
+    if (last)
+        hipLaunchKernelGGL((ns_product_kernel<T, C, true>), grid, dim3(C::THREADS), 0, st, probs, tiles,
+                           nt, mode, cur, a, b, c);
+    else
+        hipLaunchKernelGGL((ns_product_kernel<T, C, false>), grid, dim3(C::THREADS), 0, st, probs, tiles,
+                           nt, mode, cur, a, b, c);
 }
 
 template <typename T>
@@ -654,7 +647,6 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, ntiles;
     std::vector<NormPart> parts;
-    std::vector<OutRow> orows;
     char *base = ws + tsz.total;
     float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
     int64_t part_off = 0;
@@ -673,7 +665,8 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.in = static_cast<const char *>(in[idx]);
         p.out = static_cast<char *>(out[idx]);
         p.partials = partials + part_off;
-        part_off += mi.nparts + 1;
+        part_off += mi.nparts;
+        p.chunk = (int32_t)mi.chunk;
         p.m = (int32_t)mi.m;
         p.n = (int32_t)mi.n;
         p.mp = (int32_t)mi.mp;
@@ -691,10 +684,6 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         const int nm = (int)(mi.mp / kNormTile), nn = (int)(mi.np / kNormTile);
         for (int ti = 0; ti < nm; ++ti)
             for (int tj = 0; tj < nn; ++tj) ntiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
-        const int64_t out_rows = mi.tall ? mi.n : mi.m, width = mi.tall ? mi.m : mi.n;
-        for (int64_t r = 0; r < out_rows; ++r)
-            for (int64_t c0 = 0; c0 < width; c0 += kOutChunk)
-                orows.push_back(OutRow{pid, (int32_t)r, (int32_t)c0});
         const double m = (double)mi.m, n = (double)mi.n;
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += c != 0.f ? m * m * (m + 1) : 0.0;
@@ -713,7 +702,6 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
     put(tsz.o_parts(), parts.data(), parts.size() * sizeof(NormPart));
     put(tsz.o_ntiles(), ntiles.data(), ntiles.size() * sizeof(TileRef));
-    put(tsz.o_outrows(), orows.data(), orows.size() * sizeof(OutRow));
     NSQ_HIP(hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st));
 
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
@@ -721,16 +709,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
     const NormPart *d_parts = reinterpret_cast<const NormPart *>(ws + tsz.o_parts());
     const TileRef *d_ntiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ntiles());
-    const OutRow *d_orows = reinterpret_cast<const OutRow *>(ws + tsz.o_outrows());
 
     {
         TimedScope ts(kTimeNorm, st, norm_bytes);
         hipLaunchKernelGGL(ns_norm_partial_kernel<T>, dim3((unsigned)parts.size()), dim3(kThreads), 0,
                            st, d_probs, d_parts, (int32_t)parts.size());
-        hipLaunchKernelGGL(ns_norm_finish_kernel, dim3((unsigned)probs.size()), dim3(kThreads), 0, st,
-                           d_probs, (int32_t)probs.size(), eps);
         hipLaunchKernelGGL(ns_norm_apply_kernel<T>, dim3((unsigned)ntiles.size()), dim3(kThreads), 0,
-                           st, d_probs, d_ntiles, (int32_t)ntiles.size(), steps == 0 ? 1 : 0);
+                           st, d_probs, d_ntiles, (int32_t)ntiles.size(), eps, steps == 0 ? 1 : 0);
     }
     NSQ_HIP(hipGetLastError());
     int cur = 0;
@@ -739,19 +724,15 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         for (int mode = kSyrkX; mode <= kGemmBX; ++mode) {
             const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;
             const int32_t nt = (int32_t)(mode == kGemmBX ? gemm.size() : syrk.size());
-            TimedScope ts(kTimeProduct, st, work[mode]);
+            const bool last = mode == kGemmBX && s == steps - 1;
+            TimedScope ts(last ? kTimeFinal : kTimeProduct, st, work[mode]);
             if (bm == 256)
-                launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
+                launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
             else
-                launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, a, b, c);
+                launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
-    }
-    if (steps > 0) {
-        hipLaunchKernelGGL(ns_output_kernel<T>, dim3((unsigned)orows.size()), dim3(kThreads), 0, st,
-                           d_probs, d_orows, (int32_t)orows.size(), cur);
-        NSQ_HIP(hipGetLastError());
     }
     return NS_OK;
 }
