@@ -68,17 +68,16 @@ constexpr int kRowPadBytes = NSQ_ROW_PAD_BYTES;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
-    char *x0, *x1;     // X ping/pong: mp x np (ld np)
-    char *xt0, *xt1;   // X^T ping/pong: np x mp (ld mp)
-    char *a;           // mp x mp
-    char *b;           // mp x mp
+    char *x0, *x1;     // X ping/pong: mp x np (row stride ldx)
+    char *a;           // A: mp x mp (row stride ldt)
+    char *b;           // B: mp x mp (row stride ldt)
     const char *in;    // input, rows x cols
     char *out;         // output, rows x cols
     float *partials;   // nparts (<= kMaxParts) fp32 partial sums of squares
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
     int32_t ldx;       // row stride of X (elements, >= np)
-    int32_t ldt;       // row stride of X^T, A and B (elements, >= mp)
+    int32_t ldt;       // row stride of A and B (elements, >= mp)
     int32_t tall;      // input had rows > cols
     int32_t nparts;
     int32_t chunk;     // input elements per partial (a multiple of 8)
@@ -157,20 +156,124 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// LDS panel layout: row r of the panel at r * 64 bytes; its 16-byte chunk c
-// (8 bf16 / 4 f32 consecutive k) sits in slot c ^ f(r), with
-// f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1). The MFMA fragment reads (32
-// consecutive rows, one chunk each) then touch distinct banks in every group
-// of 8 lanes (32 banks of 4 bytes) and of 16 lanes (64 banks).
+// Operand staging. Each stage holds, per operand, the K slice of kRowBytes
+// bytes for each of the tile's BM rows (16 KiB for the 256 tile), in one of
+// two layouts:
 //
-// Global -> LDS: each wave instruction moves 1 KiB = 16 panel rows straight
-// into LDS (buffer_load ... lds writes lane l's 16 bytes at M0 + 16 l), so lane
-// l fetches row 16 g + l/4, logical chunk (l % 4) ^ f(row). Each wave loads a
-// contiguous block of RPW rows of each panel.
-template <typename T, class C>
-__device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int nk,
-                                             char *lds, f32x16 (&acc)[C::NBM][C::NBN]) {
+//  KMAJOR -- the operand's own rows, K contiguous (A = X X^T reads X this way).
+//    Panel row r at r * 64 bytes; its 16-byte chunk c (8 bf16 / 4 f32
+//    consecutive k) sits in slot c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1),
+//    so the fragment reads (32 consecutive rows, one chunk each) hit distinct
+//    banks in every 8 lanes (32 banks) and every 16 lanes (64 banks). Each wave
+//    instruction moves 16 rows x 64 bytes.
+//
+//  NMAJOR -- the K rows of the source matrix, the tile's BM columns contiguous:
+//    KPS = 64 / es rows of RB = BM * es bytes. Used where the operand's rows are
+//    the source's columns: X in B X (B X needs X[k][j]), and the symmetric A and
+//    B (A[i][k] = A[k][i]). Each wave instruction moves whole 512-byte row
+//    stretches, and no transposed copy of X is kept. The 16-byte unit u of row r
+//    sits at unit position u ^ (2 (r % 4)). bf16 fragments come out with
+//    ds_read_b64_tr_b16: in each group of 16 lanes, lane i points at row
+//    k0 + i/4, columns n0 + 4 (i % 4), and lane j receives column n0 + j, rows
+//    k0 .. k0+3; two such reads give the 8 consecutive k of an MFMA operand.
+//    f32 fragments are four 4-byte reads.
+//
+// Global -> LDS uses buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l,
+// so each lane fetches whatever global 16 bytes belong at its LDS slot.
+template <class C, int ES, bool NM> struct Stage {
+    static constexpr int KPS = kRowBytes / ES;        // K rows per stage (NMAJOR)
+    static constexpr int RB = C::BM * ES;             // bytes per NMAJOR row
+    static constexpr int RPI = 1024 / RB;             // NMAJOR rows per 1 KiB load
+    static_assert(!NM || (RB >= 128 && 1024 % RB == 0), "NMAJOR row size");
+};
+
+template <class C, int ES, bool NM>
+__device__ __forceinline__ void operand_offsets(int lane, int wave, int ld, int (&voff)[C::LOADS]) {
+    if constexpr (!NM) {
+        const int lrow = wave * C::RPW + (lane >> 2);
+        const int lf = ((lane >> 3) & 3) ^ ((lane >> 5) & 1);          // f(lrow)
+        const int off = lrow * ld + (((lane & 3) ^ lf) << 4);
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) voff[i] = off + i * 16 * ld;
+    } else {
+        typedef Stage<C, ES, NM> S;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int g = wave * C::LOADS + i;                          // 1 KiB block of the stage
+            const int r = g * S::RPI + (lane * 16) / S::RB;             // K row within the stage
+            const int p = ((lane * 16) % S::RB) >> 4;                   // unit position in the row
+            voff[i] = r * ld + ((p ^ (2 * (r & 3))) << 4);
+        }
+    }
+}
+
+template <class C, int ES, bool NM>
+__device__ __forceinline__ void operand_issue(const __amdgpu_buffer_rsrc_t &rs, const int (&voff)[C::LOADS],
+                                              int ld, int kb, char *region, int wave) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+        int soff;
+        char *dst;
+        if constexpr (!NM) {
+            soff = kb * kRowBytes;
+            dst = region + wave * C::RPW * kRowBytes + i * 1024;
+        } else {
+            soff = kb * Stage<C, ES, NM>::KPS * ld;
+            dst = region + (wave * C::LOADS + i) * 1024;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)dst, 16, voff[i], soff, 0, 0);
+    }
+}
+
+// MFMA operand fragment for the 32-row block starting at tile row `blk`,
+// k-group kg of the stage: lane l gets row blk + l%32, k = 8 (l/32) + e.
+template <typename T, class C, bool NM>
+__device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *region, int lane, int blk,
+                                                             int kg) {
     typedef typename Mfma<T>::frag frag;
+    if constexpr (!NM) {
+        const int row = blk + (lane & 31);
+        const int xf = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);       // f(row)
+        return *reinterpret_cast<const frag *>(region + row * kRowBytes + (((2 * kg + (lane >> 5)) ^ xf) << 4));
+    } else if constexpr (sizeof(T) == 2) {
+        typedef Stage<C, 2, true> S;
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const int i = lane & 15, g = lane >> 4;
+        const int col = blk + 16 * (g & 1) + 4 * (i & 3);          // element column in the tile
+        const int unit = col >> 3, half = (col >> 2) & 1;
+        s4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kl = 16 * kg + 8 * (g >> 1) + 4 * h + (i >> 2);
+            const char *a = region + kl * S::RB + ((unit ^ (2 * (kl & 3))) << 4) + half * 8;
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s4 *)a);
+        }
+        typedef short s8 __attribute__((ext_vector_type(8)));
+        const s8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        return __builtin_bit_cast(frag, w);
+    } else {
+        typedef Stage<C, 4, true> S;
+        const int col = blk + (lane & 31);
+        const int unit = col >> 2, within = (col & 3) * 4;
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kl = 8 * kg + 4 * (lane >> 5) + e;
+            f[e] = *reinterpret_cast<const float *>(region + kl * S::RB + ((unit ^ (2 * (kl & 3))) << 4) + within);
+        }
+        return f;
+    }
+}
+
+// acc = P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
+// first operand row (KMAJOR) or first column (NMAJOR); ld in bytes; `extent`
+// is the byte size the buffer resources may address from P and Q.
+template <typename T, class C, bool PNM, bool QNM>
+__device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
+                                             int extent_q, int nk, char *lds,
+                                             f32x16 (&acc)[C::NBM][C::NBN]) {
+    typedef typename Mfma<T>::frag frag;
+    constexpr int ES = sizeof(T);
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -183,41 +286,25 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const __amdgpu_buffer_rsrc_t rp =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, C::BM * ldp, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, extent_p, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, C::BM * ldq, 0x00020000);
-    // per-lane part of the load offsets; instruction i adds 16 i rows
-    const int lrow = wave * C::RPW + (lane >> 2);
-    const int lf = ((lane >> 3) & 3) ^ ((lane >> 5) & 1);          // f(lrow)
-    const int lchunk = ((lane & 3) ^ lf) << 4;
-    const int voff_p = lrow * ldp + lchunk, voff_q = lrow * ldq + lchunk;
-
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, extent_q, 0x00020000);
+    int voff_p[C::LOADS], voff_q[C::LOADS];
+    operand_offsets<C, ES, PNM>(lane, wave, ldp, voff_p);
+    operand_offsets<C, ES, QNM>(lane, wave, ldq, voff_q);
     auto issue = [&](int kb) __attribute__((always_inline)) {
-        char *sb = lds + (kb % kStages) * C::STAGE + wave * C::RPW * kRowBytes;
-        const int kbyte = kb * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sb + i * 1024), 16, voff_p,
-                                                     kbyte + i * 16 * ldp, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sb + C::PANEL + i * 1024), 16,
-                                                     voff_q, kbyte + i * 16 * ldq, 0, 0);
-        }
+        char *sb = lds + (kb % kStages) * C::STAGE;
+        operand_issue<C, ES, PNM>(rp, voff_p, ldp, kb, sb, wave);
+        operand_issue<C, ES, QNM>(rq, voff_q, ldq, kb, sb + C::PANEL, wave);
     };
-
-    const int hi = lane >> 5;
-    const int xf = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);           // f(row) of this lane's fragment rows
-    const int a_row = (wm * (C::BM / C::WM) + (lane & 31)) * kRowBytes;
-    const int b_row = C::PANEL + (wn * (C::BM / C::WN) + (lane & 31)) * kRowBytes;
-    int kg_off[C::KG];
-#pragma unroll
-    for (int kg = 0; kg < C::KG; ++kg) kg_off[kg] = ((2 * kg + hi) ^ xf) << 4;
+    const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
 
     constexpr int L = 2 * C::LOADS;   // loads per wave per stage
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < nk) issue(s);
     for (int kb = 0; kb < nk; ++kb) {
-        // this wave's loads for panel kb have landed (later panels may still fly)
+        // this wave's loads for stage kb have landed (later stages may still fly)
         const int ahead = min(nk - 1 - kb, kStages - 2);
         if (ahead >= 3)
             wait_vmcnt<(kStages >= 5 ? 3 : 0) * L>();
@@ -227,27 +314,25 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
             wait_vmcnt<L>();
         else
             wait_vmcnt<0>();
-        __syncthreads();   // every wave's panel kb is in LDS; buffer (kb-1) % kStages is free
+        __syncthreads();   // every wave's stage kb is in LDS; buffer (kb-1) % kStages is free
         if (kb + kStages - 1 < nk) issue(kb + kStages - 1);
-        const char *sb = lds + (kb % kStages) * C::STAGE;
+        const char *sp = lds + (kb % kStages) * C::STAGE, *sq = sp + C::PANEL;
         // fragments for k-group kg + 1 are read while the MFMAs of kg run
         frag fa[2][C::NBM], fb[2][C::NBN];
 #pragma unroll
-        for (int i = 0; i < C::NBM; ++i)
-            fa[0][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[0]);
+        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, C, PNM>(sp, lane, a_blk + 32 * i, 0);
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j)
-            fb[0][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[0]);
+        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T, C, QNM>(sq, lane, b_blk + 32 * j, 0);
 #pragma unroll
         for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
             if (kg + 1 < C::KG) {
 #pragma unroll
                 for (int i = 0; i < C::NBM; ++i)
-                    fa[nb][i] = *reinterpret_cast<const frag *>(sb + a_row + i * 32 * kRowBytes + kg_off[kg + 1]);
+                    fa[nb][i] = operand_frag<T, C, PNM>(sp, lane, a_blk + 32 * i, kg + 1);
 #pragma unroll
                 for (int j = 0; j < C::NBN; ++j)
-                    fb[nb][j] = *reinterpret_cast<const frag *>(sb + b_row + j * 32 * kRowBytes + kg_off[kg + 1]);
+                    fb[nb][j] = operand_frag<T, C, QNM>(sq, lane, b_blk + 32 * j, kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
@@ -285,67 +370,52 @@ __device__ __forceinline__ void load4(const char *base, int ld, int col, int row
     }
 }
 
-// LAST: the final B X step of the iteration. It writes a X + B X straight to
-// the caller's output in the input's orientation (rows of X for a wide input,
-// rows of X^T for a tall one) instead of into the workspace.
-template <typename T, class C, bool LAST>
+// One product launch: MODE picks the operands and epilogue.
+//   kSyrkX : A = X X^T            P = Q = X (KMAJOR)        upper tiles, mirrored
+//   kSyrkA : B = b A + c A A^T    P = Q = A (NMAJOR)        upper tiles, mirrored
+//   kGemmBX: X' = a X + B X       P = B (NMAJOR), Q = X (NMAJOR)
+// LAST (kGemmBX only): the final step writes a X + B X straight to the
+// caller's output in the input's orientation instead of into the workspace.
+template <typename T, class C, int MODE, bool LAST>
 __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
-                                                                 int32_t ntiles, int32_t mode,
-                                                                 int32_t cur, float ca, float cb,
-                                                                 float cc) {
-    constexpr int BM = C::BM;
+                                                                 int32_t ntiles, int32_t cur, float ca,
+                                                                 float cb, float cc) {
+    static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
+    constexpr int BM = C::BM, ES = sizeof(T);
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
     const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
     if (tile_id >= ntiles) return;
     const TileRef tr = tiles[tile_id];
     const NsProb &pr = probs[tr.prob];
-    const int es = sizeof(T);
-    const int mp = pr.mp, np = pr.np;
+    const int mp = pr.mp, np = pr.np, m = pr.m, n = pr.n;
     const int row0 = tr.ti * BM, col0 = tr.tj * BM;
     const int ldx = pr.ldx, ldt = pr.ldt;
     char *xc = cur ? pr.x1 : pr.x0;
     char *xn = cur ? pr.x0 : pr.x1;
-    char *xtc = cur ? pr.xt1 : pr.xt0;
-    char *xtn = cur ? pr.xt0 : pr.xt1;
     char *A = pr.a, *B = pr.b;
 
-    // Operands: C = P Q^T, both row-major along K.
-    const char *P, *Q;
-    int ld, K;
-    if (mode == kSyrkX) {            // A = X X^T
-        ld = ldx * es;
-        P = xc + (int64_t)row0 * ld;
-        Q = xc + (int64_t)col0 * ld;
-        K = np;
-    } else if (mode == kSyrkA) {     // A A = A A^T (A symmetric)
-        ld = ldt * es;
-        P = A + (int64_t)row0 * ld;
-        Q = A + (int64_t)col0 * ld;
-        K = cc == 0.f ? 0 : mp;      // c == 0: B = b A needs no product
-    } else {                         // B X = B (X^T)^T
-        ld = ldt * es;
-        P = B + (int64_t)row0 * ld;
-        Q = xtc + (int64_t)col0 * ld;
-        K = mp;
-    }
     f32x16 acc[C::NBM][C::NBN];
-    tile_product<T, C>(P, Q, ld, ld, K * es / kRowBytes, lds, acc);
+    if constexpr (MODE == kSyrkX) {
+        const int ld = ldx * ES;
+        tile_product<T, C, false, false>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld,
+                                         BM * ld, np * ES / kRowBytes, lds, acc);
+    } else if constexpr (MODE == kSyrkA) {
+        const int ld = ldt * ES;
+        const int nk = cc == 0.f ? 0 : mp * ES / kRowBytes;   // c == 0: B = b A needs no product
+        tile_product<T, C, true, true>(A + (int64_t)row0 * ES, A + (int64_t)col0 * ES, ld, ld, mp * ld,
+                                       mp * ld, nk, lds, acc);
+    } else {
+        tile_product<T, C, true, true>(B + (int64_t)row0 * ES, xc + (int64_t)col0 * ES, ldt * ES, ldx * ES,
+                                       mp * ldt * ES, mp * ldx * ES, mp * ES / kRowBytes, lds, acc);
+    }
 
     // Epilogue. Accumulator element (i, j, v) of this lane sits at tile row
     // wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32) + v%4 and tile column wn*BM/WN + 32 j + lane%32.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const bool mirror = tr.ti != tr.tj;
-    char *dst = mode == kSyrkX ? A : mode == kSyrkA ? B : xn;          // row-major result
-    char *dst_t = mode == kGemmBX ? xtn : dst;                          // transposed copy
-    const int ld_dst = mode == kGemmBX ? ldx : ldt;
-    const char *old_t = mode == kSyrkA ? A : xtc;                       // b A / a X source, transposed
-    const float s_old = mode == kSyrkA ? cb : ca;
-    const float s_acc = mode == kSyrkA ? cc : 1.0f;
-    const bool write_t = mode == kGemmBX || mirror;
-    const int m = pr.m, n = pr.n;
-    const bool out_vec = (m & 3) == 0 && (reinterpret_cast<uintptr_t>(pr.out) & (4 * sizeof(T) - 1)) == 0;
+    const bool out_vec = (m & 3) == 0 && (reinterpret_cast<uintptr_t>(pr.out) & (4 * ES - 1)) == 0;
 #pragma unroll
     for (int i = 0; i < C::NBM; ++i) {
 #pragma unroll
@@ -355,36 +425,46 @@ __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb 
             for (int q = 0; q < 4; ++q) {
                 const int gr = row0 + wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
                 T val[4];
-                if (mode == kSyrkX) {
+                if constexpr (MODE == kSyrkX) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) val[e] = from_f32<T>(acc[i][j][4 * q + e]);
-                } else {
-                    // X[gr+e][gc] from X^T; A[gr+e][gc] == A[gc][gr+e] since A is symmetric
+                    NSQ_GLOBAL T *D = gp<T>(A);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldt + gc] = val[e];
+                    if (mirror) store4<T>(A, ldt, gc, gr, val);
+                } else if constexpr (MODE == kSyrkA) {
                     float old[4];
-                    load4<T>(old_t, ldt, gc, gr, old);
+                    load4<T>(A, ldt, gc, gr, old);   // A[gr+e][gc] == A[gc][gr+e]: A is symmetric
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = from_f32<T>(cb * old[e] + cc * acc[i][j][4 * q + e]);
+                    NSQ_GLOBAL T *D = gp<T>(B);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldt + gc] = val[e];
+                    if (mirror) store4<T>(B, ldt, gc, gr, val);
+                } else {
+                    const NSQ_GLOBAL T *X = gp<T>(xc);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        val[e] = from_f32<T>(s_old * old[e] + s_acc * acc[i][j][4 * q + e]);
-                }
-                if constexpr (!LAST) {
-                    NSQ_GLOBAL T *D = gp<T>(dst);
+                        val[e] = from_f32<T>(ca * to_f32<T>(X[(int64_t)(gr + e) * ldx + gc]) + acc[i][j][4 * q + e]);
+                    if constexpr (!LAST) {
+                        NSQ_GLOBAL T *D = gp<T>(xn);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ld_dst + gc] = val[e];
-                    if (write_t) store4<T>(dst_t, ldt, gc, gr, val);
-                } else if (gc < n) {
-                    NSQ_GLOBAL T *O = gp<T>(pr.out);
-                    if (pr.tall) {                 // out is n x m: row gc, columns gr..gr+3
-                        if (out_vec && gr + 3 < m) {
-                            store4<T>(pr.out, m, gc, gr, val);
-                        } else {
+                        for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldx + gc] = val[e];
+                    } else if (gc < n) {
+                        NSQ_GLOBAL T *O = gp<T>(pr.out);
+                        if (pr.tall) {                 // out is n x m: row gc, columns gr..gr+3
+                            if (out_vec && gr + 3 < m) {
+                                store4<T>(pr.out, m, gc, gr, val);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (gr + e < m) O[(int64_t)gc * m + gr + e] = val[e];
+                            }
+                        } else {                       // out is m x n
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (gr + e < m) O[(int64_t)gc * m + gr + e] = val[e];
+                                if (gr + e < m) O[(int64_t)(gr + e) * n + gc] = val[e];
                         }
-                    } else {                       // out is m x n
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (gr + e < m) O[(int64_t)(gr + e) * n + gc] = val[e];
                     }
                 }
             }
@@ -504,11 +584,9 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
         return;
     }
     T *X = reinterpret_cast<T *>(pr.x0);
-    T *XT = reinterpret_cast<T *>(pr.xt0);
     for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
         const int a = e / kNormTile, b = e % kNormTile;
         X[(int64_t)(i0 + a) * pr.ldx + (j0 + b)] = from_f32<T>(tile[a][b]);
-        XT[(int64_t)(j0 + a) * pr.ldt + (i0 + b)] = from_f32<T>(tile[b][a]);
     }
 }
 
@@ -530,7 +608,6 @@ struct MatInfo {
 inline int64_t ld_x(const MatInfo &mi, int64_t es) { return mi.np + kRowPadBytes / es; }
 inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }
 inline size_t x_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_x(mi, es) * es)); }
-inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.np * ld_t(mi, es) * es)); }
 inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
 
 ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info) {
@@ -562,7 +639,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.norm_tiles = (mi.mp / kNormTile) * (mi.np / kNormTile);
         mi.chunk = std::max<int64_t>(kNormChunk, round_up((mi.m * mi.n + kMaxParts - 1) / kMaxParts, 8));
         mi.nparts = (mi.m * mi.n + mi.chunk - 1) / mi.chunk;
-        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
+        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
 }
@@ -630,12 +707,18 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
                     int32_t mode, int32_t cur, bool last, float a, float b, float c) {
-    if (last)
-        hipLaunchKernelGGL((ns_product_kernel<T, C, true>), grid, dim3(C::THREADS), 0, st, probs, tiles,
-                           nt, mode, cur, a, b, c);
+    if (mode == kSyrkX)
+        hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
+                           tiles, nt, cur, a, b, c);
+    else if (mode == kSyrkA)
+        hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
+                           tiles, nt, cur, a, b, c);
+    else if (!last)
+        hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
+                           tiles, nt, cur, a, b, c);
     else
-        hipLaunchKernelGGL((ns_product_kernel<T, C, false>), grid, dim3(C::THREADS), 0, st, probs, tiles,
-                           nt, mode, cur, a, b, c);
+        hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
+                           tiles, nt, cur, a, b, c);
 }
 
 template <typename T>
@@ -654,12 +737,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
-        const size_t xb = x_bytes(mi, es), tb = xt_bytes(mi, es), ab = a_bytes(mi, es);
+        const size_t xb = x_bytes(mi, es), ab = a_bytes(mi, es);
         p.x0 = base;
         p.x1 = p.x0 + xb;
-        p.xt0 = p.x1 + xb;
-        p.xt1 = p.xt0 + tb;
-        p.a = p.xt1 + tb;
+        p.a = p.x1 + xb;
         p.b = p.a + ab;
         base += mi.buf_bytes;
         p.in = static_cast<const char *>(in[idx]);
@@ -688,7 +769,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += c != 0.f ? m * m * (m + 1) : 0.0;
         f_gemm += 2 * m * m * n;
-        norm_bytes += 2.0 * m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
+        norm_bytes += 2.0 * m * n * es + (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
 
