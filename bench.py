@@ -35,6 +35,64 @@ if ROOT not in sys.path:
 METRIC = "NS matrices/sec + achieved TFLOP/s (% bf16 MFMA peak), 5-step quintic NS"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "ns_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ns_product_bx_routed16x1024.json")
+# rocprof symbol of the dominant kernel on the default workload (bf16, 256x256 tile, B X step)
+DOMINANT_SYMBOL = "ns_product_kernelIDF16bNS0_7TileCfgILi256ELi2ELi4EEELi2ELb0E"
+DOMINANT_NAME = "ns_product_kernel<bf16, 256x256 tile / 8 waves, B X step>"
+TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a"}
+
+
+def _sha256(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != _sha256(KERNEL_SRC):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
+    """Per-launch FETCH_SIZE / WRITE_SIZE of the dominant kernel from two
+    rocprofv3 --pmc runs, scaled by what the same counters read for the pack
+    copy kernel, which reads and writes `copy_bytes` per launch."""
+    import csv
+    import statistics
+
+    def per_kernel(d, counter):
+        vals = {}
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = "bx" if DOMINANT_SYMBOL in r["Kernel_Name"] else (
+                    "copy" if "route_copy_kernel" in r["Kernel_Name"] else None)
+                if key:
+                    vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                    vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: statistics.median(v.values()) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    ff = copy_bytes / 1024.0 / fetch["copy"]
+    fw = copy_bytes / 1024.0 / write["copy"]
+    traffic = (fetch["bx"] * ff + write["bx"] * fw) * 1024.0
+    return {"kernel": DOMINANT_NAME, "kernel_symbol_contains": DOMINANT_SYMBOL,
+            "source": "newton_schulz_quintic_amd/csrc/ns_kernels.hip", "source_sha256": _sha256(KERNEL_SRC),
+            "fetch_kib_per_launch_raw": fetch["bx"], "write_kib_per_launch_raw": write["bx"],
+            "copy_kernel_fetch_kib_raw": fetch["copy"], "copy_kernel_write_kib_raw": write["copy"],
+            "copy_kernel_bytes_each_way": copy_bytes, "factor_fetch": ff, "factor_write": fw,
+            "traffic_bytes_per_launch": traffic}
 
 
 def alg_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
@@ -110,8 +168,9 @@ def cpu_baseline(ms, budget_s: float):
     S = ms.num_shards
     done, t0 = 0, time.perf_counter()
     elapsed = 0.0
-    while done < ms.n and (elapsed < budget_s or done == 0):
-        i = done
+    passes = 0
+    while elapsed < budget_s or done == 0:
+        i = done % ms.n
         shape = ms.shapes[i]
         split = [ms.split_rows[i]]
         full = host_matrix(ms.seed, i, shape, std=ms.std)
@@ -127,10 +186,13 @@ def cpu_baseline(ms, budget_s: float):
         route.unpack(res, [shape], split, p["home"], S)
         elapsed += time.perf_counter() - t_start
         done += 1
+        passes = done // ms.n
     total = time.perf_counter() - t0
+    what = (f"{passes} full pass(es) over the {ms.n} matrices" if done % ms.n == 0 and passes
+            else f"the first {done} of the {ms.n} matrices")
     return {"value": done / elapsed, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {ms.n} matrices of the workload through oracle plan + pack + "
-                      f"fp64 NS ({ms.steps} steps) + unpack, {elapsed:.1f} s of work ({total:.1f} s wall)"}
+            "sample": f"{what} through oracle plan + pack + fp64 NS ({ms.steps} steps) + unpack, "
+                      f"{elapsed:.1f} s of work ({total:.1f} s wall)"}
 
 
 def main():
@@ -140,11 +202,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="routed-square",
                     choices=["routed-square", "dense-transformer", "many-small"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the HIP-event timing of the product kernel")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of the default "
+                         "workload into the traffic JSON (printed) and exit")
     args = ap.parse_args()
+    if args.counters:
+        from workloads import routed_square_batch
+        ms = routed_square_batch(uneven=True)
+        copy_bytes = sum(r * c for r, c in ms.shapes) * 2
+        print(json.dumps(summarize_counters(args.counters[0], args.counters[1], copy_bytes), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no cross-GPU "
               "part in this build; how it would shard is described in the design notes.",
@@ -193,7 +264,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    for k in range(4):
+    for k in TIMING_KINDS:
         nsq.ns_timing_read(k)           # drop anything recorded before the timed region
     if not args.no_kernel_timing:
         nsq.ns_timing_enable(True)
@@ -231,17 +302,24 @@ def main():
         "dense_equiv_flops_per_step": float(dense),
     }
     if not args.no_kernel_timing:
-        kms, kn, kwork = nsq.ns_timing_read(0)
-        rms, rn, rwork = nsq.ns_timing_read(1)
-        nms, nn, nwork = nsq.ns_timing_read(2)
-        fms, fn, fwork = nsq.ns_timing_read(3)
+        t = {name: nsq.ns_timing_read(k) for k, name in TIMING_KINDS.items()}
+        kms, kn, kwork = t["bx"]
         if kn:
             achieved = (kwork / kn) / (kms / kn * 1e-3) / 1e12
-            out["roofline"] = {"kernel": "ns_product_kernel<bf16>", "bound": "mfma",
-                               "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                               "traffic": None, "avg_launch_us": round(kms / kn * 1e3, 2),
+            traffic = stored_traffic() if args.workload == "routed-square" else None
+            out["roofline"] = {"kernel": DOMINANT_NAME, "bound": "mfma", "achieved": round(achieved, 2),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                               "avg_launch_us": round(kms / kn * 1e3, 2),
                                "alg_flops_per_launch": kwork / kn, "launches": kn}
+        phases = {}
+        for name in ("syrk_x", "syrk_a", "bx", "bx_final"):
+            pms, pn, pwork = t[name]
+            if pn:
+                phases[name] = {"avg_us": round(pms / pn * 1e3, 2),
+                                "tflops": round((pwork / pn) / (pms / pn * 1e-3) / 1e12, 1), "launches": pn}
+        out["product_phases"] = phases
+        rms, rn, rwork = t["route"]
         if rn:
             gbs = (rwork / rn) / (rms / rn * 1e-3) / 1e9
             out["route_kernel"] = {"kernel": "route_copy_kernel", "bound": "hbm",
@@ -251,6 +329,7 @@ def main():
                                    "bytes_per_launch": rwork / rn,
                                    "note": "working set fits the 256 MB MALL" if rwork / rn < 256e6
                                    else "working set exceeds the MALL"}
+        nms, nn, nwork = t["norm"]
         if nn:
             out["norm_kernels"] = {"avg_us": round(nms / nn * 1e3, 2), "bytes": nwork / nn}
     if not args.no_cpu_baseline:

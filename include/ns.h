@@ -204,15 +204,16 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
  * ------------------------------------------------------------------------ */
 
 /* Kernel timing: while enabled, the library records a HIP event pair on the
- * launch stream around every launch of its matrix-product kernel, and of its
- * pack/unpack kernel. ns_timing_read waits for those events, returns the sums
- * and clears them. Not thread-safe against concurrent batched calls.
- * kind: 0 = matrix-product kernel (every product launch but the last of each
- * call), 1 = pack/unpack kernel, 2 = norm kernels, 3 = the final product launch
- * of each call (its epilogue writes the caller's output).
+ * launch stream around every launch of its kernels. ns_timing_read waits for
+ * the events of one kind, returns their sums and clears them. Not thread-safe
+ * against concurrent batched calls.
+ * kind: 0 = the B X product kernel (every step but the last),
+ *       1 = pack/unpack kernel, 2 = norm kernels (partial + apply, one pair),
+ *       3 = the final B X launch of each call (it writes the caller's output),
+ *       4 = the A = X X^T product kernel, 5 = the B = b A + c A A product kernel.
  * total_ms: summed durations; launches: number of launches; work: summed
- * algorithmic work of those launches (flops for kinds 0 and 3, bytes moved for
- * kind 1, bytes read + written for kind 2). */
+ * algorithmic work of those launches (flops for kinds 0, 3, 4, 5; bytes moved
+ * for kind 1; bytes read + written for kind 2). */
 ns_status ns_timing_enable(int32_t enable);
 ns_status ns_timing_read(int32_t kind, double *total_ms, int64_t *launches, double *work);
 

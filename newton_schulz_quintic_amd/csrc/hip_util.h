@@ -16,7 +16,17 @@ namespace nsq {
 
 // Kernel timing (see ns_timing_enable): a scope that records a HIP event pair
 // around the launches made while it is alive, when timing is enabled.
-enum TimingKind { kTimeProduct = 0, kTimeRoute = 1, kTimeNorm = 2, kTimeFinal = 3, kTimeKinds = 4 };
+// kTimeProduct covers the B X product kernel (all but the final step);
+// kTimeSyrkX / kTimeSyrkA the two symmetric products; kTimeFinal the last B X.
+enum TimingKind {
+    kTimeProduct = 0,
+    kTimeRoute = 1,
+    kTimeNorm = 2,
+    kTimeFinal = 3,
+    kTimeSyrkX = 4,
+    kTimeSyrkA = 5,
+    kTimeKinds = 6
+};
 
 bool timing_enabled();
 // Returns an opaque slot (or -1 when timing is off). `work` is the algorithmic

@@ -207,22 +207,40 @@ __device__ __forceinline__ void operand_offsets(int lane, int wave, int ld, int 
     }
 }
 
-template <class C, int ES, bool NM>
-__device__ __forceinline__ void operand_issue(const __amdgpu_buffer_rsrc_t &rs, const int (&voff)[C::LOADS],
-                                              int ld, int kb, char *region, int wave) {
+// Loads of one operand's stage kb into `region` (one LDS stage slot).
+template <class C>
+__device__ __forceinline__ void operand_issue_kmajor(__amdgpu_buffer_rsrc_t rs, const int *voff, int kb,
+                                                     char *region, int wave) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-        int soff;
-        char *dst;
-        if constexpr (!NM) {
-            soff = kb * kRowBytes;
-            dst = region + wave * C::RPW * kRowBytes + i * 1024;
-        } else {
-            soff = kb * Stage<C, ES, NM>::KPS * ld;
-            dst = region + (wave * C::LOADS + i) * 1024;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)dst, 16, voff[i], soff, 0, 0);
-    }
+    for (int i = 0; i < C::LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (NSQ_LDS void *)(region + wave * C::RPW * kRowBytes + i * 1024), 16, voff[i], kb * kRowBytes,
+            0, 0);
+}
+
+template <class C, int ES>
+__device__ __forceinline__ void operand_issue_nmajor(__amdgpu_buffer_rsrc_t rs, const int *voff, int ld,
+                                                     int kb, char *region, int wave) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)(region + (wave * C::LOADS + i) * 1024),
+                                                 16, voff[i], kb * Stage<C, ES, true>::KPS * ld, 0, 0);
+}
+
+// Both operands' loads of stage kb into LDS slot kb % kStages.
+template <class C, int ES, bool PNM, bool QNM>
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
+                                            const int (&voff_p)[C::LOADS], const int (&voff_q)[C::LOADS],
+                                            int ldp, int ldq, int kb, char *lds, int wave) {
+    char *sb = lds + (kb % kStages) * C::STAGE;
+    if constexpr (PNM)
+        operand_issue_nmajor<C, ES>(rp, voff_p, ldp, kb, sb, wave);
+    else
+        operand_issue_kmajor<C>(rp, voff_p, kb, sb, wave);
+    if constexpr (QNM)
+        operand_issue_nmajor<C, ES>(rq, voff_q, ldq, kb, sb + C::PANEL, wave);
+    else
+        operand_issue_kmajor<C>(rq, voff_q, kb, sb + C::PANEL, wave);
 }
 
 // MFMA operand fragment for the 32-row block starting at tile row `blk`,
@@ -292,17 +310,12 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
     int voff_p[C::LOADS], voff_q[C::LOADS];
     operand_offsets<C, ES, PNM>(lane, wave, ldp, voff_p);
     operand_offsets<C, ES, QNM>(lane, wave, ldq, voff_q);
-    auto issue = [&](int kb) __attribute__((always_inline)) {
-        char *sb = lds + (kb % kStages) * C::STAGE;
-        operand_issue<C, ES, PNM>(rp, voff_p, ldp, kb, sb, wave);
-        operand_issue<C, ES, QNM>(rq, voff_q, ldq, kb, sb + C::PANEL, wave);
-    };
     const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
 
     constexpr int L = 2 * C::LOADS;   // loads per wave per stage
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
-        if (s < nk) issue(s);
+        if (s < nk) issue_stage<C, ES, PNM, QNM>(rp, rq, voff_p, voff_q, ldp, ldq, s, lds, wave);
     for (int kb = 0; kb < nk; ++kb) {
         // this wave's loads for stage kb have landed (later stages may still fly)
         const int ahead = min(nk - 1 - kb, kStages - 2);
@@ -315,7 +328,8 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         else
             wait_vmcnt<0>();
         __syncthreads();   // every wave's stage kb is in LDS; buffer (kb-1) % kStages is free
-        if (kb + kStages - 1 < nk) issue(kb + kStages - 1);
+        if (kb + kStages - 1 < nk)
+            issue_stage<C, ES, PNM, QNM>(rp, rq, voff_p, voff_q, ldp, ldq, kb + kStages - 1, lds, wave);
         const char *sp = lds + (kb % kStages) * C::STAGE, *sq = sp + C::PANEL;
         // fragments for k-group kg + 1 are read while the MFMAs of kg run
         frag fa[2][C::NBM], fb[2][C::NBN];
@@ -372,8 +386,8 @@ __device__ __forceinline__ void load4(const char *base, int ld, int col, int row
 
 // One product launch: MODE picks the operands and epilogue.
 //   kSyrkX : A = X X^T            P = Q = X (KMAJOR)        upper tiles, mirrored
-//   kSyrkA : B = b A + c A A^T    P = Q = A (NMAJOR)        upper tiles, mirrored
-//   kGemmBX: X' = a X + B X       P = B (NMAJOR), Q = X (NMAJOR)
+//   kSyrkA : B = b A + c A A^T    P = Q = A (KMAJOR)        upper tiles, mirrored
+//   kGemmBX: X' = a X + B X       P = B (KMAJOR), Q = X (NMAJOR)
 // LAST (kGemmBX only): the final step writes a X + B X straight to the
 // caller's output in the input's orientation instead of into the workspace.
 template <typename T, class C, int MODE, bool LAST>
@@ -403,11 +417,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb 
     } else if constexpr (MODE == kSyrkA) {
         const int ld = ldt * ES;
         const int nk = cc == 0.f ? 0 : mp * ES / kRowBytes;   // c == 0: B = b A needs no product
-        tile_product<T, C, true, true>(A + (int64_t)row0 * ES, A + (int64_t)col0 * ES, ld, ld, mp * ld,
-                                       mp * ld, nk, lds, acc);
+        tile_product<T, C, false, false>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld,
+                                         BM * ld, nk, lds, acc);
     } else {
-        tile_product<T, C, true, true>(B + (int64_t)row0 * ES, xc + (int64_t)col0 * ES, ldt * ES, ldx * ES,
-                                       mp * ldt * ES, mp * ldx * ES, mp * ES / kRowBytes, lds, acc);
+        const int ldb = ldt * ES;
+        tile_product<T, C, false, true>(B + (int64_t)row0 * ldb, xc + (int64_t)col0 * ES, ldb, ldx * ES,
+                                        BM * ldb, mp * ldx * ES, mp * ES / kRowBytes, lds, acc);
     }
 
     // Epilogue. Accumulator element (i, j, v) of this lane sits at tile row
@@ -806,7 +821,9 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;
             const int32_t nt = (int32_t)(mode == kGemmBX ? gemm.size() : syrk.size());
             const bool last = mode == kGemmBX && s == steps - 1;
-            TimedScope ts(last ? kTimeFinal : kTimeProduct, st, work[mode]);
+            const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
+                                                                                  : kTimeProduct;
+            TimedScope ts(kind, st, work[mode]);
             if (bm == 256)
                 launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
             else
