@@ -168,7 +168,6 @@ def cpu_baseline(ms, budget_s: float):
     S = ms.num_shards
     done, t0 = 0, time.perf_counter()
     elapsed = 0.0
-    passes = 0
     while elapsed < budget_s or done == 0:
         i = done % ms.n
         shape = ms.shapes[i]
@@ -186,9 +185,8 @@ def cpu_baseline(ms, budget_s: float):
         route.unpack(res, [shape], split, p["home"], S)
         elapsed += time.perf_counter() - t_start
         done += 1
-        passes = done // ms.n
     total = time.perf_counter() - t0
-    what = (f"{passes} full pass(es) over the {ms.n} matrices" if done % ms.n == 0 and passes
+    what = (f"{done} matrices ({done / ms.n:.2f} passes over the {ms.n}-matrix set)" if done >= ms.n
             else f"the first {done} of the {ms.n} matrices")
     return {"value": done / elapsed, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{what} through oracle plan + pack + fp64 NS ({ms.steps} steps) + unpack, "
