@@ -191,7 +191,10 @@ ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
  * order   [n] permutation of 0..n-1 giving the dispatch order (e.g. ns_plan's
  *         order), or NULL for descending cost. Results do not depend on it.
  * workspace/workspace_bytes  device memory, 256-byte aligned, at least the
- *         minimum from ns_workspace_bytes.
+ *         minimum from ns_workspace_bytes. The call uses it as scratch until its
+ *         work on `stream` has finished; two calls in flight at once (e.g. on
+ *         different streams) must not share a workspace. The per-call device
+ *         tables are copied from pinned host staging owned by the library.
  * Errors: INVALID_ARG, DTYPE, WORKSPACE, OVERFLOW, HIP. */
 ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                    const void *const *in, void *const *out, ns_dtype dtype,
@@ -203,10 +206,12 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
  * Measurement support
  * ------------------------------------------------------------------------ */
 
-/* Kernel timing: while enabled, the library records a HIP event pair on the
- * launch stream around every launch of its kernels. ns_timing_read waits for
- * the events of one kind, returns their sums and clears them. Not thread-safe
- * against concurrent batched calls.
+/* Kernel timing: for the kinds enabled (bit k of `kinds` enables kind k;
+ * -1 enables all, 0 disables), the library records a HIP event pair on the
+ * launch stream around every launch of that kind. Each pair adds a little
+ * time to the stream, so enable only the kinds being measured.
+ * ns_timing_read waits for the events of one kind, returns their sums and
+ * clears them. Not thread-safe against concurrent batched calls.
  * kind: 0 = the B X product kernel (every step but the last),
  *       1 = pack/unpack kernel, 2 = norm kernels (partial + apply, one pair),
  *       3 = the final B X launch of each call (it writes the caller's output),
@@ -214,7 +219,7 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
  * total_ms: summed durations; launches: number of launches; work: summed
  * algorithmic work of those launches (flops for kinds 0, 3, 4, 5; bytes moved
  * for kind 1; bytes read + written for kind 2). */
-ns_status ns_timing_enable(int32_t enable);
+ns_status ns_timing_enable(int32_t kinds);
 ns_status ns_timing_read(int32_t kind, double *total_ms, int64_t *launches, double *work);
 
 /* Library version string. */

@@ -279,8 +279,18 @@ def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
     return workspace
 
 
-def ns_timing_enable(enable: bool) -> None:
-    _check(lib().ns_timing_enable(1 if enable else 0))
+def ns_timing_enable(kinds) -> None:
+    """Enable HIP-event timing for the given kinds: True = all, False = none,
+    or an iterable of kind numbers (see ns_timing_read)."""
+    if kinds is True:
+        mask = -1
+    elif kinds is False or kinds is None:
+        mask = 0
+    else:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << int(k)
+    _check(lib().ns_timing_enable(mask))
 
 
 def ns_timing_read(kind: int) -> tuple[float, int, float]:

@@ -789,16 +789,23 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     if (probs.empty()) return NS_OK;
 
     // One upload of every table (stream-ordered after earlier groups' kernels).
-    std::vector<char> host(tsz.o_partials(), 0);
+    const size_t table_bytes = tsz.o_partials();
+    int slot;
+    void *staging;
+    ns_status sst = staging_acquire(table_bytes, &slot, &staging);
+    if (sst) return sst;
+    char *host = static_cast<char *>(staging);
     auto put = [&](size_t off, const void *src, size_t bytes) {
-        if (bytes) std::memcpy(host.data() + off, src, bytes);
+        if (bytes) std::memcpy(host + off, src, bytes);
     };
     put(0, probs.data(), probs.size() * sizeof(NsProb));
     put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
     put(tsz.o_parts(), parts.data(), parts.size() * sizeof(NormPart));
     put(tsz.o_ntiles(), ntiles.data(), ntiles.size() * sizeof(TileRef));
-    NSQ_HIP(hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st));
+    const hipError_t ce = hipMemcpyAsync(ws, host, table_bytes, hipMemcpyHostToDevice, st);
+    if ((sst = staging_release(slot, st, ce == hipSuccess))) return sst;
+    if (ce != hipSuccess) return fail(NS_ERR_HIP, "table upload failed: %s", hipGetErrorString(ce));
 
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());

@@ -1,0 +1,83 @@
+// Pinned host staging for the per-call device tables of the batched
+// Newton-Schulz entry point. Copies from pinned memory are truly asynchronous
+// (a pageable source makes the runtime stage the copy itself, which can hold
+// the host until the stream drains). A buffer is reused only after the event
+// recorded behind its last copy has completed, so the host never overwrites
+// data a pending copy still reads.
+
+#include <mutex>
+#include <vector>
+
+#include "hip_util.h"
+
+namespace nsq {
+
+namespace {
+struct Slot {
+    void *ptr = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool in_use = false;     // handed out and not yet released
+    bool pending = false;    // a copy from it may still be running
+};
+std::mutex g_mu;
+std::vector<Slot> g_slots;
+constexpr size_t kMaxSlots = 8;
+
+bool idle(Slot &s) {
+    if (s.in_use) return false;
+    if (s.pending && hipEventQuery(s.done) == hipSuccess) s.pending = false;
+    return !s.pending;
+}
+}  // namespace
+
+ns_status staging_acquire(size_t bytes, int *slot, void **ptr) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    int pick = -1;
+    for (size_t i = 0; i < g_slots.size(); ++i)
+        if (idle(g_slots[i]) && (pick < 0 || g_slots[i].cap >= bytes)) {
+            pick = (int)i;
+            if (g_slots[i].cap >= bytes) break;
+        }
+    if (pick < 0 && g_slots.size() < kMaxSlots) {
+        g_slots.emplace_back();
+        pick = (int)g_slots.size() - 1;
+        NSQ_HIP(hipEventCreateWithFlags(&g_slots[pick].done, hipEventDisableTiming));
+    }
+    if (pick < 0) {
+        // every slot is busy: wait for the oldest free-able one
+        for (size_t i = 0; i < g_slots.size() && pick < 0; ++i)
+            if (!g_slots[i].in_use) {
+                NSQ_HIP(hipEventSynchronize(g_slots[i].done));
+                g_slots[i].pending = false;
+                pick = (int)i;
+            }
+        if (pick < 0) return fail(NS_ERR_HIP, "no free table staging buffer (too many concurrent calls)");
+    }
+    Slot &s = g_slots[pick];
+    if (s.cap < bytes) {
+        if (s.ptr) NSQ_HIP(hipHostFree(s.ptr));
+        s.ptr = nullptr;
+        s.cap = 0;
+        const size_t cap = std::max<size_t>(bytes, 1 << 20);
+        NSQ_HIP(hipHostMalloc(&s.ptr, cap, hipHostMallocDefault));
+        s.cap = cap;
+    }
+    s.in_use = true;
+    *slot = pick;
+    *ptr = s.ptr;
+    return NS_OK;
+}
+
+ns_status staging_release(int slot, hipStream_t stream, bool copied) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Slot &s = g_slots[slot];
+    s.in_use = false;
+    if (copied) {
+        NSQ_HIP(hipEventRecord(s.done, stream));
+        s.pending = true;
+    }
+    return NS_OK;
+}
+
+}  // namespace nsq

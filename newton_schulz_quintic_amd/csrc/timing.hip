@@ -16,7 +16,7 @@ struct Rec {
     bool closed;
 };
 std::mutex g_mu;
-bool g_enabled = false;
+uint32_t g_mask = 0;   // bit k: record launches of kind k
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -34,12 +34,12 @@ hipEvent_t take_event() {
 
 bool timing_enabled() {
     std::lock_guard<std::mutex> lk(g_mu);
-    return g_enabled;
+    return g_mask != 0;
 }
 
 int timing_start(int kind, hipStream_t stream, double work) {
     std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_enabled) return -1;
+    if (kind < 0 || kind >= kTimeKinds || !(g_mask & (1u << kind))) return -1;
     Rec r{take_event(), take_event(), kind, work, false};
     if (!r.start || !r.stop) return -1;
     if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
@@ -58,9 +58,9 @@ void timing_stop(int slot, hipStream_t stream) {
 
 using namespace nsq;
 
-extern "C" ns_status ns_timing_enable(int32_t enable) {
+extern "C" ns_status ns_timing_enable(int32_t kinds) {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_enabled = enable != 0;
+    g_mask = kinds == -1 ? (1u << kTimeKinds) - 1 : (uint32_t)kinds & ((1u << kTimeKinds) - 1);
     return NS_OK;
 }
 
