@@ -8,28 +8,30 @@
 // NS and SYRK (symmetric) kernels.
 //
 // Design (one GPU, every matrix of a group in flight at once):
-//  * Workspace per matrix, padded to multiples of 128 in both dims and kept
-//    zero in the padding: X and X^T (two copies each, ping-pong), A and B.
+//  * Workspace per matrix, oriented so m <= n, padded to multiples of 256 in
+//    both dims and kept zero in the padding: X (two copies, ping-pong), A and B.
 //    Padding removes every bounds check from the product main loop; zero
 //    padding stays zero through every step (products with zero rows/cols).
-//  * All three products have the form C = P Q^T with P and Q row-major and
-//    contiguous along the contraction (K) axis:
-//        A   = X X^T  : P = Q = X
-//        A A          : P = Q = A          (A is symmetric, so A A = A A^T)
-//        B X          : P = B, Q = X^T     (X^T kept as its own array)
-//    so one MFMA main loop serves all of them: 128x128 output tiles, 4 waves of
-//    64x64, K panels of 128 bytes staged through double-buffered, padded LDS.
+//  * All three products run one MFMA main loop, C = P Q^T over K panels staged
+//    global -> LDS by buffer_load ... lds, kStages deep:
+//        A   = X X^T  : P = Q = X, both read along their rows (K-major)
+//        A A          : P = Q = A, K-major (A A = A A^T, A symmetric)
+//        B X          : P = B K-major; Q = X read N-major (rows of X are K) and
+//                       turned into MFMA operands with LDS transpose reads,
+//                       so no transposed copy of X is ever written.
+//    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups).
 //  * The symmetric products compute only tiles on or above the diagonal and
 //    store each off-diagonal tile twice (itself and its mirror), so A and B are
 //    exactly symmetric.
-//  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X
-//    (written as X' and X'^T; a final copy kernel moves X or X^T to the output in the
-//    input's orientation, shape and dtype).
+//  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X.
+//    The last step's epilogue writes straight to the caller's output in the
+//    input's orientation, shape and dtype.
 //  * Norm: per-chunk fp32 sums of squares in a fixed order (no atomics), then a
-//    tile pass that reduces the partials, scales, and writes X0 and X0^T
-//    (transposing tall inputs through LDS).
+//    tile pass that reduces the partials, scales, and writes X0 (transposing
+//    tall inputs through LDS).
 //  * Workgroup ids are remapped so consecutive tiles land on the same XCD (the
-//    hardware hands workgroups to the 8 XCDs round-robin), sharing its L2.
+//    hardware hands workgroups to the 8 XCDs round-robin), sharing its L2, and
+//    tiles are taken in groups of 4 x 8 so a run of tiles reuses operand panels.
 
 #include <algorithm>
 #include <cmath>
@@ -47,7 +49,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
-constexpr int kThreads = 256;       // 4 waves, 2 x 2 over the output tile
+constexpr int kThreads = 256;       // threads of the norm kernels
 constexpr int kRowBytes = 64;       // K bytes per LDS panel row per stage (32 bf16 / 16 f32)
 #ifndef NSQ_STAGES
 #define NSQ_STAGES 4
@@ -549,8 +551,7 @@ __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb 
     if (threadIdx.x == 0) pr.partials[np_.part] = total;
 }
 
-// Scale and write one 64x64 tile of X0 (mp x np) and
-// X0^T, zero in the padding. With write_out (steps == 0) the scaled input goes
+// Scale and write one 64x64 tile of X0 (mp x np), zero in the padding. With write_out (steps == 0) the scaled input goes
 // straight to the output instead.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *__restrict__ probs,
