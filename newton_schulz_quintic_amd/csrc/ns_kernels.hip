@@ -9,26 +9,30 @@
 //
 // Design (one GPU, every matrix of a group in flight at once):
 //  * Workspace per matrix, oriented so m <= n, padded to multiples of 256 in
-//    both dims and kept zero in the padding: X (two copies, ping-pong), A and B.
-//    Padding removes every bounds check from the product main loop; zero
-//    padding stays zero through every step (products with zero rows/cols).
-//  * All three products run one MFMA main loop, C = P Q^T over K panels staged
-//    global -> LDS by buffer_load ... lds, kStages deep:
-//        A   = X X^T  : P = Q = X, both read along their rows (K-major)
-//        A A          : P = Q = A, K-major (A A = A A^T, A symmetric)
-//        B X          : P = B K-major; Q = X read N-major (rows of X are K) and
-//                       turned into MFMA operands with LDS transpose reads,
-//                       so no transposed copy of X is ever written.
+//    both dims and kept zero in the padding: X and its transpose X^T (two
+//    copies of each, ping-pong), A and B. Padding removes every bounds check
+//    from the product main loop; zero padding stays zero through every step
+//    (products with zero rows/cols).
+//  * All three products run one MFMA main loop, C = P Q^T over K panels, with
+//    both operands read along their rows (K contiguous):
+//        A   = X X^T  : P = Q = X
+//        A A          : P = Q = A       (A A = A A^T, A symmetric)
+//        B X          : P = B, Q = X^T  (B X = B (X^T)^T)
+//    Panels of 128 bytes of K per row go global -> LDS with buffer_load ... lds
+//    into two stage buffers; every wave loads a slice of both panels.
 //    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups).
 //  * The symmetric products compute only tiles on or above the diagonal and
 //    store each off-diagonal tile twice (itself and its mirror), so A and B are
 //    exactly symmetric.
 //  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X.
-//    The last step's epilogue writes straight to the caller's output in the
-//    input's orientation, shape and dtype.
+//    The rounded tile is staged in LDS column-major; the tile is then written
+//    row-major through LDS transpose reads and column-major (the mirror, or
+//    X'^T) from plain LDS rows, both as 16-byte stores. The last step's
+//    epilogue writes straight to the caller's output in the input's
+//    orientation, shape and dtype.
 //  * Norm: per-chunk fp32 sums of squares in a fixed order (no atomics), then a
-//    tile pass that reduces the partials, scales, and writes X0 (transposing
-//    tall inputs through LDS).
+//    tile pass that reduces the partials, scales, and writes X0 and X0^T
+//    (transposing tall inputs through LDS).
 //  * Workgroup ids are remapped so consecutive tiles land on the same XCD (the
 //    hardware hands workgroups to the 8 XCDs round-robin), sharing its L2, and
 //    tiles are taken in groups of 4 x 8 so a run of tiles reuses operand panels.
@@ -47,30 +51,26 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
 constexpr int kThreads = 256;       // threads of the norm kernels
-constexpr int kRowBytes = 64;       // K bytes per LDS panel row per stage (32 bf16 / 16 f32)
-#ifndef NSQ_STAGES
-#define NSQ_STAGES 4
-#endif
-constexpr int kStages = NSQ_STAGES; // LDS pipeline depth (kStages - 1 panels in flight)
+constexpr int kRowBytes = 128;      // K bytes per LDS panel row per stage (64 bf16 / 32 f32)
 constexpr int kNormChunk = 16384;   // minimum elements per norm partial
 constexpr int kMaxParts = kThreads; // at most one partial per thread of the apply reduction
 constexpr int kNormTile = 64;       // norm apply tile edge
 constexpr int kNumXcd = 8;
-#ifndef NSQ_ROW_PAD_BYTES
-#define NSQ_ROW_PAD_BYTES 256
-#endif
 // Every workspace row is padded by this many bytes past its padded width, so
-// the row stride is an odd multiple of 256 bytes: a K panel (the same 64 bytes
-// of 256 consecutive rows) then spreads over all L2 channels instead of
-// landing on one or two of them, as a power-of-two stride makes it do.
-constexpr int kRowPadBytes = NSQ_ROW_PAD_BYTES;
+// the row stride is an odd multiple of 256 bytes: a K panel (the same bytes of
+// 256 consecutive rows) then spreads over the L2 channels instead of landing
+// on a few of them, as a power-of-two stride makes it do.
+constexpr int kRowPadBytes = 256;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
     char *x0, *x1;     // X ping/pong: mp x np (row stride ldx)
+    char *xt0, *xt1;   // X^T ping/pong: np x mp (row stride ldxt)
     char *a;           // A: mp x mp (row stride ldt)
     char *b;           // B: mp x mp (row stride ldt)
     const char *in;    // input, rows x cols
@@ -78,8 +78,9 @@ struct NsProb {
     float *partials;   // nparts (<= kMaxParts) fp32 partial sums of squares
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
-    int32_t ldx;       // row stride of X (elements, >= np)
-    int32_t ldt;       // row stride of A and B (elements, >= mp)
+    int32_t ldx;       // row stride of X (elements, > np)
+    int32_t ldxt;      // row stride of X^T (elements, > mp)
+    int32_t ldt;       // row stride of A and B (elements, > mp)
     int32_t tall;      // input had rows > cols
     int32_t nparts;
     int32_t chunk;     // input elements per partial (a multiple of 8)
@@ -133,8 +134,7 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 enum Mode { kSyrkX = 0, kSyrkA = 1, kGemmBX = 2 };
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
-// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
-// panels of kRowBytes per row, kStages deep.
+// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks.
 template <int BM_, int WM_, int WN_> struct TileCfg {
     static constexpr int BM = BM_, WM = WM_, WN = WN_;
     static constexpr int WAVES = WM * WN;
@@ -143,157 +143,43 @@ template <int BM_, int WM_, int WN_> struct TileCfg {
     static constexpr int NBN = BM / WN / 32;    // ... column direction
     static constexpr int PANEL = BM * kRowBytes;
     static constexpr int STAGE = 2 * PANEL;     // P panel then Q panel
-    static constexpr int LDS = kStages * STAGE;
+    static constexpr int LDS = 2 * STAGE;       // two stage buffers
     static constexpr int RPW = BM / WAVES;      // panel rows each wave loads
-    static constexpr int LOADS = RPW / 16;      // 1 KiB loads per wave per panel
-    static constexpr int KG = kRowBytes / 32;   // k-groups (one MFMA K step each) per stage
-    static_assert(RPW % 16 == 0, "each wave loads whole 16-row groups");
+    static constexpr int RPI = 1024 / kRowBytes;  // panel rows per 1 KiB wave load
+    static constexpr int LOADS = RPW / RPI;     // loads per wave per panel
+    static constexpr int KG = kRowBytes / 32;   // k-groups (one 32-byte MFMA K step each) per stage
+    static_assert(RPW % RPI == 0, "each wave loads whole 8-row groups");
 };
 typedef TileCfg<256, 2, 4> Big;    // 8 waves, 2 per SIMD, 128 x 64 per wave
 typedef TileCfg<128, 2, 2> Small;  // 4 waves, 64 x 64 per wave (two workgroups per CU)
 
-// vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
+// Operand staging. Each stage holds, per operand, kRowBytes bytes of K for
+// each of the tile's BM rows. Panel row r sits at r * 128 bytes; its 16-byte
+// chunk c (8 bf16 / 4 f32 consecutive k) sits in slot c ^ swz(r),
+// swz(r) = (r >> 1) & 7, so the fragment reads (32 consecutive rows, one chunk
+// each) hit distinct banks in every 16 lanes. Global -> LDS uses
+// buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l, so each lane fetches
+// whatever global chunk belongs at its LDS slot; one wave instruction moves
+// 8 rows x 128 bytes.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Operand staging. Each stage holds, per operand, the K slice of kRowBytes
-// bytes for each of the tile's BM rows (16 KiB for the 256 tile), in one of
-// two layouts:
-//
-//  KMAJOR -- the operand's own rows, K contiguous (A = X X^T reads X this way).
-//    Panel row r at r * 64 bytes; its 16-byte chunk c (8 bf16 / 4 f32
-//    consecutive k) sits in slot c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1),
-//    so the fragment reads (32 consecutive rows, one chunk each) hit distinct
-//    banks in every 8 lanes (32 banks) and every 16 lanes (64 banks). Each wave
-//    instruction moves 16 rows x 64 bytes.
-//
-//  NMAJOR -- the K rows of the source matrix, the tile's BM columns contiguous:
-//    KPS = 64 / es rows of RB = BM * es bytes. Used where the operand's rows are
-//    the source's columns: X in B X (B X needs X[k][j]), and the symmetric A and
-//    B (A[i][k] = A[k][i]). Each wave instruction moves whole 512-byte row
-//    stretches, and no transposed copy of X is kept. The 16-byte unit u of row r
-//    sits at unit position u ^ (2 (r % 4)). bf16 fragments come out with
-//    ds_read_b64_tr_b16: in each group of 16 lanes, lane i points at row
-//    k0 + i/4, columns n0 + 4 (i % 4), and lane j receives column n0 + j, rows
-//    k0 .. k0+3; two such reads give the 8 consecutive k of an MFMA operand.
-//    f32 fragments are four 4-byte reads.
-//
-// Global -> LDS uses buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l,
-// so each lane fetches whatever global 16 bytes belong at its LDS slot.
-template <class C, int ES, bool NM> struct Stage {
-    static constexpr int KPS = kRowBytes / ES;        // K rows per stage (NMAJOR)
-    static constexpr int RB = C::BM * ES;             // bytes per NMAJOR row
-    static constexpr int RPI = 1024 / RB;             // NMAJOR rows per 1 KiB load
-    static_assert(!NM || (RB >= 128 && 1024 % RB == 0), "NMAJOR row size");
-};
-
-template <class C, int ES, bool NM>
-__device__ __forceinline__ void operand_offsets(int lane, int wave, int ld, int (&voff)[C::LOADS]) {
-    if constexpr (!NM) {
-        const int lrow = wave * C::RPW + (lane >> 2);
-        const int lf = ((lane >> 3) & 3) ^ ((lane >> 5) & 1);          // f(lrow)
-        const int off = lrow * ld + (((lane & 3) ^ lf) << 4);
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) voff[i] = off + i * 16 * ld;
-    } else {
-        typedef Stage<C, ES, NM> S;
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int g = wave * C::LOADS + i;                          // 1 KiB block of the stage
-            const int r = g * S::RPI + (lane * 16) / S::RB;             // K row within the stage
-            const int p = ((lane * 16) % S::RB) >> 4;                   // unit position in the row
-            voff[i] = r * ld + ((p ^ (2 * (r & 3))) << 4);
-        }
-    }
-}
-
-// Loads of one operand's stage kb into `region` (one LDS stage slot).
-template <class C>
-__device__ __forceinline__ void operand_issue_kmajor(__amdgpu_buffer_rsrc_t rs, const int *voff, int kb,
-                                                     char *region, int wave) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (NSQ_LDS void *)(region + wave * C::RPW * kRowBytes + i * 1024), 16, voff[i], kb * kRowBytes,
-            0, 0);
-}
-
-template <class C, int ES>
-__device__ __forceinline__ void operand_issue_nmajor(__amdgpu_buffer_rsrc_t rs, const int *voff, int ld,
-                                                     int kb, char *region, int wave) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)(region + (wave * C::LOADS + i) * 1024),
-                                                 16, voff[i], kb * Stage<C, ES, true>::KPS * ld, 0, 0);
-}
-
-// Both operands' loads of stage kb into LDS slot kb % kStages.
-template <class C, int ES, bool PNM, bool QNM>
-__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
-                                            const int (&voff_p)[C::LOADS], const int (&voff_q)[C::LOADS],
-                                            int ldp, int ldq, int kb, char *lds, int wave) {
-    char *sb = lds + (kb % kStages) * C::STAGE;
-    if constexpr (PNM)
-        operand_issue_nmajor<C, ES>(rp, voff_p, ldp, kb, sb, wave);
-    else
-        operand_issue_kmajor<C>(rp, voff_p, kb, sb, wave);
-    if constexpr (QNM)
-        operand_issue_nmajor<C, ES>(rq, voff_q, ldq, kb, sb + C::PANEL, wave);
-    else
-        operand_issue_kmajor<C>(rq, voff_q, kb, sb + C::PANEL, wave);
-}
-
-// MFMA operand fragment for the 32-row block starting at tile row `blk`,
-// k-group kg of the stage: lane l gets row blk + l%32, k = 8 (l/32) + e.
-template <typename T, class C, bool NM>
-__device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *region, int lane, int blk,
-                                                             int kg) {
+// MFMA operand fragment for the 32-row block starting at panel row `blk`,
+// k-group kg of the stage: lane l gets row blk + l%32, chunk 2 kg + l/32.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *region, int lane, int blk, int kg) {
     typedef typename Mfma<T>::frag frag;
-    if constexpr (!NM) {
-        const int row = blk + (lane & 31);
-        const int xf = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);       // f(row)
-        return *reinterpret_cast<const frag *>(region + row * kRowBytes + (((2 * kg + (lane >> 5)) ^ xf) << 4));
-    } else if constexpr (sizeof(T) == 2) {
-        typedef Stage<C, 2, true> S;
-        typedef short s4 __attribute__((ext_vector_type(4)));
-        const int i = lane & 15, g = lane >> 4;
-        const int col = blk + 16 * (g & 1) + 4 * (i & 3);          // element column in the tile
-        const int unit = col >> 3, half = (col >> 2) & 1;
-        s4 v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kl = 16 * kg + 8 * (g >> 1) + 4 * h + (i >> 2);
-            const char *a = region + kl * S::RB + ((unit ^ (2 * (kl & 3))) << 4) + half * 8;
-            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s4 *)a);
-        }
-        typedef short s8 __attribute__((ext_vector_type(8)));
-        const s8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-        return __builtin_bit_cast(frag, w);
-    } else {
-        typedef Stage<C, 4, true> S;
-        const int col = blk + (lane & 31);
-        const int unit = col >> 2, within = (col & 3) * 4;
-        frag f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int kl = 8 * kg + 4 * (lane >> 5) + e;
-            f[e] = *reinterpret_cast<const float *>(region + kl * S::RB + ((unit ^ (2 * (kl & 3))) << 4) + within);
-        }
-        return f;
-    }
+    const int row = blk + (lane & 31);
+    const int c = 2 * kg + (lane >> 5);
+    return *reinterpret_cast<const frag *>(region + row * kRowBytes + ((c ^ swz(row)) << 4));
 }
 
 // acc = P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
-// first operand row (KMAJOR) or first column (NMAJOR); ld in bytes; `extent`
-// is the byte size the buffer resources may address from P and Q.
-template <typename T, class C, bool PNM, bool QNM>
+// first operand row; ldp, ldq are row strides in bytes; `extent_*` is the byte
+// size the buffer resources may address from P and Q.
+template <typename T, class C>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
-                                             int extent_q, int nk, char *lds,
-                                             f32x16 (&acc)[C::NBM][C::NBN]) {
+                                             int extent_q, int nk, char *lds, f32x16 (&acc)[C::NBM][C::NBN]) {
     typedef typename Mfma<T>::frag frag;
-    constexpr int ES = sizeof(T);
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -310,45 +196,50 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
     const __amdgpu_buffer_rsrc_t rq =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, extent_q, 0x00020000);
     int voff_p[C::LOADS], voff_q[C::LOADS];
-    operand_offsets<C, ES, PNM>(lane, wave, ldp, voff_p);
-    operand_offsets<C, ES, QNM>(lane, wave, ldq, voff_q);
-    const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
-
-    constexpr int L = 2 * C::LOADS;   // loads per wave per stage
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < nk) issue_stage<C, ES, PNM, QNM>(rp, rq, voff_p, voff_q, ldp, ldq, s, lds, wave);
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int row = wave * C::RPW + i * C::RPI + (lane >> 3);
+        const int chunk = ((lane & 7) ^ swz(row)) << 4;
+        voff_p[i] = row * ldp + chunk;
+        voff_q[i] = row * ldq + chunk;
+    }
+    const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
+    // This wave's loads of stage kb: rows [wave RPW, (wave + 1) RPW) of both
+    // panels into stage buffer kb % 2, 8 rows x 128 bytes per instruction.
+    auto issue = [&](int kb) {
+        char *sp = lds + (kb & 1) * C::STAGE + wave * C::RPW * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sp + i * C::RPI * kRowBytes), 16,
+                                                     (int)voff_p[i], kb * kRowBytes, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sp + C::PANEL + i * C::RPI * kRowBytes),
+                                                     16, (int)voff_q[i], kb * kRowBytes, 0, 0);
+    };
+
+    if (nk > 0) issue(0);
     for (int kb = 0; kb < nk; ++kb) {
-        // this wave's loads for stage kb have landed (later stages may still fly)
-        const int ahead = min(nk - 1 - kb, kStages - 2);
-        if (ahead >= 3)
-            wait_vmcnt<(kStages >= 5 ? 3 : 0) * L>();
-        else if (ahead == 2)
-            wait_vmcnt<2 * L>();
-        else if (ahead == 1)
-            wait_vmcnt<L>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();   // every wave's stage kb is in LDS; buffer (kb-1) % kStages is free
-        if (kb + kStages - 1 < nk)
-            issue_stage<C, ES, PNM, QNM>(rp, rq, voff_p, voff_q, ldp, ldq, kb + kStages - 1, lds, wave);
-        const char *sp = lds + (kb % kStages) * C::STAGE, *sq = sp + C::PANEL;
+        // Every wave's loads of stage kb have landed (the barrier waits for
+        // this wave's outstanding loads) and every wave is done with stage
+        // kb - 1, whose buffer the next loads overwrite.
+        __syncthreads();
+        if (kb + 1 < nk) issue(kb + 1);
+        const char *sp = lds + (kb & 1) * C::STAGE, *sq = sp + C::PANEL;
         // fragments for k-group kg + 1 are read while the MFMAs of kg run
         frag fa[2][C::NBM], fb[2][C::NBN];
 #pragma unroll
-        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, C, PNM>(sp, lane, a_blk + 32 * i, 0);
+        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T>(sp, lane, a_blk + 32 * i, 0);
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T, C, QNM>(sq, lane, b_blk + 32 * j, 0);
+        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T>(sq, lane, b_blk + 32 * j, 0);
 #pragma unroll
         for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
             if (kg + 1 < C::KG) {
 #pragma unroll
-                for (int i = 0; i < C::NBM; ++i)
-                    fa[nb][i] = operand_frag<T, C, PNM>(sp, lane, a_blk + 32 * i, kg + 1);
+                for (int i = 0; i < C::NBM; ++i) fa[nb][i] = operand_frag<T>(sp, lane, a_blk + 32 * i, kg + 1);
 #pragma unroll
-                for (int j = 0; j < C::NBN; ++j)
-                    fb[nb][j] = operand_frag<T, C, QNM>(sq, lane, b_blk + 32 * j, kg + 1);
+                for (int j = 0; j < C::NBN; ++j) fb[nb][j] = operand_frag<T>(sq, lane, b_blk + 32 * j, kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
@@ -359,17 +250,108 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
     }
 }
 
-// Store 4 consecutive-row values of one column into a row-major array at
-// [col][row..row+3] (the mirror / transposed copy), as one vector store.
-template <typename T>
-__device__ __forceinline__ void store4(char *base, int ld, int col, int row, const T v[4]) {
-    NSQ_GLOBAL T *p = gp<T>(base) + (int64_t)col * ld + row;
+// --- epilogue staging ------------------------------------------------------
+// The rounded tile D (BM x BM, D[r][c]) is staged column-major: LDS row c holds
+// D[0..BM)[c] (BM * es bytes), its 16-byte unit u at unit position
+// u ^ swt(c). swt maps 16 consecutive columns to 16 distinct positions, so the
+// staging writes (32 consecutive columns, 8 or 16 bytes each) spread over the
+// banks, and it maps 4 consecutive columns to positions that differ in bits 1-2,
+// so a transpose read (4 columns x 32 bytes) touches 8 distinct positions.
+__device__ __forceinline__ int swt(int c) { return ((c & 3) << 1) | (((c >> 2) & 1) << 3) | ((c >> 3) & 1); }
+
+template <typename T, int BM>
+__device__ __forceinline__ int stage_off(int c, int r) {   // byte offset of D[r][c]
+    const int byte = r * (int)sizeof(T);
+    return c * (BM * (int)sizeof(T)) + ((((byte >> 4) ^ swt(c)) << 4) | (byte & 15));
+}
+
+// D[r..r+3][c] = v into the staging area.
+template <typename T, int BM>
+__device__ __forceinline__ void stage4(char *lds, int r, int c, const float v[4]) {
+    char *p = lds + stage_off<T, BM>(c, r);
     if constexpr (sizeof(T) == 2) {
         typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-        *(NSQ_GLOBAL b4 *)p = b4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<b4 *>(p) = b4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     } else {
-        *(NSQ_GLOBAL f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
     }
+}
+
+// Row-major chunks of D: 16 bytes of row r starting at column c.
+//   bf16: blocks of 16 rows x 32 columns; lane (t = l % 16, g = l / 16) takes
+//         row r0 + t, columns c0 + 8 g .. + 8, from two LDS transpose reads:
+//         lane t addresses column c + t / 4, rows r0 + 4 (t % 4) .. + 4 of the
+//         staging, and receives rows r0 + t of columns c .. c + 3.
+//   f32:  blocks of 16 rows x 16 columns; lane (t, g) takes row r0 + t,
+//         columns c0 + 4 g .. + 4, from four 4-byte reads.
+template <typename T, int BM> struct RowChunks {
+    static constexpr int BCOLS = sizeof(T) == 2 ? 32 : 16;
+    static constexpr int BLOCKS = (BM / 16) * (BM / BCOLS);
+};
+
+template <typename T, int BM>
+__device__ __forceinline__ i32x4 row_chunk(const char *lds, int blk, int lane, int &r, int &c) {
+    constexpr int BC = RowChunks<T, BM>::BCOLS;
+    const int t = lane & 15, g = lane >> 4;
+    const int r0 = (blk % (BM / 16)) * 16, c0 = (blk / (BM / 16)) * BC;
+    r = r0 + t;
+    if constexpr (sizeof(T) == 2) {
+        c = c0 + 8 * g;
+        s16x4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const char *a = lds + stage_off<T, BM>(c + 4 * h + (t >> 2), r0 + 4 * (t & 3));
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)a);
+        }
+        const s16x4 lo = v[0], hi = v[1];
+        i32x4 w;
+        w[0] = (int)(uint16_t)lo[0] | ((int)(uint16_t)lo[1] << 16);
+        w[1] = (int)(uint16_t)lo[2] | ((int)(uint16_t)lo[3] << 16);
+        w[2] = (int)(uint16_t)hi[0] | ((int)(uint16_t)hi[1] << 16);
+        w[3] = (int)(uint16_t)hi[2] | ((int)(uint16_t)hi[3] << 16);
+        return w;
+    } else {
+        c = c0 + 4 * g;
+        i32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const int *>(lds + stage_off<T, BM>(c + e, r));
+        return w;
+    }
+}
+
+// Column-major chunks of D (rows of the staging): 16 bytes of column c
+// starting at row r = 16 u / es.
+template <typename T, int BM>
+__device__ __forceinline__ i32x4 col_chunk(const char *lds, int idx, int &c, int &r) {
+    constexpr int NU = BM * (int)sizeof(T) / 16;
+    c = idx / NU;
+    const int u = idx % NU;
+    r = u * (16 / (int)sizeof(T));
+    return *reinterpret_cast<const i32x4 *>(lds + c * (BM * (int)sizeof(T)) + ((u ^ swt(c)) << 4));
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(char *base, int64_t elem, i32x4 w) {
+    *(NSQ_GLOBAL i32x4 *)(base + elem * (int64_t)sizeof(T)) = w;
+}
+
+// Bounds-checked store of the 16 / es elements of chunk w starting at
+// dst[row][col] of a rows x cols row-major array.
+template <typename T>
+__device__ __forceinline__ void store_chunk_checked(char *dst, int64_t rows, int64_t cols, int64_t row, int64_t col,
+                                                    i32x4 w, bool vec_ok) {
+    constexpr int E = 16 / (int)sizeof(T);
+    if (row >= rows || col >= cols) return;
+    if (vec_ok && col + E <= cols) {
+        store16<T>(dst, row * cols + col, w);
+        return;
+    }
+    T vals[E];
+    __builtin_memcpy(vals, &w, 16);
+    NSQ_GLOBAL T *p = gp<T>(dst) + row * cols;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (col + e < cols) p[col + e] = vals[e];
 }
 
 // Load [col][row..row+3] of a row-major array as 4 floats.
@@ -387,103 +369,120 @@ __device__ __forceinline__ void load4(const char *base, int ld, int col, int row
 }
 
 // One product launch: MODE picks the operands and epilogue.
-//   kSyrkX : A = X X^T            P = Q = X (KMAJOR)        upper tiles, mirrored
-//   kSyrkA : B = b A + c A A^T    P = Q = A (KMAJOR)        upper tiles, mirrored
-//   kGemmBX: X' = a X + B X       P = B (KMAJOR), Q = X (NMAJOR)
+//   kSyrkX : A = X X^T            P = X, Q = X       upper tiles, mirrored
+//   kSyrkA : B = b A + c A A^T    P = A, Q = A       upper tiles, mirrored
+//   kGemmBX: X' = a X + B X       P = B, Q = X^T     writes X' and X'^T
 // LAST (kGemmBX only): the final step writes a X + B X straight to the
 // caller's output in the input's orientation instead of into the workspace.
 template <typename T, class C, int MODE, bool LAST>
-__global__ __launch_bounds__(C::THREADS, 1) void ns_product_kernel(const NsProb *__restrict__ probs,
-                                                                 const TileRef *__restrict__ tiles,
-                                                                 int32_t ntiles, int32_t cur, float ca,
-                                                                 float cb, float cc) {
+__global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
+    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur, float ca,
+    float cb, float cc) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
+    static_assert(BM * BM * ES <= C::LDS, "the staged tile fits the operand buffers");
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
     const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
     if (tile_id >= ntiles) return;
     const TileRef tr = tiles[tile_id];
     const NsProb &pr = probs[tr.prob];
-    const int mp = pr.mp, np = pr.np, m = pr.m, n = pr.n;
+    const int mp = pr.mp, np = pr.np;
     const int row0 = tr.ti * BM, col0 = tr.tj * BM;
-    const int ldx = pr.ldx, ldt = pr.ldt;
+    const int ldx = pr.ldx, ldxt = pr.ldxt, ldt = pr.ldt;
     char *xc = cur ? pr.x1 : pr.x0;
     char *xn = cur ? pr.x0 : pr.x1;
+    char *xtc = cur ? pr.xt1 : pr.xt0;
+    char *xtn = cur ? pr.xt0 : pr.xt1;
     char *A = pr.a, *B = pr.b;
 
     f32x16 acc[C::NBM][C::NBN];
     if constexpr (MODE == kSyrkX) {
         const int ld = ldx * ES;
-        tile_product<T, C, false, false>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld,
-                                         BM * ld, np * ES / kRowBytes, lds, acc);
+        tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+                           np * ES / kRowBytes, lds, acc);
     } else if constexpr (MODE == kSyrkA) {
         const int ld = ldt * ES;
         const int nk = cc == 0.f ? 0 : mp * ES / kRowBytes;   // c == 0: B = b A needs no product
-        tile_product<T, C, false, false>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld,
-                                         BM * ld, nk, lds, acc);
+        tile_product<T, C>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk, lds, acc);
     } else {
-        const int ldb = ldt * ES;
-        tile_product<T, C, false, true>(B + (int64_t)row0 * ldb, xc + (int64_t)col0 * ES, ldb, ldx * ES,
-                                        BM * ldb, mp * ldx * ES, mp * ES / kRowBytes, lds, acc);
+        const int ldb = ldt * ES, ldq = ldxt * ES;
+        tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
+                           mp * ES / kRowBytes, lds, acc);
     }
 
-    // Epilogue. Accumulator element (i, j, v) of this lane sits at tile row
-    // wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32) + v%4 and tile column wn*BM/WN + 32 j + lane%32.
+    // Epilogue, part 1: fp32 arithmetic, rounding, staging. Accumulator element
+    // (i, j, v) of this lane sits at tile row wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32)
+    // + v%4 and tile column wn*BM/WN + 32 j + lane%32.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
-    const bool mirror = tr.ti != tr.tj;
-    const bool out_vec = (m & 3) == 0 && (reinterpret_cast<uintptr_t>(pr.out) & (4 * ES - 1)) == 0;
+    __syncthreads();   // every wave is done reading operand panels
 #pragma unroll
     for (int i = 0; i < C::NBM; ++i) {
 #pragma unroll
         for (int j = 0; j < C::NBN; ++j) {
-            const int gc = col0 + wn * (BM / C::WN) + j * 32 + (lane & 31);
+            const int c = wn * (BM / C::WN) + j * 32 + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int gr = row0 + wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
-                T val[4];
+                const int r = wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
+                float v[4];
                 if constexpr (MODE == kSyrkX) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = from_f32<T>(acc[i][j][4 * q + e]);
-                    NSQ_GLOBAL T *D = gp<T>(A);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldt + gc] = val[e];
-                    if (mirror) store4<T>(A, ldt, gc, gr, val);
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
                 } else if constexpr (MODE == kSyrkA) {
                     float old[4];
-                    load4<T>(A, ldt, gc, gr, old);   // A[gr+e][gc] == A[gc][gr+e]: A is symmetric
+                    load4<T>(A, ldt, col0 + c, row0 + r, old);   // A[r][c] == A[c][r]: A is symmetric
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = from_f32<T>(cb * old[e] + cc * acc[i][j][4 * q + e]);
-                    NSQ_GLOBAL T *D = gp<T>(B);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldt + gc] = val[e];
-                    if (mirror) store4<T>(B, ldt, gc, gr, val);
+                    for (int e = 0; e < 4; ++e) v[e] = cb * old[e] + cc * acc[i][j][4 * q + e];
                 } else {
-                    const NSQ_GLOBAL T *X = gp<T>(xc);
+                    float old[4];
+                    load4<T>(xtc, ldxt, col0 + c, row0 + r, old);   // X[r][c] == X^T[c][r]
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        val[e] = from_f32<T>(ca * to_f32<T>(X[(int64_t)(gr + e) * ldx + gc]) + acc[i][j][4 * q + e]);
-                    if constexpr (!LAST) {
-                        NSQ_GLOBAL T *D = gp<T>(xn);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) D[(int64_t)(gr + e) * ldx + gc] = val[e];
-                    } else if (gc < n) {
-                        NSQ_GLOBAL T *O = gp<T>(pr.out);
-                        if (pr.tall) {                 // out is n x m: row gc, columns gr..gr+3
-                            if (out_vec && gr + 3 < m) {
-                                store4<T>(pr.out, m, gc, gr, val);
-                            } else {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    if (gr + e < m) O[(int64_t)gc * m + gr + e] = val[e];
-                            }
-                        } else {                       // out is m x n
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (gr + e < m) O[(int64_t)(gr + e) * n + gc] = val[e];
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = ca * old[e] + acc[i][j][4 * q + e];
                 }
+                stage4<T, BM>(lds, r, c, v);
+            }
+        }
+    }
+    __syncthreads();
+
+    // Epilogue, part 2: write the staged tile.
+    constexpr int NU = BM * ES / 16;                 // 16-byte units per staged column
+    constexpr int COL_CHUNKS = BM * NU;
+    if constexpr (!LAST) {
+        // row-major: the tile itself (A, B or X'), at (row0, col0)
+        char *D = MODE == kSyrkX ? A : MODE == kSyrkA ? B : xn;
+        const int ldd = MODE == kGemmBX ? ldx : ldt;
+        for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
+            int r, c;
+            const i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
+            store16<T>(D, (int64_t)(row0 + r) * ldd + col0 + c, w);
+        }
+        // column-major: the mirror tile at (col0, row0), or X'^T
+        if (MODE == kGemmBX || tr.ti != tr.tj) {
+            char *E = MODE == kGemmBX ? xtn : D;
+            const int lde = MODE == kGemmBX ? ldxt : ldt;
+            for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
+                int c, r;
+                const i32x4 w = col_chunk<T, BM>(lds, idx, c, r);
+                store16<T>(E, (int64_t)(col0 + c) * lde + row0 + r, w);
+            }
+        }
+    } else {
+        const int m = pr.m, n = pr.n;
+        const bool aligned = (reinterpret_cast<uintptr_t>(pr.out) & 15) == 0;
+        if (!pr.tall) {   // out is m x n: row-major chunks
+            const bool vec_ok = aligned && ((int64_t)n * ES) % 16 == 0;
+            for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
+                int r, c;
+                const i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
+                store_chunk_checked<T>(pr.out, m, n, row0 + r, col0 + c, w, vec_ok);
+            }
+        } else {          // out is n x m: column-major chunks
+            const bool vec_ok = aligned && ((int64_t)m * ES) % 16 == 0;
+            for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
+                int c, r;
+                const i32x4 w = col_chunk<T, BM>(lds, idx, c, r);
+                store_chunk_checked<T>(pr.out, n, m, col0 + c, row0 + r, w, vec_ok);
             }
         }
     }
@@ -551,8 +550,9 @@ __global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb 
     if (threadIdx.x == 0) pr.partials[np_.part] = total;
 }
 
-// Scale and write one 64x64 tile of X0 (mp x np), zero in the padding. With write_out (steps == 0) the scaled input goes
-// straight to the output instead.
+// Scale and write one 64x64 tile of X0 (mp x np) and of X0^T (np x mp), zero
+// in the padding. With write_out (steps == 0) the scaled input goes straight to
+// the output instead.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles,
@@ -600,9 +600,11 @@ __global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *_
         return;
     }
     T *X = reinterpret_cast<T *>(pr.x0);
+    T *XT = reinterpret_cast<T *>(pr.xt0);
     for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
         const int a = e / kNormTile, b = e % kNormTile;
         X[(int64_t)(i0 + a) * pr.ldx + (j0 + b)] = from_f32<T>(tile[a][b]);
+        XT[(int64_t)(j0 + a) * pr.ldxt + (i0 + b)] = from_f32<T>(tile[b][a]);
     }
 }
 
@@ -622,8 +624,9 @@ struct MatInfo {
 
 // Row strides (elements) and array sizes of one matrix's workspace.
 inline int64_t ld_x(const MatInfo &mi, int64_t es) { return mi.np + kRowPadBytes / es; }
-inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }
+inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }   // A, B and X^T
 inline size_t x_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_x(mi, es) * es)); }
+inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.np * ld_t(mi, es) * es)); }
 inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
 
 ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info) {
@@ -643,7 +646,8 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.n = std::max(mi.rows, mi.cols);
         // tile indices are 16-bit; byte offsets inside one padded matrix are 32-bit
         if (mi.n > (int64_t)65535 * kNormTile ||
-            round_up(mi.m, kPad) * (round_up(mi.n, kPad) + kRowPadBytes / es) * es >= (1ll << 31))
+            round_up(mi.m, kPad) * (round_up(mi.n, kPad) + kRowPadBytes / es) * es >= (1ll << 31) ||
+            round_up(mi.n, kPad) * (round_up(mi.m, kPad) + kRowPadBytes / es) * es >= (1ll << 31))
             return fail(NS_ERR_OVERFLOW, "tensor %d: %lld x %lld is too large", i,
                         (long long)mi.rows, (long long)mi.cols);
         mi.mp = round_up(mi.m, kPad);
@@ -655,7 +659,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.norm_tiles = (mi.mp / kNormTile) * (mi.np / kNormTile);
         mi.chunk = std::max<int64_t>(kNormChunk, round_up((mi.m * mi.n + kMaxParts - 1) / kMaxParts, 8));
         mi.nparts = (mi.m * mi.n + mi.chunk - 1) / mi.chunk;
-        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * a_bytes(mi, es);
+        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
 }
@@ -692,8 +696,10 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
 }
 
 // Product tile edge for a group: 256 when the big tiles still give the GPU
-// enough workgroups, else 128. NS_TILE=128|256 overrides (tuning).
-int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &info) {
+// enough workgroups, else 128; f32 always uses 128 (its staged 256 x 256 tile
+// would not fit the LDS). NS_TILE=128|256 overrides for bf16 (tuning).
+int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &info, int64_t es) {
+    if (es == 4) return 128;
     if (const char *env = getenv("NS_TILE")) {
         const int v = atoi(env);
         if (v == 128 || v == 256) return v;
@@ -742,7 +748,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                     const void *const *in, void *const *out, int32_t steps, float a, float b,
                     float c, float eps, char *ws, const TableSizes &tsz, hipStream_t st) {
     const int64_t es = sizeof(T);
-    const int bm = pick_tile(group, info);
+    const int bm = pick_tile(group, info, es);
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, ntiles;
     std::vector<NormPart> parts;
@@ -753,10 +759,12 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
-        const size_t xb = x_bytes(mi, es), ab = a_bytes(mi, es);
+        const size_t xb = x_bytes(mi, es), xtb = xt_bytes(mi, es), ab = a_bytes(mi, es);
         p.x0 = base;
         p.x1 = p.x0 + xb;
-        p.a = p.x1 + xb;
+        p.xt0 = p.x1 + xb;
+        p.xt1 = p.xt0 + xtb;
+        p.a = p.xt1 + xtb;
         p.b = p.a + ab;
         base += mi.buf_bytes;
         p.in = static_cast<const char *>(in[idx]);
@@ -770,6 +778,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.np = (int32_t)mi.np;
         p.ldx = (int32_t)ld_x(mi, es);
         p.ldt = (int32_t)ld_t(mi, es);
+        p.ldxt = (int32_t)ld_t(mi, es);
         p.tall = mi.tall;
         p.nparts = (int32_t)mi.nparts;
         const int32_t pid = (int32_t)probs.size();
@@ -785,7 +794,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += c != 0.f ? m * m * (m + 1) : 0.0;
         f_gemm += 2 * m * m * n;
-        norm_bytes += 2.0 * m * n * es + (double)mi.mp * (double)mi.np * es;
+        norm_bytes += 2.0 * m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
 
@@ -832,10 +841,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
             TimedScope ts(kind, st, work[mode]);
-            if (bm == 256)
-                launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
-            else
-                launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
+            if constexpr (sizeof(T) == 2) {
+                if (bm == 256) {
+                    launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
+                    continue;
+                }
+            }
+            launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
