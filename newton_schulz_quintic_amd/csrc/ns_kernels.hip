@@ -173,7 +173,7 @@ __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *regio
     return *reinterpret_cast<const frag *>(region + row * kRowBytes + ((c ^ swz(row)) << 4));
 }
 
-// acc = P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
+// acc += P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
 // first operand row; ldp, ldq are row strides in bytes; `extent_*` is the byte
 // size the buffer resources may address from P and Q.
 template <typename T, class C>
@@ -183,13 +183,6 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
-
-#pragma unroll
-    for (int i = 0; i < C::NBM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NBN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const __amdgpu_buffer_rsrc_t rp =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, extent_p, 0x00020000);
@@ -354,30 +347,88 @@ __device__ __forceinline__ void store_chunk_checked(char *dst, int64_t rows, int
         if (col + e < cols) p[col + e] = vals[e];
 }
 
-// Load [col][row..row+3] of a row-major array as 4 floats.
-template <typename T>
-__device__ __forceinline__ void load4(const char *base, int ld, int col, int row, float o[4]) {
-    const NSQ_GLOBAL T *p = gp<T>(base) + (int64_t)col * ld + row;
-    if constexpr (sizeof(T) == 2) {
-        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-        const b4 w = *(const NSQ_GLOBAL b4 *)p;
-        o[0] = (float)w[0], o[1] = (float)w[1], o[2] = (float)w[2], o[3] = (float)w[3];
-    } else {
-        const f32x4 w = *(const NSQ_GLOBAL f32x4 *)p;
-        o[0] = w[0], o[1] = w[1], o[2] = w[2], o[3] = w[3];
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NBM][C::NBN]) {
+#pragma unroll
+    for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NBN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+}
+
+// acc = s * M[row0 + r][col0 + c] for this wave's accumulator elements, M
+// row-major with row stride ld bytes. The BM x BM tile of M goes global -> LDS
+// first (coalesced, rows of BM * es bytes, the 16-byte unit u of row r at unit
+// position u ^ 2 (r % 4)); each lane then picks its accumulator layout (four
+// consecutive rows of one column) out of it: for bf16 with LDS transpose reads
+// (in each 16-lane group lane t addresses row r0 + t / 4, columns
+// c0 + 4 (t % 4) .. + 4, and receives rows r0 .. r0 + 3 of column c0 + t),
+// for f32 with four 4-byte reads. Ends with a barrier: the LDS is free again.
+template <typename T, class C>
+__device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int col0, float s, char *lds,
+                                         f32x16 (&acc)[C::NBM][C::NBN]) {
+    constexpr int ES = sizeof(T), RB = C::BM * ES, RPI = 1024 / RB, NI = C::BM / RPI / C::WAVES;
+    static_assert(C::BM % (RPI * C::WAVES) == 0, "whole 1 KiB loads per wave");
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const char *base = M + (int64_t)row0 * ld + (int64_t)col0 * ES;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, C::BM * ld, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int blk = wave * NI + i;                        // 1 KiB block of the staged tile
+        const int row = blk * RPI + (lane * 16) / RB;
+        const int pos = ((lane * 16) % RB) >> 4;              // unit position in the LDS row
+        const int voff = row * ld + ((pos ^ (2 * (row & 3))) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)(lds + blk * 1024), 16, voff, 0, 0, 0);
     }
+    __syncthreads();   // waits for this wave's loads, then for every wave's
+    auto at = [&](int r, int c) -> const char * {
+        const int byte = c * ES;
+        return lds + r * RB + ((((byte >> 4) ^ (2 * (r & 3)))) << 4) + (byte & 15);
+    };
+#pragma unroll
+    for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NBN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rb = wm * (C::BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
+                const int cb = wn * (C::BM / C::WN) + j * 32;
+                float old[4];
+                if constexpr (ES == 2) {
+                    const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & 1);
+                    const s16x4 w =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), c0 + 4 * (t & 3)));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);   // bf16 -> fp32
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, cb + (lane & 31)));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = s * old[e];
+            }
+    __syncthreads();   // every wave is done with the staged tile
 }
 
 // One product launch: MODE picks the operands and epilogue.
-//   kSyrkX : A = X X^T            P = X, Q = X       upper tiles, mirrored
-//   kSyrkA : B = b A + c A A^T    P = A, Q = A       upper tiles, mirrored
-//   kGemmBX: X' = a X + B X       P = B, Q = X^T     writes X' and X'^T
+//   kSyrkX : A = X X^T                     P = X, Q = X     upper tiles, mirrored
+//   kSyrkA : B = s_final (s_init A + A A^T)  P = A, Q = A     upper tiles, mirrored
+//   kGemmBX: X' = s_init X + B X           P = B, Q = X^T   writes X' and X'^T
+// The accumulators start at s_init times the old tile, so the epilogue needs
+// no second read of it: with (s_init, s_final) = (b / c, c), B = b A + c A A
+// up to fp32 rounding; when c == 0 (or b / c is not finite, where c A A is
+// below fp32 resolution of b A) the host passes (b, 1) and do_product = 0, so
+// B = b A. For B X, s_init = a.
 // LAST (kGemmBX only): the final step writes a X + B X straight to the
 // caller's output in the input's orientation instead of into the workspace.
 template <typename T, class C, int MODE, bool LAST>
 __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
-    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur, float ca,
-    float cb, float cc) {
+    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
+    float s_init, float s_final, int32_t do_product) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
     static_assert(BM * BM * ES <= C::LDS, "the staged tile fits the operand buffers");
@@ -397,20 +448,23 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 
     f32x16 acc[C::NBM][C::NBN];
     if constexpr (MODE == kSyrkX) {
+        zero_acc<C>(acc);
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                            np * ES / kRowBytes, lds, acc);
     } else if constexpr (MODE == kSyrkA) {
+        init_acc<T, C>(A, ldt * ES, row0, col0, s_init, lds, acc);
         const int ld = ldt * ES;
-        const int nk = cc == 0.f ? 0 : mp * ES / kRowBytes;   // c == 0: B = b A needs no product
+        const int nk = do_product ? mp * ES / kRowBytes : 0;
         tile_product<T, C>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk, lds, acc);
     } else {
+        init_acc<T, C>(xc, ldx * ES, row0, col0, s_init, lds, acc);
         const int ldb = ldt * ES, ldq = ldxt * ES;
         tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
                            mp * ES / kRowBytes, lds, acc);
     }
 
-    // Epilogue, part 1: fp32 arithmetic, rounding, staging. Accumulator element
+    // Epilogue, part 1: scaling, rounding, staging. Accumulator element
     // (i, j, v) of this lane sits at tile row wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32)
     // + v%4 and tile column wn*BM/WN + 32 j + lane%32.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -425,20 +479,9 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
             for (int q = 0; q < 4; ++q) {
                 const int r = wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
                 float v[4];
-                if constexpr (MODE == kSyrkX) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-                } else if constexpr (MODE == kSyrkA) {
-                    float old[4];
-                    load4<T>(A, ldt, col0 + c, row0 + r, old);   // A[r][c] == A[c][r]: A is symmetric
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = cb * old[e] + cc * acc[i][j][4 * q + e];
-                } else {
-                    float old[4];
-                    load4<T>(xtc, ldxt, col0 + c, row0 + r, old);   // X[r][c] == X^T[c][r]
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = ca * old[e] + acc[i][j][4 * q + e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    v[e] = MODE == kSyrkA ? s_final * acc[i][j][4 * q + e] : acc[i][j][4 * q + e];
                 stage4<T, BM>(lds, r, c, v);
             }
         }
@@ -728,19 +771,19 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
-                    int32_t mode, int32_t cur, bool last, float a, float b, float c) {
+                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, int32_t do_product) {
     if (mode == kSyrkX)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, a, b, c);
+                           tiles, nt, cur, s_init, s_final, do_product);
     else if (mode == kSyrkA)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, a, b, c);
+                           tiles, nt, cur, s_init, s_final, do_product);
     else if (!last)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, a, b, c);
+                           tiles, nt, cur, s_init, s_final, do_product);
     else
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, a, b, c);
+                           tiles, nt, cur, s_init, s_final, do_product);
 }
 
 template <typename T>
@@ -792,7 +835,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             for (int tj = 0; tj < nn; ++tj) ntiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
         const double m = (double)mi.m, n = (double)mi.n;
         f_syrk_x += m * (m + 1) * n;
-        f_syrk_a += c != 0.f ? m * m * (m + 1) : 0.0;
+        f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;
         f_gemm += 2 * m * m * n;
         norm_bytes += 2.0 * m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
     }
@@ -833,6 +876,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     NSQ_HIP(hipGetLastError());
     int cur = 0;
     const double work[3] = {f_syrk_x, f_syrk_a, f_gemm};
+    // B = b A + c A A as c (b / c A + A A): the accumulators of the A A product
+    // start at (b / c) A. With c == 0, or b / c out of fp32 range (c A A is then
+    // below fp32 resolution of b A), B = b A and the product is skipped.
+    const float ratio = c != 0.f ? b / c : 0.f;
+    const bool sa_fused = c != 0.f && std::isfinite(ratio);
+    const float sa_init = sa_fused ? ratio : b, sa_final = sa_fused ? c : 1.f;
+    const int32_t sa_product = sa_fused ? 1 : 0;
     for (int32_t s = 0; s < steps; ++s) {
         for (int mode = kSyrkX; mode <= kGemmBX; ++mode) {
             const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;
@@ -841,13 +891,18 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
             TimedScope ts(kind, st, work[mode]);
+            const float s_init = mode == kSyrkX ? 0.f : mode == kSyrkA ? sa_init : a;
+            const float s_final = mode == kSyrkA ? sa_final : 1.f;
+            const int32_t do_product = mode == kSyrkA ? sa_product : 1;
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
-                    launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
+                    launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
+                                           do_product);
                     continue;
                 }
             }
-            launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, a, b, c);
+            launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
+                                     do_product);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
