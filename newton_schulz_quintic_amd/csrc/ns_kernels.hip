@@ -56,7 +56,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
 constexpr int kThreads = 256;       // threads of the norm kernels
-constexpr int kRowBytes = 128;      // K bytes per LDS panel row per stage (64 bf16 / 32 f32)
 constexpr int kNormChunk = 16384;   // minimum elements per norm partial
 constexpr int kMaxParts = kThreads; // at most one partial per thread of the apply reduction
 constexpr int kNormTile = 64;       // norm apply tile edge
@@ -134,43 +133,67 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 enum Mode { kSyrkX = 0, kSyrkA = 1, kGemmBX = 2 };
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
-// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks.
-template <int BM_, int WM_, int WN_> struct TileCfg {
-    static constexpr int BM = BM_, WM = WM_, WN = WN_;
+// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
+// panels of ROWB bytes per row, in a ring of NBUF stage buffers.
+template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
+    static constexpr int BM = BM_, WM = WM_, WN = WN_, ROWB = ROWB_, NBUF = NBUF_;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int NBM = BM / WM / 32;    // 32x32 blocks per wave, row direction
     static constexpr int NBN = BM / WN / 32;    // ... column direction
-    static constexpr int PANEL = BM * kRowBytes;
+    static constexpr int PANEL = BM * ROWB;
     static constexpr int STAGE = 2 * PANEL;     // P panel then Q panel
-    static constexpr int LDS = 2 * STAGE;       // two stage buffers
+    static constexpr int RING = NBUF * STAGE;
     static constexpr int RPW = BM / WAVES;      // panel rows each wave loads
-    static constexpr int RPI = 1024 / kRowBytes;  // panel rows per 1 KiB wave load
+    static constexpr int RPI = 1024 / ROWB;     // panel rows per 1 KiB wave load
     static constexpr int LOADS = RPW / RPI;     // loads per wave per panel
-    static constexpr int KG = kRowBytes / 32;   // k-groups (one 32-byte MFMA K step each) per stage
-    static_assert(RPW % RPI == 0, "each wave loads whole 8-row groups");
+    static constexpr int KG = ROWB / 32;        // k-groups (one 32-byte MFMA K step each) per stage
+    static_assert(ROWB == 64 || ROWB == 128, "panel row size");
+    static_assert(RPW % RPI == 0, "each wave loads whole row groups");
+    static_assert(NBUF >= 2 && NBUF <= 5, "ring depth");
 };
-typedef TileCfg<256, 2, 4> Big;    // 8 waves, 2 per SIMD, 128 x 64 per wave
-typedef TileCfg<128, 2, 2> Small;  // 4 waves, 64 x 64 per wave (two workgroups per CU)
+#ifndef NSQ_BIG_ROWB
+#define NSQ_BIG_ROWB 128
+#endif
+#ifndef NSQ_BIG_NBUF
+#define NSQ_BIG_NBUF 2
+#endif
+typedef TileCfg<256, 2, 4, NSQ_BIG_ROWB, NSQ_BIG_NBUF> Big;   // 8 waves, 2 per SIMD, 128 x 64 per wave
+typedef TileCfg<128, 2, 2, 128, 2> Small;                     // 4 waves, 64 x 64 per wave (two per CU)
 
-// Operand staging. Each stage holds, per operand, kRowBytes bytes of K for
-// each of the tile's BM rows. Panel row r sits at r * 128 bytes; its 16-byte
-// chunk c (8 bf16 / 4 f32 consecutive k) sits in slot c ^ swz(r),
-// swz(r) = (r >> 1) & 7, so the fragment reads (32 consecutive rows, one chunk
-// each) hit distinct banks in every 16 lanes. Global -> LDS uses
-// buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l, so each lane fetches
-// whatever global chunk belongs at its LDS slot; one wave instruction moves
-// 8 rows x 128 bytes.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// Operand staging. Each stage holds, per operand, ROWB bytes of K for each of
+// the tile's BM rows. Panel row r sits at r * ROWB bytes; its 16-byte chunk c
+// (8 bf16 / 4 f32 consecutive k) sits in slot c ^ swz(r), which makes the
+// fragment reads (32 consecutive rows, one chunk each) hit distinct banks in
+// every 16 lanes:
+//   ROWB = 128: swz(r) = (r >> 1) & 7
+//   ROWB = 64:  swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
+// Global -> LDS uses buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l,
+// so each lane fetches whatever global chunk belongs at its LDS slot; one wave
+// instruction moves 1 KiB (1024 / ROWB rows).
+template <int ROWB> __device__ __forceinline__ int swz(int r) {
+    if constexpr (ROWB == 128) return (r >> 1) & 7;
+    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+
+// s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that waits for this wave's LDS operations but not for its
+// global loads (the ring keeps later stages in flight across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // MFMA operand fragment for the 32-row block starting at panel row `blk`,
 // k-group kg of the stage: lane l gets row blk + l%32, chunk 2 kg + l/32.
-template <typename T>
+template <typename T, int ROWB>
 __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *region, int lane, int blk, int kg) {
     typedef typename Mfma<T>::frag frag;
     const int row = blk + (lane & 31);
     const int c = 2 * kg + (lane >> 5);
-    return *reinterpret_cast<const frag *>(region + row * kRowBytes + ((c ^ swz(row)) << 4));
+    return *reinterpret_cast<const frag *>(region + row * ROWB + ((c ^ swz<ROWB>(row)) << 4));
 }
 
 // acc += P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
@@ -188,51 +211,71 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, extent_p, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, extent_q, 0x00020000);
+    constexpr int ROWB = C::ROWB, CPR = ROWB / 16;   // 16-byte chunks per panel row
     int voff_p[C::LOADS], voff_q[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const int row = wave * C::RPW + i * C::RPI + (lane >> 3);
-        const int chunk = ((lane & 7) ^ swz(row)) << 4;
+        const int row = wave * C::RPW + i * C::RPI + lane / CPR;
+        const int chunk = ((lane % CPR) ^ swz<ROWB>(row)) << 4;
         voff_p[i] = row * ldp + chunk;
         voff_q[i] = row * ldq + chunk;
     }
     const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
     // This wave's loads of stage kb: rows [wave RPW, (wave + 1) RPW) of both
-    // panels into stage buffer kb % 2, 8 rows x 128 bytes per instruction.
+    // panels into ring buffer kb % NBUF, 1 KiB per instruction.
     auto issue = [&](int kb) {
-        char *sp = lds + (kb & 1) * C::STAGE + wave * C::RPW * kRowBytes;
+        char *sp = lds + (kb % C::NBUF) * C::STAGE + wave * C::RPW * ROWB;
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sp + i * C::RPI * kRowBytes), 16,
-                                                     (int)voff_p[i], kb * kRowBytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)(sp + i * C::RPI * ROWB), 16,
+                                                     (int)voff_p[i], kb * ROWB, 0, 0);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sp + C::PANEL + i * C::RPI * kRowBytes),
-                                                     16, (int)voff_q[i], kb * kRowBytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sp + C::PANEL + i * C::RPI * ROWB), 16,
+                                                     (int)voff_q[i], kb * ROWB, 0, 0);
+    };
+    // Wait until this wave's loads of the current stage have landed, leaving
+    // the n stages issued after it in flight.
+    constexpr int L = 2 * C::LOADS;
+    auto wait_stage = [&](int n) {
+        if constexpr (C::NBUF >= 5) {
+            if (n >= 3) { wait_vmcnt<3 * L>(); return; }
+        }
+        if constexpr (C::NBUF >= 4) {
+            if (n >= 2) { wait_vmcnt<2 * L>(); return; }
+        }
+        if constexpr (C::NBUF >= 3) {
+            if (n >= 1) { wait_vmcnt<L>(); return; }
+        }
+        wait_vmcnt<0>();
     };
 
-    if (nk > 0) issue(0);
+#pragma unroll
+    for (int s = 0; s < C::NBUF - 1; ++s)
+        if (s < nk) issue(s);
     for (int kb = 0; kb < nk; ++kb) {
-        // Every wave's loads of stage kb have landed (the barrier waits for
-        // this wave's outstanding loads) and every wave is done with stage
-        // kb - 1, whose buffer the next loads overwrite.
-        __syncthreads();
-        if (kb + 1 < nk) issue(kb + 1);
-        const char *sp = lds + (kb & 1) * C::STAGE, *sq = sp + C::PANEL;
+        // Every wave's loads of stage kb have landed and every wave is done
+        // with stage kb - 1, whose buffer the next loads overwrite.
+        wait_stage(min(C::NBUF - 2, nk - 1 - kb));
+        lds_barrier();
+        if (kb + C::NBUF - 1 < nk) issue(kb + C::NBUF - 1);
+        const char *sp = lds + (kb % C::NBUF) * C::STAGE, *sq = sp + C::PANEL;
         // fragments for k-group kg + 1 are read while the MFMAs of kg run
         frag fa[2][C::NBM], fb[2][C::NBN];
 #pragma unroll
-        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T>(sp, lane, a_blk + 32 * i, 0);
+        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, 0);
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T>(sq, lane, b_blk + 32 * j, 0);
+        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, 0);
 #pragma unroll
         for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
             if (kg + 1 < C::KG) {
 #pragma unroll
-                for (int i = 0; i < C::NBM; ++i) fa[nb][i] = operand_frag<T>(sp, lane, a_blk + 32 * i, kg + 1);
+                for (int i = 0; i < C::NBM; ++i)
+                    fa[nb][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, kg + 1);
 #pragma unroll
-                for (int j = 0; j < C::NBN; ++j) fb[nb][j] = operand_frag<T>(sq, lane, b_blk + 32 * j, kg + 1);
+                for (int j = 0; j < C::NBN; ++j)
+                    fb[nb][j] = operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
@@ -431,8 +474,8 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     float s_init, float s_final, int32_t do_product) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
-    static_assert(BM * BM * ES <= C::LDS, "the staged tile fits the operand buffers");
-    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+    constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
     const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
     if (tile_id >= ntiles) return;
     const TileRef tr = tiles[tile_id];
@@ -451,17 +494,17 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         zero_acc<C>(acc);
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
-                           np * ES / kRowBytes, lds, acc);
+                           np * ES / C::ROWB, lds, acc);
     } else if constexpr (MODE == kSyrkA) {
         init_acc<T, C>(A, ldt * ES, row0, col0, s_init, lds, acc);
         const int ld = ldt * ES;
-        const int nk = do_product ? mp * ES / kRowBytes : 0;
+        const int nk = do_product ? mp * ES / C::ROWB : 0;
         tile_product<T, C>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk, lds, acc);
     } else {
         init_acc<T, C>(xc, ldx * ES, row0, col0, s_init, lds, acc);
         const int ldb = ldt * ES, ldq = ldxt * ES;
         tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
-                           mp * ES / kRowBytes, lds, acc);
+                           mp * ES / C::ROWB, lds, acc);
     }
 
     // Epilogue, part 1: scaling, rounding, staging. Accumulator element
