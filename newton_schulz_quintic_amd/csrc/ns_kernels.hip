@@ -55,10 +55,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
-constexpr int kThreads = 256;       // threads of the norm kernels
-constexpr int kNormChunk = 16384;   // minimum elements per norm partial
-constexpr int kMaxParts = kThreads; // at most one partial per thread of the apply reduction
-constexpr int kNormTile = 64;       // norm apply tile edge
+constexpr int kPrepTile = 128;      // tile edge of the input-staging pass
+constexpr int kPrepThreads = 256;   // its threads
+constexpr int kScaleSlots = 256;    // width of the fixed-order reduction of the norm partials
 constexpr int kNumXcd = 8;
 // Every workspace row is padded by this many bytes past its padded width, so
 // the row stride is an odd multiple of 256 bytes: a K panel (the same bytes of
@@ -74,15 +73,14 @@ struct NsProb {
     char *b;           // B: mp x mp (row stride ldt)
     const char *in;    // input, rows x cols
     char *out;         // output, rows x cols
-    float *partials;   // nparts (<= kMaxParts) fp32 partial sums of squares
+    float *partials;   // nparts fp32 sums of squares, one per staging tile
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
     int32_t ldx;       // row stride of X (elements, > np)
     int32_t ldxt;      // row stride of X^T (elements, > mp)
     int32_t ldt;       // row stride of A and B (elements, > mp)
     int32_t tall;      // input had rows > cols
-    int32_t nparts;
-    int32_t chunk;     // input elements per partial (a multiple of 8)
+    int32_t nparts;    // (mp / kPrepTile) * (np / kPrepTile)
 };
 
 struct TileRef {
@@ -457,6 +455,30 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
     __syncthreads();   // every wave is done with the staged tile
 }
 
+// The normalisation scale 1 / (||G||_F + eps) of one matrix from its partial
+// sums of squares, reduced in a fixed order: partial k goes to slot
+// k % kScaleSlots (summed in increasing k), then the slots are summed as a
+// binary tree. Independent of the workgroup size (>= kScaleSlots threads), so
+// every kernel that needs it gets the same bits. `red` is kScaleSlots floats of
+// LDS; ends with a barrier.
+__device__ __forceinline__ float norm_scale(const float *partials, int nparts, float eps, float *red) {
+    const int t = threadIdx.x;
+    if (t < kScaleSlots) {
+        float v = 0.f;
+        for (int k = t; k < nparts; k += kScaleSlots) v += partials[k];
+        red[t] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = kScaleSlots / 2; w > 0; w >>= 1) {
+        if (t < w) red[t] += red[t + w];
+        __syncthreads();
+    }
+    const float total = red[0];
+    __syncthreads();
+    return 1.0f / (sqrtf(total) + eps);
+}
+
 // One product launch: MODE picks the operands and epilogue.
 //   kSyrkX : A = X X^T                     P = X, Q = X     upper tiles, mirrored
 //   kSyrkA : B = s_final (s_init A + A A^T)  P = A, Q = A     upper tiles, mirrored
@@ -466,12 +488,15 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
 // up to fp32 rounding; when c == 0 (or b / c is not finite, where c A A is
 // below fp32 resolution of b A) the host passes (b, 1) and do_product = 0, so
 // B = b A. For B X, s_init = a.
+// FIRST (the first step): X0 in the workspace holds the input G unscaled, and
+// the normalisation X0 = s G, s = 1 / (||G||_F + eps), is folded in here:
+// A0 = s^2 (G G^T), B0 is stored scaled by s, and X1 = (a s) G + (s B0) G.
 // LAST (kGemmBX only): the final step writes a X + B X straight to the
 // caller's output in the input's orientation instead of into the workspace.
 template <typename T, class C, int MODE, bool LAST>
 __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
     const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
-    float s_init, float s_final, int32_t do_product) {
+    float s_init, float s_final, int32_t do_product, int32_t first, float eps) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
     constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
@@ -488,6 +513,12 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     char *xtc = cur ? pr.xt1 : pr.xt0;
     char *xtn = cur ? pr.xt0 : pr.xt1;
     char *A = pr.a, *B = pr.b;
+    if (first) {
+        const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds));
+        if constexpr (MODE == kSyrkX) s_final = sc * sc;
+        else if constexpr (MODE == kSyrkA) s_final *= sc;
+        else s_init *= sc;
+    }
 
     f32x16 acc[C::NBM][C::NBN];
     if constexpr (MODE == kSyrkX) {
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[e] = MODE == kSyrkA ? s_final * acc[i][j][4 * q + e] : acc[i][j][4 * q + e];
+                    v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : s_final * acc[i][j][4 * q + e];
                 stage4<T, BM>(lds, r, c, v);
             }
         }
@@ -574,123 +605,123 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     }
 }
 
-// Fixed-order fp32 sum over a workgroup (every thread gets the total).
-__device__ __forceinline__ float block_sum(float v, float *red) {
-    red[threadIdx.x] = v;
-    __syncthreads();
-#pragma unroll
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    const float total = red[0];
-    __syncthreads();
-    return total;
-}
-
-struct NormPart {
-    int32_t prob;
-    int32_t part;
-};
-
-// Sum of squares of one chunk of one input, in fp32, in a fixed order.
+// Input staging, one kPrepTile x kPrepTile tile of X (m x n, oriented) per
+// workgroup: the input G goes unscaled into X0 and its transpose into X0^T
+// (zero in the padding), and the tile's fp32 sum of squares goes to
+// partials[ti * (np / kPrepTile) + tj], summed in a fixed order. The tile is read
+// as stored (rows of G; for a tall G those are columns of X), copied straight to
+// the matching workspace array with 16-byte stores, and staged in LDS (rows of
+// kPrepTile * es bytes, the 16-byte unit u of row r at unit position
+// u ^ 2 (r % 4)); the other array's rows come out of LDS with transpose reads
+// (bf16) or 4-byte reads (f32).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void ns_norm_partial_kernel(const NsProb *__restrict__ probs,
-                                                                   const NormPart *__restrict__ list,
-                                                                   int32_t count) {
-    __shared__ float red[kThreads];
-    const int bid = blockIdx.x;
-    if (bid >= count) return;
-    const NormPart np_ = list[bid];
-    const NsProb &pr = probs[np_.prob];
-    const int64_t numel = (int64_t)pr.m * pr.n;
-    const int64_t start = (int64_t)np_.part * pr.chunk;
-    const int64_t end = min(numel, start + (int64_t)pr.chunk);
-    const T *in = reinterpret_cast<const T *>(pr.in);
-    float s = 0.f;
-    constexpr int kVec = 16 / sizeof(T);
-    if ((reinterpret_cast<uintptr_t>(in) & 15) == 0) {
-        // start is a multiple of 8 elements, so in + start stays 16-byte aligned
-        const uint4 *v4 = reinterpret_cast<const uint4 *>(in + start);
-        const int64_t nvec = (end - start) / kVec;
-        for (int64_t k = threadIdx.x; k < nvec; k += kThreads) {
-            uint4 raw = v4[k];
-            const T *e = reinterpret_cast<const T *>(&raw);
-#pragma unroll
-            for (int u = 0; u < kVec; ++u) {
-                const float f = to_f32<T>(e[u]);
-                s += f * f;
-            }
-        }
-        for (int64_t k = start + nvec * kVec + threadIdx.x; k < end; k += kThreads) {
-            const float f = to_f32<T>(in[k]);
-            s += f * f;
-        }
-    } else {
-        for (int64_t k = start + threadIdx.x; k < end; k += kThreads) {
-            const float f = to_f32<T>(in[k]);
-            s += f * f;
-        }
-    }
-    const float total = block_sum(s, red);
-    if (threadIdx.x == 0) pr.partials[np_.part] = total;
-}
-
-// Scale and write one 64x64 tile of X0 (mp x np) and of X0^T (np x mp), zero
-// in the padding. With write_out (steps == 0) the scaled input goes straight to
-// the output instead.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void ns_norm_apply_kernel(const NsProb *__restrict__ probs,
-                                                                 const TileRef *__restrict__ tiles,
-                                                                 int32_t count, float eps,
-                                                                 int32_t write_out) {
-    __shared__ float red[kThreads];
-    __shared__ float tile[kNormTile][kNormTile + 1];
+__global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *__restrict__ probs,
+                                                                 const TileRef *__restrict__ tiles, int32_t count) {
+    constexpr int ES = sizeof(T), E = 16 / ES, TE = kPrepTile;
+    constexpr int RB = TE * ES, CPR = TE / E;           // staged row bytes, 16-byte chunks per row
+    __shared__ __attribute__((aligned(16))) char lds[TE * RB];
+    __shared__ float red[kPrepThreads];
     const int bid = blockIdx.x;
     if (bid >= count) return;
     const TileRef tr = tiles[bid];
-    const NsProb pr = probs[tr.prob];
-    // ||G||_F from the matrix's partials: the same fixed-order sum in every workgroup
-    const float part = (int)threadIdx.x < pr.nparts ? pr.partials[threadIdx.x] : 0.f;
-    const float scale = 1.0f / (sqrtf(block_sum(part, red)) + eps);
-
-    const T *in = reinterpret_cast<const T *>(pr.in);
-    const int i0 = tr.ti * kNormTile, j0 = tr.tj * kNormTile;  // X rows / cols
-    // tile[r][c] = X0[i0 + r][j0 + c]
-    for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
-        const int a = e / kNormTile, b = e % kNormTile;  // b runs fastest: coalesced input reads
-        float v = 0.f;
-        if (!pr.tall) {
-            const int i = i0 + a, j = j0 + b;
-            if (i < pr.m && j < pr.n) v = to_f32<T>(in[(int64_t)i * pr.n + j]);
-            tile[a][b] = to_f32<T>(from_f32<T>(v * scale));
-        } else {
-            const int j = j0 + a, i = i0 + b;  // input is n x m: row j, col i
-            if (i < pr.m && j < pr.n) v = to_f32<T>(in[(int64_t)j * pr.m + i]);
-            tile[b][a] = to_f32<T>(from_f32<T>(v * scale));
-        }
-    }
-    __syncthreads();
-    if (write_out) {
-        T *O = reinterpret_cast<T *>(pr.out);
-        for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
-            const int a = e / kNormTile, b = e % kNormTile;
-            if (!pr.tall) {
-                const int i = i0 + a, j = j0 + b;
-                if (i < pr.m && j < pr.n) O[(int64_t)i * pr.n + j] = from_f32<T>(tile[a][b]);
+    const NsProb &pr = probs[tr.prob];
+    const int i0 = tr.ti * TE, j0 = tr.tj * TE;        // X rows / cols of the tile
+    const bool tall = pr.tall;
+    // as stored: row r of the tile is input row r0 + r, column c is input column c0 + c
+    const int r0 = tall ? j0 : i0, c0 = tall ? i0 : j0;
+    const int rows = tall ? pr.n : pr.m, cols = tall ? pr.m : pr.n;   // input shape
+    char *direct = tall ? pr.xt0 : pr.x0;                 // receives the tile as stored
+    char *trans = tall ? pr.x0 : pr.xt0;                  // receives its transpose
+    const int ld_direct = tall ? pr.ldxt : pr.ldx, ld_trans = tall ? pr.ldx : pr.ldxt;
+    const bool vec_in = (reinterpret_cast<uintptr_t>(pr.in) & 15) == 0 && ((int64_t)cols * ES) % 16 == 0;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < TE * CPR / kPrepThreads; ++k) {
+        const int f = threadIdx.x + kPrepThreads * k;
+        const int r = f / CPR, u = f % CPR, c = u * E;
+        const int64_t gr = r0 + r, gc = c0 + c;
+        i32x4 w = {0, 0, 0, 0};
+        if (gr < rows) {
+            const char *src = pr.in + (gr * cols + gc) * ES;
+            if (vec_in && gc + E <= cols) {
+                w = *reinterpret_cast<const i32x4 *>(src);
             } else {
-                const int j = j0 + a, i = i0 + b;
-                if (i < pr.m && j < pr.n) O[(int64_t)j * pr.m + i] = from_f32<T>(tile[b][a]);
+                T vals[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) vals[e] = gc + e < cols ? reinterpret_cast<const T *>(src)[e] : T(0);
+                __builtin_memcpy(&w, vals, 16);
             }
         }
-        return;
+        T vals[E];
+        __builtin_memcpy(vals, &w, 16);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float v = to_f32<T>(vals[e]);
+            ss += v * v;
+        }
+        store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
+        *reinterpret_cast<i32x4 *>(lds + r * RB + ((u ^ (2 * (r & 3))) << 4)) = w;
     }
-    T *X = reinterpret_cast<T *>(pr.x0);
-    T *XT = reinterpret_cast<T *>(pr.xt0);
-    for (int e = threadIdx.x; e < kNormTile * kNormTile; e += kThreads) {
-        const int a = e / kNormTile, b = e % kNormTile;
-        X[(int64_t)(i0 + a) * pr.ldx + (j0 + b)] = from_f32<T>(tile[a][b]);
-        XT[(int64_t)(j0 + a) * pr.ldxt + (i0 + b)] = from_f32<T>(tile[b][a]);
+    // fixed-order block sum of the squares
+    red[threadIdx.x] = ss;
+    __syncthreads();
+#pragma unroll
+    for (int w = kPrepThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) pr.partials[tr.ti * (pr.np / TE) + tr.tj] = red[0];
+
+    // transpose: output row c (tile column), 16 bytes = E consecutive tile rows
+    auto at = [&](int r, int c) -> const char * {
+        const int byte = c * ES;
+        return lds + r * RB + (((byte >> 4) ^ (2 * (r & 3))) << 4) + (byte & 15);
+    };
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 15, g = lane >> 4;
+    constexpr int BR = 4 * E;                          // tile rows per block (4 lane groups x E)
+    constexpr int BLOCKS = (TE / 16) * (TE / BR);
+    for (int blk = wave; blk < BLOCKS; blk += kPrepThreads / 64) {
+        const int cb = (blk % (TE / 16)) * 16, rb = (blk / (TE / 16)) * BR + E * g;
+        const int c = cb + t;
+        i32x4 w;
+        if constexpr (ES == 2) {
+            s16x4 v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (NSQ_LDS s16x4 *)at(rb + 4 * h + (t >> 2), cb + 4 * (t & 3)));
+            w[0] = (int)(uint16_t)v[0][0] | ((int)(uint16_t)v[0][1] << 16);
+            w[1] = (int)(uint16_t)v[0][2] | ((int)(uint16_t)v[0][3] << 16);
+            w[2] = (int)(uint16_t)v[1][0] | ((int)(uint16_t)v[1][1] << 16);
+            w[3] = (int)(uint16_t)v[1][2] | ((int)(uint16_t)v[1][3] << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const int *>(at(rb + e, c));
+        }
+        store16<T>(trans, (int64_t)(c0 + c) * ld_trans + r0 + rb, w);
+    }
+}
+
+// steps == 0: the output is the normalised input, out = s G in the input's
+// layout, one kPrepTile x kPrepTile tile of the input (as stored) per workgroup.
+template <typename T>
+__global__ __launch_bounds__(kPrepThreads) void ns_scale_out_kernel(const NsProb *__restrict__ probs,
+                                                                   const TileRef *__restrict__ tiles,
+                                                                   int32_t count, float eps) {
+    __shared__ float red[kScaleSlots];
+    const int bid = blockIdx.x;
+    if (bid >= count) return;
+    const TileRef tr = tiles[bid];
+    const NsProb &pr = probs[tr.prob];
+    const float sc = norm_scale(pr.partials, pr.nparts, eps, red);
+    const bool tall = pr.tall;
+    const int r0 = tall ? tr.tj * kPrepTile : tr.ti * kPrepTile, c0 = tall ? tr.ti * kPrepTile : tr.tj * kPrepTile;
+    const int rows = tall ? pr.n : pr.m, cols = tall ? pr.m : pr.n;
+    const T *in = reinterpret_cast<const T *>(pr.in);
+    T *out = reinterpret_cast<T *>(pr.out);
+    for (int e = threadIdx.x; e < kPrepTile * kPrepTile; e += kPrepThreads) {
+        const int64_t r = r0 + e / kPrepTile, c = c0 + e % kPrepTile;
+        if (r < rows && c < cols) out[r * cols + c] = from_f32<T>(to_f32<T>(in[r * cols + c]) * sc);
     }
 }
 
@@ -704,7 +735,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
-    int64_t nparts, chunk, syrk_tiles, gemm_tiles, norm_tiles;
+    int64_t nparts, syrk_tiles, gemm_tiles;
     size_t buf_bytes;
 };
 
@@ -731,7 +762,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.m = std::min(mi.rows, mi.cols);
         mi.n = std::max(mi.rows, mi.cols);
         // tile indices are 16-bit; byte offsets inside one padded matrix are 32-bit
-        if (mi.n > (int64_t)65535 * kNormTile ||
+        if (mi.n > (int64_t)65535 * kPrepTile ||
             round_up(mi.m, kPad) * (round_up(mi.n, kPad) + kRowPadBytes / es) * es >= (1ll << 31) ||
             round_up(mi.n, kPad) * (round_up(mi.m, kPad) + kRowPadBytes / es) * es >= (1ll << 31))
             return fail(NS_ERR_OVERFLOW, "tensor %d: %lld x %lld is too large", i,
@@ -742,9 +773,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         const int64_t tm = mi.mp / 128, tn = mi.np / 128;
         mi.syrk_tiles = tm * (tm + 1) / 2;
         mi.gemm_tiles = tm * tn;
-        mi.norm_tiles = (mi.mp / kNormTile) * (mi.np / kNormTile);
-        mi.chunk = std::max<int64_t>(kNormChunk, round_up((mi.m * mi.n + kMaxParts - 1) / kMaxParts, 8));
-        mi.nparts = (mi.m * mi.n + mi.chunk - 1) / mi.chunk;
+        mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
@@ -752,30 +781,27 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
 
 // Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, parts, ntiles, partials, total;
+    size_t probs, syrk, gemm, ptiles, partials, total;
     size_t o_syrk() const { return probs; }
     size_t o_gemm() const { return o_syrk() + syrk; }
-    size_t o_parts() const { return o_gemm() + gemm; }
-    size_t o_ntiles() const { return o_parts() + parts; }
-    size_t o_partials() const { return o_ntiles() + ntiles; }
+    size_t o_ptiles() const { return o_gemm() + gemm; }
+    size_t o_partials() const { return o_ptiles() + ptiles; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, pa = 0, nt = 0;
+    int64_t np = 0, sy = 0, ge = 0, pa = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
         sy += mi.syrk_tiles;
         ge += mi.gemm_tiles;
         pa += mi.nparts;
-        nt += mi.norm_tiles;
     }
     TableSizes t;
     t.probs = align256(np * sizeof(NsProb));
     t.syrk = align256(sy * sizeof(TileRef));
     t.gemm = align256(ge * sizeof(TileRef));
-    t.parts = align256(pa * sizeof(NormPart));
-    t.ntiles = align256(nt * sizeof(TileRef));
+    t.ptiles = align256(pa * sizeof(TileRef));
     t.partials = align256(pa * sizeof(float));
     t.total = t.o_partials() + t.partials;
     return t;
@@ -814,19 +840,20 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
-                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, int32_t do_product) {
+                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, int32_t do_product,
+                    int32_t first, float eps) {
     if (mode == kSyrkX)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
     else if (mode == kSyrkA)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
     else if (!last)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
     else
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
 }
 
 template <typename T>
@@ -836,8 +863,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const int64_t es = sizeof(T);
     const int bm = pick_tile(group, info, es);
     std::vector<NsProb> probs;
-    std::vector<TileRef> syrk, gemm, ntiles;
-    std::vector<NormPart> parts;
+    std::vector<TileRef> syrk, gemm, ptiles;
     char *base = ws + tsz.total;
     float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
     int64_t part_off = 0;
@@ -857,7 +883,6 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.out = static_cast<char *>(out[idx]);
         p.partials = partials + part_off;
         part_off += mi.nparts;
-        p.chunk = (int32_t)mi.chunk;
         p.m = (int32_t)mi.m;
         p.n = (int32_t)mi.n;
         p.mp = (int32_t)mi.mp;
@@ -872,15 +897,14 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
         grouped_tiles(pid, tm, tm, true, syrk);
         grouped_tiles(pid, tm, tn, false, gemm);
-        for (int64_t k = 0; k < mi.nparts; ++k) parts.push_back(NormPart{pid, (int32_t)k});
-        const int nm = (int)(mi.mp / kNormTile), nn = (int)(mi.np / kNormTile);
-        for (int ti = 0; ti < nm; ++ti)
-            for (int tj = 0; tj < nn; ++tj) ntiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+        const int pm = (int)(mi.mp / kPrepTile), pn = (int)(mi.np / kPrepTile);
+        for (int ti = 0; ti < pm; ++ti)   // partial index ti * pn + tj
+            for (int tj = 0; tj < pn; ++tj) ptiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
         const double m = (double)mi.m, n = (double)mi.n;
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;
         f_gemm += 2 * m * m * n;
-        norm_bytes += 2.0 * m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
+        norm_bytes += m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
 
@@ -897,8 +921,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     put(0, probs.data(), probs.size() * sizeof(NsProb));
     put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
-    put(tsz.o_parts(), parts.data(), parts.size() * sizeof(NormPart));
-    put(tsz.o_ntiles(), ntiles.data(), ntiles.size() * sizeof(TileRef));
+    put(tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
     const hipError_t ce = hipMemcpyAsync(ws, host, table_bytes, hipMemcpyHostToDevice, st);
     if ((sst = staging_release(slot, st, ce == hipSuccess))) return sst;
     if (ce != hipSuccess) return fail(NS_ERR_HIP, "table upload failed: %s", hipGetErrorString(ce));
@@ -906,15 +929,16 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
     const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
-    const NormPart *d_parts = reinterpret_cast<const NormPart *>(ws + tsz.o_parts());
-    const TileRef *d_ntiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ntiles());
+    const TileRef *d_ptiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ptiles());
+    const int32_t npt = (int32_t)ptiles.size();
 
     {
         TimedScope ts(kTimeNorm, st, norm_bytes);
-        hipLaunchKernelGGL(ns_norm_partial_kernel<T>, dim3((unsigned)parts.size()), dim3(kThreads), 0,
-                           st, d_probs, d_parts, (int32_t)parts.size());
-        hipLaunchKernelGGL(ns_norm_apply_kernel<T>, dim3((unsigned)ntiles.size()), dim3(kThreads), 0,
-                           st, d_probs, d_ntiles, (int32_t)ntiles.size(), eps, steps == 0 ? 1 : 0);
+        hipLaunchKernelGGL(ns_prepare_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
+                           d_ptiles, npt);
+        if (steps == 0)
+            hipLaunchKernelGGL(ns_scale_out_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
+                               d_ptiles, npt, eps);
     }
     NSQ_HIP(hipGetLastError());
     int cur = 0;
@@ -934,18 +958,18 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
             TimedScope ts(kind, st, work[mode]);
-            const float s_init = mode == kSyrkX ? 0.f : mode == kSyrkA ? sa_init : a;
+            const float s_init = mode == kSyrkX ? 1.f : mode == kSyrkA ? sa_init : a;
             const float s_final = mode == kSyrkA ? sa_final : 1.f;
             const int32_t do_product = mode == kSyrkA ? sa_product : 1;
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
                     launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                           do_product);
+                                           do_product, s == 0, eps);
                     continue;
                 }
             }
             launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                     do_product);
+                                     do_product, s == 0, eps);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
