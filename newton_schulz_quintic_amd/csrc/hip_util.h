@@ -34,11 +34,12 @@ bool timing_enabled();
 int timing_start(int kind, hipStream_t stream, double work);
 void timing_stop(int slot, hipStream_t stream);
 
-// Pinned host staging buffers for per-call table uploads (staging.hip).
-// Acquire a buffer of at least `bytes`, fill it, enqueue the copy, then
-// release it with the copy's stream so it is reused only after the copy ends.
-ns_status staging_acquire(size_t bytes, int *slot, void **ptr);
-ns_status staging_release(int slot, hipStream_t stream, bool copied);
+// Pinned host staging buffers for the per-call tables (staging.hip). Acquire
+// a buffer of at least `bytes` (host pointer and the device's pointer to the
+// same memory), fill it, enqueue the kernel that reads it, then release it
+// with that stream so it is reused only after the kernel ends.
+ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr);
+ns_status staging_release(int slot, hipStream_t stream, bool used);
 
 struct TimedScope {
     int slot;

@@ -32,7 +32,10 @@ struct RouteSeg {
 };
 static_assert(sizeof(RouteSeg) == 48, "RouteSeg layout");
 
-constexpr int64_t kRouteChunkBytes = 16384;
+#ifndef NSQ_ROUTE_CHUNK
+#define NSQ_ROUTE_CHUNK 16384
+#endif
+constexpr int64_t kRouteChunkBytes = NSQ_ROUTE_CHUNK;
 
 }  // namespace nsq
 

@@ -614,14 +614,24 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 // kPrepTile * es bytes, the 16-byte unit u of row r at unit position
 // u ^ 2 (r % 4)); the other array's rows come out of LDS with transpose reads
 // (bf16) or 4-byte reads (f32).
+//
+// This is the first kernel of a call: its descriptor and tile list are read
+// from the pinned host staging buffer, and the workgroups also copy the whole
+// table block (table_units 16-byte units) from there into the workspace for
+// the kernels that follow.
 template <typename T>
 __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *__restrict__ probs,
-                                                                 const TileRef *__restrict__ tiles, int32_t count) {
+                                                                 const TileRef *__restrict__ tiles, int32_t count,
+                                                                 const i32x4 *__restrict__ table_src,
+                                                                 i32x4 *__restrict__ table_dst,
+                                                                 int32_t table_units) {
     constexpr int ES = sizeof(T), E = 16 / ES, TE = kPrepTile;
     constexpr int RB = TE * ES, CPR = TE / E;           // staged row bytes, 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) char lds[TE * RB];
     __shared__ float red[kPrepThreads];
     const int bid = blockIdx.x;
+    for (int u = bid * kPrepThreads + threadIdx.x; u < table_units; u += gridDim.x * kPrepThreads)
+        table_dst[u] = table_src[u];
     if (bid >= count) return;
     const TileRef tr = tiles[bid];
     const NsProb &pr = probs[tr.prob];
@@ -908,11 +918,12 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     }
     if (probs.empty()) return NS_OK;
 
-    // One upload of every table (stream-ordered after earlier groups' kernels).
-    const size_t table_bytes = tsz.o_partials();
+    // The tables go to pinned host memory; the first kernel reads its own from
+    // there and copies all of them into the workspace head.
+    const size_t table_bytes = tsz.o_partials();   // a multiple of 256
     int slot;
-    void *staging;
-    ns_status sst = staging_acquire(table_bytes, &slot, &staging);
+    void *staging, *staging_dev;
+    ns_status sst = staging_acquire(table_bytes, &slot, &staging, &staging_dev);
     if (sst) return sst;
     char *host = static_cast<char *>(staging);
     auto put = [&](size_t off, const void *src, size_t bytes) {
@@ -922,9 +933,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
     put(tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
-    const hipError_t ce = hipMemcpyAsync(ws, host, table_bytes, hipMemcpyHostToDevice, st);
-    if ((sst = staging_release(slot, st, ce == hipSuccess))) return sst;
-    if (ce != hipSuccess) return fail(NS_ERR_HIP, "table upload failed: %s", hipGetErrorString(ce));
+    const char *hdev = static_cast<const char *>(staging_dev);
 
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
@@ -934,8 +943,14 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
 
     {
         TimedScope ts(kTimeNorm, st, norm_bytes);
-        hipLaunchKernelGGL(ns_prepare_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
-                           d_ptiles, npt);
+        hipLaunchKernelGGL(ns_prepare_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st,
+                           reinterpret_cast<const NsProb *>(hdev),
+                           reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
+                           reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
+                           (int32_t)(table_bytes / 16));
+        const hipError_t le = hipGetLastError();
+        if ((sst = staging_release(slot, st, le == hipSuccess))) return sst;
+        if (le != hipSuccess) return fail(NS_ERR_HIP, "launch failed: %s", hipGetErrorString(le));
         if (steps == 0)
             hipLaunchKernelGGL(ns_scale_out_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
                                d_ptiles, npt, eps);

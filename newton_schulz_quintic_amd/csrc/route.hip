@@ -7,11 +7,15 @@
 // concatenates per-rank shards in buffer order; OwnerScatterPlan.unpack
 // extracts each rank's flat result shard.
 //
-// One launch moves every piece. The pieces are cut into 16 KiB chunks numbered
-// globally; a workgroup takes chunks in a grid-stride loop, finds the piece by
-// binary search over the pieces' first chunk numbers, and copies the chunk with
-// 16-byte loads and stores when both ends are 16-byte aligned (narrower
-// accesses otherwise). HBM-bound: every byte is read once and written once.
+// One launch moves every piece. The pieces are cut into chunks (16 KiB)
+// numbered globally; a workgroup takes chunks in a grid-stride loop, finds the
+// piece by binary search over the pieces' first chunk numbers, and copies the
+// chunk with 16-byte loads and stores when both ends are 16-byte aligned
+// (narrower accesses otherwise); a full aligned chunk has all of each thread's
+// loads in flight before its stores. HBM-bound: every byte is read once and
+// written once. Plans that move more than the 256 MB last-level cache (MALL)
+// store with non-temporal hints; smaller ones keep their output cache-resident
+// for the kernel that reads it next.
 
 #include "hip_util.h"
 
@@ -25,6 +29,7 @@ struct PtrSet {
     char *p[NS_MAX_SHARDS];
 };
 
+template <bool NT>
 __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict__ dst, int64_t len) {
     const int t = threadIdx.x;
     const uintptr_t mis = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
@@ -32,13 +37,24 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
         const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
         uint4 *d4 = reinterpret_cast<uint4 *>(dst);
         const int64_t n16 = len >> 4;
+        constexpr int kPer = (int)(kRouteChunkBytes / 16 / kRouteThreads);   // 16-byte units per thread
+        static_assert(kRouteChunkBytes % (16 * kRouteThreads) == 0, "whole units per thread");
         if (n16 == kRouteChunkBytes / 16) {
-            // full chunk: 4 loads in flight per thread before the stores
-            uint4 v0 = s4[t], v1 = s4[t + 256], v2 = s4[t + 512], v3 = s4[t + 768];
-            d4[t] = v0;
-            d4[t + 256] = v1;
-            d4[t + 512] = v2;
-            d4[t + 768] = v3;
+            // full chunk: all of this thread's loads in flight before the stores
+            uint4 v[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) v[k] = s4[t + kRouteThreads * k];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                if constexpr (NT) {
+                    __builtin_nontemporal_store(v[k].x, &d4[t + kRouteThreads * k].x);
+                    __builtin_nontemporal_store(v[k].y, &d4[t + kRouteThreads * k].y);
+                    __builtin_nontemporal_store(v[k].z, &d4[t + kRouteThreads * k].z);
+                    __builtin_nontemporal_store(v[k].w, &d4[t + kRouteThreads * k].w);
+                } else {
+                    d4[t + kRouteThreads * k] = v[k];
+                }
+            }
         } else {
             for (int64_t i = t; i < n16; i += kRouteThreads) d4[i] = s4[i];
         }
@@ -57,15 +73,26 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
 }
 
 // to_home = 1: shard -> home (pack); 0: home -> shard (unpack).
+// Plans with at most kLdsSegs pieces keep the piece table in LDS for the
+// per-chunk binary search.
+constexpr int kLdsSegs = 256;
+constexpr int64_t kMallBytes = 256ll << 20;
+template <bool NT>
 __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSeg *__restrict__ segs,
                                                                    int32_t nseg, int64_t total_chunks,
                                                                    PtrSet shard, PtrSet home,
                                                                    int32_t to_home) {
+    __shared__ int64_t first_chunk[kLdsSegs];
+    const bool in_lds = nseg <= kLdsSegs;
+    if (in_lds) {
+        for (int i = threadIdx.x; i < nseg; i += kRouteThreads) first_chunk[i] = segs[i].chunk_begin;
+        __syncthreads();
+    }
     for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
         int32_t lo = 0, hi = nseg - 1;
         while (lo < hi) {
             const int32_t mid = (lo + hi + 1) >> 1;
-            if (segs[mid].chunk_begin <= c)
+            if ((in_lds ? first_chunk[mid] : segs[mid].chunk_begin) <= c)
                 lo = mid;
             else
                 hi = mid - 1;
@@ -77,9 +104,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSe
         char *sp = shard.p[g.shard] + g.shard_off + off;
         char *hp = home.p[g.home] + g.home_off + off;
         if (to_home)
-            copy_chunk(sp, hp, len);
+            copy_chunk<NT>(sp, hp, len);
         else
-            copy_chunk(hp, sp, len);
+            copy_chunk<NT>(hp, sp, len);
     }
 }
 
@@ -111,9 +138,13 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
     const int64_t grid = plan->total_chunks < kRouteMaxGrid ? plan->total_chunks : kRouteMaxGrid;
     {
         TimedScope ts(kTimeRoute, st, 2.0 * (double)plan->total_bytes);
-        hipLaunchKernelGGL(route_copy_kernel, dim3((unsigned)grid), dim3(kRouteThreads), 0, st,
-                           reinterpret_cast<const RouteSeg *>(plan->device_table),
-                           (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
+        const RouteSeg *table = reinterpret_cast<const RouteSeg *>(plan->device_table);
+        if (plan->total_bytes > kMallBytes)
+            hipLaunchKernelGGL(route_copy_kernel<true>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
+                               (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
+        else
+            hipLaunchKernelGGL(route_copy_kernel<false>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
+                               (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
     }
     NSQ_HIP(hipGetLastError());
     return NS_OK;

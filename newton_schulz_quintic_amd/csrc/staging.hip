@@ -1,9 +1,9 @@
 // Pinned host staging for the per-call device tables of the batched
-// Newton-Schulz entry point. Copies from pinned memory are truly asynchronous
-// (a pageable source makes the runtime stage the copy itself, which can hold
-// the host until the stream drains). A buffer is reused only after the event
-// recorded behind its last copy has completed, so the host never overwrites
-// data a pending copy still reads.
+// Newton-Schulz entry point. The first kernel of a call reads the tables
+// straight from this buffer (it is mapped into the device's address space) and
+// copies them into the workspace for the later kernels. A buffer is reused only
+// after the event recorded behind that kernel has completed, so the host never
+// overwrites data a pending kernel still reads.
 
 #include <mutex>
 #include <vector>
@@ -15,10 +15,11 @@ namespace nsq {
 namespace {
 struct Slot {
     void *ptr = nullptr;
+    void *dev = nullptr;   // the same memory as the device addresses it
     size_t cap = 0;
     hipEvent_t done = nullptr;
     bool in_use = false;     // handed out and not yet released
-    bool pending = false;    // a copy from it may still be running
+    bool pending = false;    // a kernel may still be reading it
 };
 std::mutex g_mu;
 std::vector<Slot> g_slots;
@@ -31,7 +32,7 @@ bool idle(Slot &s) {
 }
 }  // namespace
 
-ns_status staging_acquire(size_t bytes, int *slot, void **ptr) {
+ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr) {
     std::lock_guard<std::mutex> lk(g_mu);
     int pick = -1;
     for (size_t i = 0; i < g_slots.size(); ++i)
@@ -57,23 +58,25 @@ ns_status staging_acquire(size_t bytes, int *slot, void **ptr) {
     Slot &s = g_slots[pick];
     if (s.cap < bytes) {
         if (s.ptr) NSQ_HIP(hipHostFree(s.ptr));
-        s.ptr = nullptr;
+        s.ptr = s.dev = nullptr;
         s.cap = 0;
         const size_t cap = std::max<size_t>(bytes, 1 << 20);
         NSQ_HIP(hipHostMalloc(&s.ptr, cap, hipHostMallocDefault));
+        NSQ_HIP(hipHostGetDevicePointer(&s.dev, s.ptr, 0));
         s.cap = cap;
     }
     s.in_use = true;
     *slot = pick;
     *ptr = s.ptr;
+    *dev_ptr = s.dev;
     return NS_OK;
 }
 
-ns_status staging_release(int slot, hipStream_t stream, bool copied) {
+ns_status staging_release(int slot, hipStream_t stream, bool used) {
     std::lock_guard<std::mutex> lk(g_mu);
     Slot &s = g_slots[slot];
     s.in_use = false;
-    if (copied) {
+    if (used) {
         NSQ_HIP(hipEventRecord(s.done, stream));
         s.pending = true;
     }
