@@ -8,9 +8,8 @@
 // extracts each rank's flat result shard.
 //
 // One launch moves every piece. The pieces are cut into chunks (16 KiB)
-// numbered globally; a workgroup takes chunks in a grid-stride loop, finds the
-// piece by binary search over the pieces' first chunk numbers, and copies the
-// chunk with 16-byte loads and stores when both ends are 16-byte aligned
+// numbered globally; each workgroup takes a contiguous range of chunks and
+// copies each chunk with 16-byte loads and stores when both ends are 16-byte aligned
 // (narrower accesses otherwise); a full aligned chunk has all of each thread's
 // loads in flight before its stores. HBM-bound: every byte is read once and
 // written once. Plans that move more than the 256 MB last-level cache (MALL)
@@ -23,7 +22,10 @@ namespace nsq {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteMaxGrid = 8192;
+#ifndef NSQ_ROUTE_GRID
+#define NSQ_ROUTE_GRID 262144
+#endif
+constexpr int kRouteMaxGrid = NSQ_ROUTE_GRID;
 
 struct PtrSet {
     char *p[NS_MAX_SHARDS];
@@ -73,31 +75,29 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
 }
 
 // to_home = 1: shard -> home (pack); 0: home -> shard (unpack).
-// Plans with at most kLdsSegs pieces keep the piece table in LDS for the
-// per-chunk binary search.
-constexpr int kLdsSegs = 256;
+// Workgroup b copies the contiguous chunk range [b per, (b + 1) per): it finds
+// the piece holding its first chunk by binary search over the pieces' first
+// chunk numbers, then walks forward through the pieces.
 constexpr int64_t kMallBytes = 256ll << 20;
 template <bool NT>
 __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSeg *__restrict__ segs,
                                                                    int32_t nseg, int64_t total_chunks,
-                                                                   PtrSet shard, PtrSet home,
+                                                                   int64_t per, PtrSet shard, PtrSet home,
                                                                    int32_t to_home) {
-    __shared__ int64_t first_chunk[kLdsSegs];
-    const bool in_lds = nseg <= kLdsSegs;
-    if (in_lds) {
-        for (int i = threadIdx.x; i < nseg; i += kRouteThreads) first_chunk[i] = segs[i].chunk_begin;
-        __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * per;
+    const int64_t c1 = c0 + per < total_chunks ? c0 + per : total_chunks;
+    if (c0 >= c1) return;
+    int32_t lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (segs[mid].chunk_begin <= c0)
+            lo = mid;
+        else
+            hi = mid - 1;
     }
-    for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
-        int32_t lo = 0, hi = nseg - 1;
-        while (lo < hi) {
-            const int32_t mid = (lo + hi + 1) >> 1;
-            if ((in_lds ? first_chunk[mid] : segs[mid].chunk_begin) <= c)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const RouteSeg g = segs[lo];
+    RouteSeg g = segs[lo];
+    for (int64_t c = c0; c < c1; ++c) {
+        while (lo + 1 < nseg && segs[lo + 1].chunk_begin <= c) g = segs[++lo];
         const int64_t off = (c - g.chunk_begin) * kRouteChunkBytes;
         const int64_t rem = g.len - off;
         const int64_t len = rem < kRouteChunkBytes ? rem : kRouteChunkBytes;
@@ -135,16 +135,17 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
     }
     if (plan->segs.empty()) return NS_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int64_t grid = plan->total_chunks < kRouteMaxGrid ? plan->total_chunks : kRouteMaxGrid;
+    const int64_t per = (plan->total_chunks + kRouteMaxGrid - 1) / kRouteMaxGrid;   // chunks per workgroup
+    const int64_t grid = (plan->total_chunks + per - 1) / per;
     {
         TimedScope ts(kTimeRoute, st, 2.0 * (double)plan->total_bytes);
         const RouteSeg *table = reinterpret_cast<const RouteSeg *>(plan->device_table);
         if (plan->total_bytes > kMallBytes)
             hipLaunchKernelGGL(route_copy_kernel<true>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
-                               (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
+                               (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
         else
             hipLaunchKernelGGL(route_copy_kernel<false>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
-                               (int32_t)plan->segs.size(), plan->total_chunks, sh, ho, to_home);
+                               (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
     }
     NSQ_HIP(hipGetLastError());
     return NS_OK;
