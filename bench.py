@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "ns_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ns_product_bx_routed16x1024.json")
 # rocprof symbol of the dominant kernel on the default workload (bf16, 256x256 tile, B X step)
-DOMINANT_SYMBOL = "ns_product_kernelIDF16bNS0_7TileCfgILi256ELi2ELi4EEELi2ELb0E"
+DOMINANT_SYMBOL = "ns_product_kernelIDF16bNS0_7TileCfgILi256ELi2ELi4ELi128ELi2EEELi2ELb0E"
 DOMINANT_NAME = "ns_product_kernel<bf16, 256x256 tile / 8 waves, B X step>"
 TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a"}
 

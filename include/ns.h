@@ -180,8 +180,12 @@ ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
  *
  * Precision: bf16 tensors keep X, A and B in bf16 between products; every
  * product runs on bf16 MFMA with fp32 accumulation, and the norm and the
- * epilogues (b A + c (A A), a X + B X) are computed in fp32 and rounded once
- * (round to nearest even). f32 tensors keep everything in fp32 (f32 MFMA).
+ * epilogues are computed in fp32 and rounded once (round to nearest even):
+ * B = c ((b / c) A + A A) (B = b A when c == 0), X' = a X + B X, the sums
+ * accumulated in fp32 from the old tile onward. The normalisation
+ * X0 = G / (||G||_F + eps) is applied in fp32 inside the first step's
+ * products (A0 = s^2 G G^T, B0 and X1 scaled by s), so X0 itself is never
+ * rounded. f32 tensors keep everything in fp32 (f32 MFMA).
  *
  * in[i], out[i]   device pointers, contiguous row-major, 2-byte (bf16) or
  *                 4-byte (f32) aligned; out[i] may equal in[i]; distinct outputs
@@ -194,7 +198,9 @@ ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
  *         minimum from ns_workspace_bytes. The call uses it as scratch until its
  *         work on `stream` has finished; two calls in flight at once (e.g. on
  *         different streams) must not share a workspace. The per-call device
- *         tables are copied from pinned host staging owned by the library.
+ *         tables are written to pinned host staging owned by the library; the
+ *         call's first kernel reads them from there and copies them into the
+ *         workspace.
  * Errors: INVALID_ARG, DTYPE, WORKSPACE, OVERFLOW, HIP. */
 ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                    const void *const *in, void *const *out, ns_dtype dtype,
