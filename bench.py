@@ -5,7 +5,10 @@ host), pack the row shards into their homes (one HIP launch; the route plan is
 built once and reused, as the pages' cached `plan` dict is), batched 5-step
 quintic Newton-Schulz on the home buffers (norm + 15 product launches), and
 unpack the results into result shards (one HIP launch). Inputs are resident in
-HBM before the timed region.
+HBM before the timed region. With --routing fused the step is one
+ns_orthogonalize_routed call instead, which reads the shard buffers and writes
+the result shards itself (no home buffers, no pack / unpack launches); the mode
+not selected is timed as well and reported under `other_routing`.
 
 Default workload: 16 bf16 1024x1024 matrices, N(0, 0.02), stored as 4 uneven
 row shards (one home empty). Other workloads: --workload dense-transformer
@@ -200,6 +203,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="routed-square",
                     choices=["routed-square", "dense-transformer", "many-small"])
+    ap.add_argument("--routing", default="pack", choices=["pack", "fused"],
+                    help="pack: pack -> batched NS on the home buffers -> unpack (three calls); fused: "
+                         "ns_orthogonalize_routed reads and writes the shard buffers directly. The other "
+                         "mode is timed too and reported under `other_routing`")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -248,16 +255,24 @@ def main():
         for d in shape:
             numel *= d
         views.append(homes[h][off:off + numel].view(shape))
-    need, _ = nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)
+    need = max(nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)[0],
+               nsq.ns_routed_workspace_bytes(plan, nsq.NS_BF16)[0])
     workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
-    def step():
+    def step_pack():
         pl = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
         nsq.ns_pack_shards(plan, shards_in, homes, stream)
         nsq.ns_orthogonalize_batched(views, views, steps=ms.steps, coeffs=ms.coeffs, order=pl["order"],
                                      workspace=workspace, stream=stream)
         nsq.ns_unpack_shards(plan, homes, shards_out, stream)
+
+    def step_fused():
+        pl = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
+        nsq.ns_orthogonalize_routed(plan, shards_in, shards_out, nsq.NS_BF16, steps=ms.steps,
+                                    coeffs=ms.coeffs, order=pl["order"], workspace=workspace, stream=stream)
+
+    step, other = (step_pack, step_fused) if args.routing == "pack" else (step_fused, step_pack)
 
     for _ in range(args.warmup):
         step()
@@ -286,6 +301,15 @@ def main():
         torch.cuda.synchronize()
         nsq.ns_timing_enable(False)
         breakdown = {name: nsq.ns_timing_read(k) for k, name in TIMING_KINDS.items()}
+    # The other routing mode, same inputs and step count, no instrumentation.
+    for _ in range(args.warmup):
+        other()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        other()
+    torch.cuda.synchronize()
+    ms_other = (time.perf_counter() - t2) * 1e3 / args.steps
 
     flops = sum(alg_flops(*oriented(s), ms.steps, ms.coeffs[2] != 0.0) for s in ms.shapes)
     dense = sum(ms.steps * (4 * m * m * n + 2 * m ** 3) for m, n in (oriented(s) for s in ms.shapes))
@@ -305,11 +329,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": ms.name, "matrices": ms.n, "distinct_shapes": len(set(ms.shapes)),
                    "shards": S, "ns_steps": ms.steps, "coeffs": list(ms.coeffs),
-                   "homes_used": len(set(p["home"]))},
+                   "homes_used": len(set(p["home"])), "routing": args.routing},
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "alg_flops_per_step": flops,
         "dense_equiv_flops_per_step": float(dense),
+        "other_routing": {"routing": "fused" if args.routing == "pack" else "pack",
+                          "ms_per_step": round(ms_other, 4),
+                          "value": round(ms.n / (ms_other * 1e-3), 3)},
     }
     if not args.no_kernel_timing:
         t = breakdown

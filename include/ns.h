@@ -209,6 +209,42 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                    size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * Fused routing: Newton-Schulz straight from and back to the shard buffers
+ * [layer_sharded, route_to_ns_home / route_from_ns_home around the
+ *  orthogonalisation; owner_planning, OwnerGatherPlan.reconstruct_full and
+ *  OwnerScatterPlan.unpack]
+ * ------------------------------------------------------------------------ */
+
+/* Workspace (bytes) for ns_orthogonalize_routed on `plan`, and the minimum
+ * (*min_bytes, may be NULL), as for ns_workspace_bytes. dtype must have the
+ * plan's elem_bytes. Errors: INVALID_ARG, DTYPE, PLAN_MISMATCH, OVERFLOW. */
+ns_status ns_routed_workspace_bytes(const ns_route_plan *plan, ns_dtype dtype, size_t *bytes,
+                                    size_t *min_bytes);
+
+/* The result of ns_pack_shards, then ns_orthogonalize_batched on all of the
+ * plan's tensors (in the home buffers), then ns_unpack_shards into shard_out,
+ * without home buffers: the first kernel reads each tensor's rows from its
+ * pieces in the shard buffers and the last one writes the result rows to the
+ * same offsets of the output shard buffers. Bit-identical to that sequence
+ * (same kernels, same arithmetic). The homes play no part: on one GPU every
+ * tensor of the plan is orthogonalised by the one call.
+ *
+ * plan        from ns_route_plan_create (no upload needed); its elem_bytes
+ *             must match dtype.
+ * shard_in    [num_shards] device pointers, layouts as in the route plan; an
+ *             entry may be NULL only if that shard has zero elements.
+ * shard_out   [num_shards] likewise; shard_out[s] may equal shard_in[s]
+ *             (in place); otherwise buffers must not overlap.
+ * steps, a, b, c, eps, order, workspace, workspace_bytes, stream: as for
+ *             ns_orthogonalize_batched (order indexes the plan's tensors;
+ *             the workspace minimum comes from ns_routed_workspace_bytes).
+ * Errors: INVALID_ARG, DTYPE, PLAN_MISMATCH, WORKSPACE, OVERFLOW, HIP. */
+ns_status ns_orthogonalize_routed(const ns_route_plan *plan, const void *const *shard_in,
+                                  void *const *shard_out, ns_dtype dtype, int32_t steps, float a,
+                                  float b, float c, float eps, const int32_t *order,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
  * Measurement support
  * ------------------------------------------------------------------------ */
 

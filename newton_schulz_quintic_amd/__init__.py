@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     lib,
     ns_last_error,
     ns_orthogonalize_batched,
+    ns_orthogonalize_routed,
     ns_pack_shards,
     ns_plan,
     ns_route_plan_create,
@@ -28,5 +29,6 @@ from ._lib import (  # noqa: F401
     ns_timing_read,
     ns_unpack_shards,
     ns_version,
+    ns_routed_workspace_bytes,
     ns_workspace_bytes,
 )

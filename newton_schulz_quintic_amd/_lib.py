@@ -25,7 +25,8 @@ STATUS = {
 EXPORTS = [
     "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
-    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_timing_enable", "ns_timing_read",
+    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_routed_workspace_bytes",
+    "ns_orthogonalize_routed", "ns_timing_enable", "ns_timing_read",
 ]
 
 
@@ -59,6 +60,8 @@ _SIGS = {
     "ns_workspace_bytes": (_I32, [_I32, _P, _I32, _P, _P]),
     "ns_orthogonalize_batched": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P,
                                         _SZ, _P]),
+    "ns_routed_workspace_bytes": (_I32, [_P, _I32, _P, _P]),
+    "ns_orthogonalize_routed": (_I32, [_P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P, _SZ, _P]),
     "ns_timing_enable": (_I32, [_I32]),
     "ns_timing_read": (_I32, [_I32, _P, _P, _P]),
 }
@@ -276,6 +279,37 @@ def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
                                           float(a), float(b), float(c), float(eps),
                                           None if ord_arr is None else _addr(ord_arr),
                                           workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ns_routed_workspace_bytes(plan: RoutePlan, dtype: int) -> tuple[int, int]:
+    b, mb = _SZ(0), _SZ(0)
+    _check(lib().ns_routed_workspace_bytes(plan.handle, dtype, ctypes.addressof(b), ctypes.addressof(mb)))
+    return b.value, mb.value
+
+
+def ns_orthogonalize_routed(plan: RoutePlan, shard_in, shard_out, dtype: int, steps: int = 5,
+                            coeffs=(3.4445, -4.7750, 2.0315), eps: float = 1e-7, order=None,
+                            workspace=None, stream=None):
+    """Newton-Schulz on every tensor of ``plan``, read from and written to its row
+    pieces in the shard buffers (see ns.h). ``shard_in`` / ``shard_out``: one
+    device tensor (or None for an empty shard) per shard, holding elements of
+    ``dtype``'s size. The workspace is allocated with torch if not given and is
+    returned."""
+    if dtype not in (NS_BF16, NS_F32):
+        raise TypeError(f"unsupported dtype code {dtype}")
+    src, dst = _ptr_array(shard_in, plan.num_shards), _ptr_array(shard_out, plan.num_shards)
+    if workspace is None:
+        import torch
+        need, _ = ns_routed_workspace_bytes(plan, dtype)
+        dev = next((t.device for t in list(shard_in) + list(shard_out) if t is not None), "cuda")
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    a, b, c = coeffs
+    ord_arr = None if order is None else _arr(_I32, order)
+    _check(lib().ns_orthogonalize_routed(plan.handle, _addr(src), _addr(dst), dtype, steps, float(a),
+                                         float(b), float(c), float(eps),
+                                         None if ord_arr is None else _addr(ord_arr),
+                                         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return workspace
 
 

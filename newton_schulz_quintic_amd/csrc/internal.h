@@ -43,6 +43,8 @@ struct ns_route_plan {
     int32_t n = 0;
     int32_t num_shards = 0;
     int32_t elem_bytes = 0;
+    std::vector<ns_shape> shapes;      // [n] as given
+    std::vector<int64_t> split_rows;   // [n * num_shards] as given
     std::vector<int64_t> shard_elems, home_elems, home_offset, shard_offset;
     std::vector<nsq::RouteSeg> segs;
     int64_t total_chunks = 0;

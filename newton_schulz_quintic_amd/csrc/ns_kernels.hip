@@ -71,8 +71,6 @@ struct NsProb {
     char *xt0, *xt1;   // X^T ping/pong: np x mp (row stride ldxt)
     char *a;           // A: mp x mp (row stride ldt)
     char *b;           // B: mp x mp (row stride ldt)
-    const char *in;    // input, rows x cols
-    char *out;         // output, rows x cols
     float *partials;   // nparts fp32 sums of squares, one per staging tile
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
@@ -81,13 +79,45 @@ struct NsProb {
     int32_t ldt;       // row stride of A and B (elements, > mp)
     int32_t tall;      // input had rows > cols
     int32_t nparts;    // (mp / kPrepTile) * (np / kPrepTile)
+    int32_t vec_in;    // every input piece allows 16-byte accesses (aligned base, row bytes % 16 == 0)
+    int32_t vec_out;   // ... every output piece
 };
 
+// Rows [row0, next piece's row0) of a tensor as stored (rows x cols,
+// row-major): element (r, c) of the input is at in + ((r - row0) cols + c) es,
+// of the output at out + ((r - row0) cols + c) es. An unrouted tensor is one
+// piece; a routed one has a piece per shard buffer that holds some of its rows
+// (route_to_ns_home / route_from_ns_home of "core.optimizer.layer_sharded_a2a"
+// move exactly these pieces). Pieces of a tensor are sorted by row0, the first
+// has row0 = 0 and none is empty.
+struct RowPiece {
+    int64_t row0;
+    const char *in;
+    char *out;
+};
+static_assert(sizeof(RowPiece) == 24, "RowPiece layout");
+
+// A tile of one tensor: (ti, tj) in the tile grid of the launch that uses it.
+// pieces[piece .. piece + npiece) are the pieces holding the tensor rows (as
+// stored) that the tile reads or writes; npiece >= 1.
 struct TileRef {
     int32_t prob;
     uint16_t ti, tj;
+    int32_t piece, npiece;
 };
-static_assert(sizeof(TileRef) == 8, "TileRef layout");
+static_assert(sizeof(TileRef) == 16, "TileRef layout");
+
+// The piece among band[0 .. n) (sorted by row0, band[0].row0 <= row) holding
+// row `row`.
+__device__ __forceinline__ const RowPiece &find_piece(const RowPiece *band, int n, int64_t row) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (band[mid].row0 <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    return band[lo];
+}
 
 template <typename T> struct Mfma;
 
@@ -369,20 +399,22 @@ __device__ __forceinline__ void store16(char *base, int64_t elem, i32x4 w) {
     *(NSQ_GLOBAL i32x4 *)(base + elem * (int64_t)sizeof(T)) = w;
 }
 
-// Bounds-checked store of the 16 / es elements of chunk w starting at
-// dst[row][col] of a rows x cols row-major array.
+// Bounds-checked store of the 16 / es elements of chunk w at [row][col] of the
+// caller's output (rows x cols as stored, rows spread over pieces).
 template <typename T>
-__device__ __forceinline__ void store_chunk_checked(char *dst, int64_t rows, int64_t cols, int64_t row, int64_t col,
-                                                    i32x4 w, bool vec_ok) {
+__device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowPiece *band, int nband,
+                                                    int64_t rows, int64_t cols, int64_t row, int64_t col, i32x4 w) {
     constexpr int E = 16 / (int)sizeof(T);
     if (row >= rows || col >= cols) return;
-    if (vec_ok && col + E <= cols) {
-        store16<T>(dst, row * cols + col, w);
+    const RowPiece &pc = find_piece(band, nband, row);
+    char *dst = pc.out + (row - pc.row0) * cols * (int64_t)sizeof(T);
+    if (pr.vec_out && col + E <= cols) {
+        store16<T>(dst, col, w);
         return;
     }
     T vals[E];
     __builtin_memcpy(vals, &w, 16);
-    NSQ_GLOBAL T *p = gp<T>(dst) + row * cols;
+    NSQ_GLOBAL T *p = gp<T>(dst);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (col + e < cols) p[col + e] = vals[e];
@@ -496,7 +528,7 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
 template <typename T, class C, int MODE, bool LAST>
 __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
     const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
-    float s_init, float s_final, int32_t do_product, int32_t first, float eps) {
+    float s_init, float s_final, int32_t do_product, int32_t first, float eps, const RowPiece *__restrict__ pieces) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
     constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
@@ -586,20 +618,18 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         }
     } else {
         const int m = pr.m, n = pr.n;
-        const bool aligned = (reinterpret_cast<uintptr_t>(pr.out) & 15) == 0;
+        const RowPiece *band = pieces + tr.piece;
         if (!pr.tall) {   // out is m x n: row-major chunks
-            const bool vec_ok = aligned && ((int64_t)n * ES) % 16 == 0;
             for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
                 int r, c;
                 const i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
-                store_chunk_checked<T>(pr.out, m, n, row0 + r, col0 + c, w, vec_ok);
+                store_chunk_checked<T>(pr, band, tr.npiece, m, n, row0 + r, col0 + c, w);
             }
         } else {          // out is n x m: column-major chunks
-            const bool vec_ok = aligned && ((int64_t)m * ES) % 16 == 0;
             for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
                 int c, r;
                 const i32x4 w = col_chunk<T, BM>(lds, idx, c, r);
-                store_chunk_checked<T>(pr.out, n, m, col0 + c, row0 + r, w, vec_ok);
+                store_chunk_checked<T>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
             }
         }
     }
@@ -624,17 +654,21 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
                                                                  const TileRef *__restrict__ tiles, int32_t count,
                                                                  const i32x4 *__restrict__ table_src,
                                                                  i32x4 *__restrict__ table_dst,
-                                                                 int32_t table_units) {
+                                                                 int32_t table_units,
+                                                                 const RowPiece *__restrict__ pieces) {
     constexpr int ES = sizeof(T), E = 16 / ES, TE = kPrepTile;
     constexpr int RB = TE * ES, CPR = TE / E;           // staged row bytes, 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) char lds[TE * RB];
     __shared__ float red[kPrepThreads];
+    __shared__ RowPiece band[kPrepTile];   // the pieces holding the tile's input rows
     const int bid = blockIdx.x;
     for (int u = bid * kPrepThreads + threadIdx.x; u < table_units; u += gridDim.x * kPrepThreads)
         table_dst[u] = table_src[u];
     if (bid >= count) return;
     const TileRef tr = tiles[bid];
     const NsProb &pr = probs[tr.prob];
+    if (threadIdx.x < tr.npiece) band[threadIdx.x] = pieces[tr.piece + threadIdx.x];
+    __syncthreads();
     const int i0 = tr.ti * TE, j0 = tr.tj * TE;        // X rows / cols of the tile
     const bool tall = pr.tall;
     // as stored: row r of the tile is input row r0 + r, column c is input column c0 + c
@@ -643,7 +677,7 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
     char *direct = tall ? pr.xt0 : pr.x0;                 // receives the tile as stored
     char *trans = tall ? pr.x0 : pr.xt0;                  // receives its transpose
     const int ld_direct = tall ? pr.ldxt : pr.ldx, ld_trans = tall ? pr.ldx : pr.ldxt;
-    const bool vec_in = (reinterpret_cast<uintptr_t>(pr.in) & 15) == 0 && ((int64_t)cols * ES) % 16 == 0;
+    const bool vec_in = pr.vec_in;
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < TE * CPR / kPrepThreads; ++k) {
@@ -652,7 +686,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         const int64_t gr = r0 + r, gc = c0 + c;
         i32x4 w = {0, 0, 0, 0};
         if (gr < rows) {
-            const char *src = pr.in + (gr * cols + gc) * ES;
+            const RowPiece &pc = find_piece(band, tr.npiece, gr);
+            const char *src = pc.in + ((gr - pc.row0) * cols + gc) * ES;
             if (vec_in && gc + E <= cols) {
                 w = *reinterpret_cast<const i32x4 *>(src);
             } else {
@@ -717,7 +752,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
 template <typename T>
 __global__ __launch_bounds__(kPrepThreads) void ns_scale_out_kernel(const NsProb *__restrict__ probs,
                                                                    const TileRef *__restrict__ tiles,
-                                                                   int32_t count, float eps) {
+                                                                   int32_t count, float eps,
+                                                                   const RowPiece *__restrict__ pieces) {
     __shared__ float red[kScaleSlots];
     const int bid = blockIdx.x;
     if (bid >= count) return;
@@ -727,11 +763,13 @@ __global__ __launch_bounds__(kPrepThreads) void ns_scale_out_kernel(const NsProb
     const bool tall = pr.tall;
     const int r0 = tall ? tr.tj * kPrepTile : tr.ti * kPrepTile, c0 = tall ? tr.ti * kPrepTile : tr.tj * kPrepTile;
     const int rows = tall ? pr.n : pr.m, cols = tall ? pr.m : pr.n;
-    const T *in = reinterpret_cast<const T *>(pr.in);
-    T *out = reinterpret_cast<T *>(pr.out);
     for (int e = threadIdx.x; e < kPrepTile * kPrepTile; e += kPrepThreads) {
         const int64_t r = r0 + e / kPrepTile, c = c0 + e % kPrepTile;
-        if (r < rows && c < cols) out[r * cols + c] = from_f32<T>(to_f32<T>(in[r * cols + c]) * sc);
+        if (r < rows && c < cols) {
+            const RowPiece &pc = find_piece(pieces + tr.piece, tr.npiece, r);
+            const int64_t k = (r - pc.row0) * cols + c;
+            reinterpret_cast<T *>(pc.out)[k] = from_f32<T>(to_f32<T>(reinterpret_cast<const T *>(pc.in)[k]) * sc);
+        }
     }
 }
 
@@ -746,8 +784,12 @@ struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
     int64_t nparts, syrk_tiles, gemm_tiles;
+    int64_t npieces;   // row pieces its input / output is split into
     size_t buf_bytes;
 };
+
+// Row pieces of every tensor of a call (indexed like the shapes).
+using PieceLists = std::vector<std::vector<RowPiece>>;
 
 // Row strides (elements) and array sizes of one matrix's workspace.
 inline int64_t ld_x(const MatInfo &mi, int64_t es) { return mi.np + kRowPadBytes / es; }
@@ -784,6 +826,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.syrk_tiles = tm * (tm + 1) / 2;
         mi.gemm_tiles = tm * tn;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
+        mi.npieces = 1;
         mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
@@ -791,30 +834,59 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
 
 // Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, ptiles, partials, total;
+    size_t probs, syrk, gemm, ptiles, pieces, partials, total;
     size_t o_syrk() const { return probs; }
     size_t o_gemm() const { return o_syrk() + syrk; }
     size_t o_ptiles() const { return o_gemm() + gemm; }
-    size_t o_partials() const { return o_ptiles() + ptiles; }
+    size_t o_pieces() const { return o_ptiles() + ptiles; }
+    size_t o_partials() const { return o_pieces() + pieces; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, pa = 0;
+    int64_t np = 0, sy = 0, ge = 0, pa = 0, pc = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
         sy += mi.syrk_tiles;
         ge += mi.gemm_tiles;
         pa += mi.nparts;
+        pc += mi.npieces;
     }
     TableSizes t;
     t.probs = align256(np * sizeof(NsProb));
     t.syrk = align256(sy * sizeof(TileRef));
     t.gemm = align256(ge * sizeof(TileRef));
     t.ptiles = align256(pa * sizeof(TileRef));
+    t.pieces = align256(pc * sizeof(RowPiece));
     t.partials = align256(pa * sizeof(float));
     t.total = t.o_partials() + t.partials;
     return t;
+}
+
+// Workspace for running every tensor at once, and the minimum (the largest
+// tensor alone).
+void workspace_need(const std::vector<MatInfo> &info, size_t *bytes, size_t *min_bytes) {
+    const TableSizes t = table_sizes(info);
+    size_t all = t.total, biggest = 0;
+    for (const MatInfo &mi : info) {
+        all += mi.buf_bytes;
+        biggest = std::max(biggest, mi.buf_bytes);
+    }
+    *bytes = all;
+    if (min_bytes) *min_bytes = t.total + biggest;
+}
+
+// Pieces of `pc` (sorted by row0, pc[0].row0 == 0) overlapping stored rows
+// [lo, hi): the first is the one holding row lo (the last piece when lo is past
+// the end, i.e. a tile of padding only).
+void band_of(const std::vector<RowPiece> &pc, int64_t lo, int64_t hi, int32_t *first, int32_t *count) {
+    int32_t f = 0;
+    const int32_t np = (int32_t)pc.size();
+    while (f + 1 < np && pc[f + 1].row0 <= lo) ++f;
+    int32_t e = f + 1;
+    while (e < np && pc[e].row0 < hi) ++e;
+    *first = f;
+    *count = e - f;
 }
 
 // Product tile edge for a group: 256 when the big tiles still give the GPU
@@ -845,35 +917,36 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
         for (int bj = 0; bj < tn; bj += kGroupCols)
             for (int ti = bi; ti < std::min(tm, bi + kGroupRows); ++ti)
                 for (int tj = bj; tj < std::min(tn, bj + kGroupCols); ++tj)
-                    if (!upper || tj >= ti) out.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+                    if (!upper || tj >= ti) out.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj, 0, 1});
 }
 
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
                     int32_t mode, int32_t cur, bool last, float s_init, float s_final, int32_t do_product,
-                    int32_t first, float eps) {
+                    int32_t first, float eps, const RowPiece *pieces) {
     if (mode == kSyrkX)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
     else if (mode == kSyrkA)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
     else if (!last)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
     else
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps);
+                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
 }
 
 template <typename T>
 ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo> &info,
-                    const void *const *in, void *const *out, int32_t steps, float a, float b,
+                    const PieceLists &pieces, int32_t steps, float a, float b,
                     float c, float eps, char *ws, const TableSizes &tsz, hipStream_t st) {
     const int64_t es = sizeof(T);
     const int bm = pick_tile(group, info, es);
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, ptiles;
+    std::vector<RowPiece> gpieces;
     char *base = ws + tsz.total;
     float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
     int64_t part_off = 0;
@@ -889,8 +962,17 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.a = p.xt1 + xtb;
         p.b = p.a + ab;
         base += mi.buf_bytes;
-        p.in = static_cast<const char *>(in[idx]);
-        p.out = static_cast<char *>(out[idx]);
+        const std::vector<RowPiece> &pc = pieces[idx];
+        const int32_t pbase = (int32_t)gpieces.size();
+        const int64_t row_bytes = (mi.tall ? mi.m : mi.n) * es;   // as stored
+        bool vin = row_bytes % 16 == 0, vout = vin;
+        for (const RowPiece &q : pc) {
+            vin = vin && reinterpret_cast<uintptr_t>(q.in) % 16 == 0;
+            vout = vout && reinterpret_cast<uintptr_t>(q.out) % 16 == 0;
+            gpieces.push_back(q);
+        }
+        p.vec_in = vin;
+        p.vec_out = vout;
         p.partials = partials + part_off;
         part_off += mi.nparts;
         p.m = (int32_t)mi.m;
@@ -904,12 +986,26 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.nparts = (int32_t)mi.nparts;
         const int32_t pid = (int32_t)probs.size();
         probs.push_back(p);
+        // Each tile names the pieces holding the stored rows it reads (staging
+        // tiles) or writes (B X tiles, whose last launch writes the output):
+        // X rows for a wide tensor, X columns for a tall one.
+        auto set_band = [&](TileRef &t, int edge) {
+            const int64_t lo = (int64_t)(mi.tall ? t.tj : t.ti) * edge;
+            band_of(pc, lo, lo + edge, &t.piece, &t.npiece);
+            t.piece += pbase;
+        };
         const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
+        const size_t s0 = syrk.size(), g0 = gemm.size();
         grouped_tiles(pid, tm, tm, true, syrk);
+        for (size_t k = s0; k < syrk.size(); ++k) syrk[k].piece = pbase;   // unused by the SYRK steps
         grouped_tiles(pid, tm, tn, false, gemm);
+        for (size_t k = g0; k < gemm.size(); ++k) set_band(gemm[k], bm);
         const int pm = (int)(mi.mp / kPrepTile), pn = (int)(mi.np / kPrepTile);
         for (int ti = 0; ti < pm; ++ti)   // partial index ti * pn + tj
-            for (int tj = 0; tj < pn; ++tj) ptiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj});
+            for (int tj = 0; tj < pn; ++tj) {
+                ptiles.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj, 0, 1});
+                set_band(ptiles.back(), kPrepTile);
+            }
         const double m = (double)mi.m, n = (double)mi.n;
         f_syrk_x += m * (m + 1) * n;
         f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;
@@ -933,12 +1029,14 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
     put(tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
+    put(tsz.o_pieces(), gpieces.data(), gpieces.size() * sizeof(RowPiece));
     const char *hdev = static_cast<const char *>(staging_dev);
 
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
     const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
     const TileRef *d_ptiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ptiles());
+    const RowPiece *d_pieces = reinterpret_cast<const RowPiece *>(ws + tsz.o_pieces());
     const int32_t npt = (int32_t)ptiles.size();
 
     {
@@ -947,13 +1045,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                            reinterpret_cast<const NsProb *>(hdev),
                            reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
                            reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
-                           (int32_t)(table_bytes / 16));
+                           (int32_t)(table_bytes / 16), reinterpret_cast<const RowPiece *>(hdev + tsz.o_pieces()));
         const hipError_t le = hipGetLastError();
         if ((sst = staging_release(slot, st, le == hipSuccess))) return sst;
         if (le != hipSuccess) return fail(NS_ERR_HIP, "launch failed: %s", hipGetErrorString(le));
         if (steps == 0)
             hipLaunchKernelGGL(ns_scale_out_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
-                               d_ptiles, npt, eps);
+                               d_ptiles, npt, eps, d_pieces);
     }
     NSQ_HIP(hipGetLastError());
     int cur = 0;
@@ -979,12 +1077,12 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
                     launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                           do_product, s == 0, eps);
+                                           do_product, s == 0, eps, d_pieces);
                     continue;
                 }
             }
             launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                     do_product, s == 0, eps);
+                                     do_product, s == 0, eps, d_pieces);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
@@ -992,49 +1090,12 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     return NS_OK;
 }
 
-}  // namespace
-}  // namespace nsq
-
-using namespace nsq;
-
-extern "C" ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
-                                        size_t *bytes, size_t *min_bytes) {
-    if (!bytes) return fail(NS_ERR_INVALID_ARG, "bytes is NULL");
-    std::vector<MatInfo> info;
-    ns_status st = describe(n, shapes, dtype, info);
-    if (st) return st;
-    const TableSizes t = table_sizes(info);
-    size_t all = t.total, biggest = 0;
-    for (const MatInfo &mi : info) {
-        all += mi.buf_bytes;
-        biggest = std::max(biggest, mi.buf_bytes);
-    }
-    *bytes = all;
-    if (min_bytes) *min_bytes = t.total + biggest;
-    return NS_OK;
-}
-
-extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
-                                              const void *const *in, void *const *out,
-                                              ns_dtype dtype, int32_t steps, float a, float b,
-                                              float c, float eps, const int32_t *order,
-                                              void *workspace, size_t workspace_bytes,
-                                              void *stream) {
-    std::vector<MatInfo> info;
-    ns_status st = describe(n, shapes, dtype, info);
-    if (st) return st;
-    if (steps < 0) return fail(NS_ERR_INVALID_ARG, "steps = %d < 0", steps);
-    if (!(eps >= 0.f) || !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
-        return fail(NS_ERR_INVALID_ARG, "coefficients must be finite and eps >= 0");
-    if (n == 0) return NS_OK;
-    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
-    const size_t es = dtype == NS_BF16 ? 2 : 4;
-    for (int32_t i = 0; i < n; ++i) {
-        if (!info[i].active) continue;
-        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
-        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
-            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
-    }
+// The common path of both entry points: every active tensor's input and output
+// rows are given as row pieces.
+ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype,
+                        int32_t steps, float a, float b, float c, float eps, const int32_t *order,
+                        void *workspace, size_t workspace_bytes, hipStream_t hs) {
+    const int32_t n = (int32_t)info.size();
     // Dispatch order: caller's permutation, else descending cost (ties by index).
     std::vector<int32_t> ord(n);
     if (order) {
@@ -1055,30 +1116,29 @@ extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
         std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return cost(x) > cost(y); });
     }
     const TableSizes tsz = table_sizes(info);
-    size_t biggest = 0;
-    for (const MatInfo &mi : info) biggest = std::max(biggest, mi.buf_bytes);
+    size_t all, need;
+    workspace_need(info, &all, &need);
     if (!workspace) return fail(NS_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
         return fail(NS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < tsz.total + biggest)
-        return fail(NS_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes,
-                    tsz.total + biggest);
+    if (workspace_bytes < need)
+        return fail(NS_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, need);
     // Groups of consecutive matrices (in dispatch order) whose buffers fit.
     const size_t room = workspace_bytes - tsz.total;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     std::vector<int32_t> group;
     size_t used = 0;
     auto flush = [&]() -> ns_status {
         if (group.empty()) return NS_OK;
         ns_status r = dtype == NS_BF16
-                          ? run_group<__bf16>(group, info, in, out, steps, a, b, c, eps,
+                          ? run_group<__bf16>(group, info, pieces, steps, a, b, c, eps,
                                               static_cast<char *>(workspace), tsz, hs)
-                          : run_group<float>(group, info, in, out, steps, a, b, c, eps,
+                          : run_group<float>(group, info, pieces, steps, a, b, c, eps,
                                              static_cast<char *>(workspace), tsz, hs);
         group.clear();
         used = 0;
         return r;
     };
+    ns_status st;
     for (int32_t i : ord) {
         if (!info[i].active) continue;
         if (used + info[i].buf_bytes > room && (st = flush())) return st;
@@ -1086,4 +1146,113 @@ extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
         used += info[i].buf_bytes;
     }
     return flush();
+}
+
+ns_status check_coefficients(int32_t steps, float a, float b, float c, float eps) {
+    if (steps < 0) return fail(NS_ERR_INVALID_ARG, "steps = %d < 0", steps);
+    if (!(eps >= 0.f) || !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+        return fail(NS_ERR_INVALID_ARG, "coefficients must be finite and eps >= 0");
+    return NS_OK;
+}
+
+// Tensors of a route plan, with each tensor's row pieces as described by the
+// plan (one per shard holding a nonzero number of its rows).
+ns_status describe_routed(const ns_route_plan *plan, ns_dtype dtype, std::vector<MatInfo> &info) {
+    if (!plan) return fail(NS_ERR_INVALID_ARG, "plan is NULL");
+    ns_status st = describe(plan->n, plan->shapes.data(), dtype, info);
+    if (st) return st;
+    if ((dtype == NS_BF16 ? 2 : 4) != plan->elem_bytes)
+        return fail(NS_ERR_PLAN_MISMATCH, "dtype element size differs from the plan's %d bytes", plan->elem_bytes);
+    const int32_t S = plan->num_shards;
+    for (int32_t i = 0; i < plan->n; ++i) {
+        int64_t k = 0;
+        for (int32_t s = 0; s < S; ++s) k += plan->split_rows[(size_t)i * S + s] > 0;
+        info[i].npieces = std::max<int64_t>(k, 1);
+    }
+    return NS_OK;
+}
+
+}  // namespace
+}  // namespace nsq
+
+using namespace nsq;
+
+extern "C" ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
+                                        size_t *bytes, size_t *min_bytes) {
+    if (!bytes) return fail(NS_ERR_INVALID_ARG, "bytes is NULL");
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info);
+    if (st) return st;
+    workspace_need(info, bytes, min_bytes);
+    return NS_OK;
+}
+
+extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
+                                              const void *const *in, void *const *out,
+                                              ns_dtype dtype, int32_t steps, float a, float b,
+                                              float c, float eps, const int32_t *order,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (n == 0) return NS_OK;
+    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
+    const size_t es = dtype == NS_BF16 ? 2 : 4;
+    PieceLists pieces(n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!info[i].active) continue;
+        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
+        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i])});
+    }
+    return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" ns_status ns_routed_workspace_bytes(const ns_route_plan *plan, ns_dtype dtype, size_t *bytes,
+                                               size_t *min_bytes) {
+    if (!bytes) return fail(NS_ERR_INVALID_ARG, "bytes is NULL");
+    std::vector<MatInfo> info;
+    ns_status st = describe_routed(plan, dtype, info);
+    if (st) return st;
+    workspace_need(info, bytes, min_bytes);
+    return NS_OK;
+}
+
+extern "C" ns_status ns_orthogonalize_routed(const ns_route_plan *plan, const void *const *shard_in,
+                                             void *const *shard_out, ns_dtype dtype, int32_t steps,
+                                             float a, float b, float c, float eps, const int32_t *order,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    std::vector<MatInfo> info;
+    ns_status st = describe_routed(plan, dtype, info);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (plan->n == 0) return NS_OK;
+    const int32_t S = plan->num_shards, n = plan->n;
+    const int64_t es = plan->elem_bytes;
+    if (!shard_in || !shard_out) return fail(NS_ERR_INVALID_ARG, "shard_in and shard_out are required");
+    for (int32_t s = 0; s < S; ++s) {
+        if (plan->shard_elems[s] == 0) continue;
+        if (!shard_in[s] || !shard_out[s]) return fail(NS_ERR_INVALID_ARG, "shard %d: NULL buffer", s);
+        if ((reinterpret_cast<uintptr_t>(shard_in[s]) | reinterpret_cast<uintptr_t>(shard_out[s])) % es)
+            return fail(NS_ERR_INVALID_ARG, "shard %d: buffer not %lld-byte aligned", s, (long long)es);
+    }
+    PieceLists pieces(n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!info[i].active) continue;
+        int64_t row0 = 0;
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t r = plan->split_rows[(size_t)i * S + s];
+            if (r == 0) continue;
+            const int64_t off = plan->shard_offset[(size_t)i * S + s] * es;
+            pieces[i].push_back(RowPiece{row0, static_cast<const char *>(shard_in[s]) + off,
+                                         static_cast<char *>(shard_out[s]) + off});
+            row0 += r;
+        }
+    }
+    return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
 }

@@ -175,6 +175,10 @@ extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int
     plan->n = n;
     plan->num_shards = S;
     plan->elem_bytes = elem_bytes;
+    if (n > 0) {
+        plan->shapes.assign(shapes, shapes + n);
+        plan->split_rows.assign(split_rows, split_rows + (size_t)n * S);
+    }
     plan->shard_elems.assign(S, 0);
     plan->home_elems.assign(S, 0);
     plan->home_offset.assign(n, 0);

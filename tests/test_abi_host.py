@@ -206,3 +206,32 @@ def test_workspace_and_batched_errors():
                                         ctypes.addressof(odd), 0, 5, 3.4, -4.7, 2.0, 1e-7, None, 4096,
                                         1 << 30, None) == -1
     assert "aligned" in nsq.ns_last_error()
+
+
+def test_routed_workspace_and_errors():
+    ms = routed_square_batch(uneven=True)
+    plan = nsq.ns_route_plan_create(ms.shapes, 4, ms.split_rows, [0] * ms.n, 2)
+    b, mb = nsq.ns_routed_workspace_bytes(plan, nsq.NS_BF16)
+    ub, umb = nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)
+    # the same buffers; only the piece table grows (one piece per nonzero split)
+    assert 0 <= b - ub <= 4096 and 0 <= mb - umb <= 4096
+    assert _status(nsq.ns_routed_workspace_bytes, plan, nsq.NS_F32) == "NS_ERR_PLAN_MISMATCH"
+    assert _status(nsq.ns_routed_workspace_bytes, plan, 9) == "NS_ERR_DTYPE"
+    lib = nsq.lib()
+    bs = _lib._SZ(0)
+    assert lib.ns_routed_workspace_bytes(None, 0, ctypes.addressof(bs), None) == -1
+    # host validation only: nothing is launched
+    nul = _lib._arr(ctypes.c_void_p, [None] * 4)
+    ok = _lib._arr(ctypes.c_void_p, [256] * 4)
+    call = lambda p, i, o, dtype=0, steps=5, eps=1e-7: lib.ns_orthogonalize_routed(  # noqa: E731
+        p, i, o, dtype, steps, 3.4, -4.7, 2.0, eps, None, None, 0, None)
+    assert call(None, ctypes.addressof(ok), ctypes.addressof(ok)) == -1
+    assert call(plan.handle, ctypes.addressof(ok), ctypes.addressof(ok), dtype=1) == -6
+    assert call(plan.handle, ctypes.addressof(ok), ctypes.addressof(ok), steps=-1) == -1
+    assert call(plan.handle, ctypes.addressof(nul), ctypes.addressof(ok)) == -1
+    assert call(plan.handle, None, ctypes.addressof(ok)) == -1
+    odd = _lib._arr(ctypes.c_void_p, [257] * 4)
+    assert call(plan.handle, ctypes.addressof(odd), ctypes.addressof(ok)) == -1
+    assert call(plan.handle, ctypes.addressof(ok), ctypes.addressof(ok)) == -7   # no workspace
+    empty = nsq.ns_route_plan_create([], 2, [], [], 2)
+    assert call(empty.handle, None, None) == 0
