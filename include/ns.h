@@ -178,14 +178,16 @@ ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
  * and write X (transposed back if it was transposed) to out[i] in the input's
  * shape and dtype [owner_planning, ns_cost_fn].
  *
- * Precision: bf16 tensors keep X, A and B in bf16 between products; every
+ * Precision: bf16 tensors keep X, A and B' in bf16 between products; every
  * product runs on bf16 MFMA with fp32 accumulation, and the norm and the
- * epilogues are computed in fp32 and rounded once (round to nearest even):
- * B = c ((b / c) A + A A) (B = b A when c == 0), X' = a X + B X, the sums
- * accumulated in fp32 from the old tile onward. The normalisation
- * X0 = G / (||G||_F + eps) is applied in fp32 inside the first step's
- * products (A0 = s^2 G G^T, B0 and X1 scaled by s), so X0 itself is never
- * rounded. f32 tensors keep everything in fp32 (f32 MFMA).
+ * epilogues are computed in fp32 and rounded once (round to nearest even).
+ * The step is evaluated as X' = B' X with B' = a I + B, an exact rewrite of
+ * a X + B X: B' = c ((b / c) A + A A) + a I (b A + a I when c == 0) is summed
+ * in fp32 from the old A tile onward and rounded once, so a + B_ii cancels
+ * before rounding. The normalisation X0 = G / (||G||_F + eps) is applied in
+ * fp32 inside the first step's products (A0 = s^2 G G^T, B0' stored scaled
+ * by s), so X0 itself is never rounded. f32 tensors keep everything in fp32
+ * (f32 MFMA).
  *
  * in[i], out[i]   device pointers, contiguous row-major, 2-byte (bf16) or
  *                 4-byte (f32) aligned; out[i] may equal in[i]; distinct outputs

@@ -186,7 +186,10 @@ template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
 #ifndef NSQ_BIG_NBUF
 #define NSQ_BIG_NBUF 2
 #endif
-typedef TileCfg<256, 2, 4, NSQ_BIG_ROWB, NSQ_BIG_NBUF> Big;   // 8 waves, 2 per SIMD, 128 x 64 per wave
+#ifndef NSQ_BIG_WN
+#define NSQ_BIG_WN 4
+#endif
+typedef TileCfg<256, 2, NSQ_BIG_WN, NSQ_BIG_ROWB, NSQ_BIG_NBUF> Big;   // 8 waves, 2 per SIMD, 128 x 64 per wave
 typedef TileCfg<128, 2, 2, 128, 2> Small;                     // 4 waves, 64 x 64 per wave (two per CU)
 
 // Operand staging. Each stage holds, per operand, ROWB bytes of K for each of
@@ -406,7 +409,7 @@ __device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowP
                                                     int64_t rows, int64_t cols, int64_t row, int64_t col, i32x4 w) {
     constexpr int E = 16 / (int)sizeof(T);
     if (row >= rows || col >= cols) return;
-    const RowPiece &pc = find_piece(band, nband, row);
+    const RowPiece pc = find_piece(band, nband, row);
     char *dst = pc.out + (row - pc.row0) * cols * (int64_t)sizeof(T);
     if (pr.vec_out && col + E <= cols) {
         store16<T>(dst, col, w);
@@ -512,23 +515,27 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
 }
 
 // One product launch: MODE picks the operands and epilogue.
-//   kSyrkX : A = X X^T                     P = X, Q = X     upper tiles, mirrored
-//   kSyrkA : B = s_final (s_init A + A A^T)  P = A, Q = A     upper tiles, mirrored
-//   kGemmBX: X' = s_init X + B X           P = B, Q = X^T   writes X' and X'^T
-// The accumulators start at s_init times the old tile, so the epilogue needs
-// no second read of it: with (s_init, s_final) = (b / c, c), B = b A + c A A
-// up to fp32 rounding; when c == 0 (or b / c is not finite, where c A A is
-// below fp32 resolution of b A) the host passes (b, 1) and do_product = 0, so
-// B = b A. For B X, s_init = a.
+//   kSyrkX : A = X X^T                          P = X, Q = X     upper tiles, mirrored
+//   kSyrkA : B' = s_final (s_init A + A A^T) + s_diag I
+//                                               P = A, Q = A     upper tiles, mirrored
+//   kGemmBX: X' = B' X                          P = B', Q = X^T  writes X' and X'^T
+// The step X' = a X + B X with B = b A + c A A is computed as X' = B' X with
+// B' = a I + B: the a X term becomes a on B's diagonal (added in fp32 before
+// B' is rounded), so the B X product needs no old tile. The A A product's
+// accumulators start at s_init times the old A tile: with (s_init, s_final) =
+// (b / c, c), B = b A + c A A up to fp32 rounding; when c == 0 (or b / c is
+// not finite, where c A A is below fp32 resolution of b A) the host passes
+// (b, 1) and do_product = 0, so B = b A. s_diag = a, added for rows < m only.
 // FIRST (the first step): X0 in the workspace holds the input G unscaled, and
 // the normalisation X0 = s G, s = 1 / (||G||_F + eps), is folded in here:
-// A0 = s^2 (G G^T), B0 is stored scaled by s, and X1 = (a s) G + (s B0) G.
-// LAST (kGemmBX only): the final step writes a X + B X straight to the
-// caller's output in the input's orientation instead of into the workspace.
+// A0 = s^2 (G G^T), and B0' is stored scaled by s, so X1 = (s B0') G.
+// LAST (kGemmBX only): the final step writes B' X straight to the caller's
+// output in the input's orientation instead of into the workspace.
 template <typename T, class C, int MODE, bool LAST>
 __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
     const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
-    float s_init, float s_final, int32_t do_product, int32_t first, float eps, const RowPiece *__restrict__ pieces) {
+    float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
+    const RowPiece *__restrict__ pieces) {
     static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
     constexpr int BM = C::BM, ES = sizeof(T);
     constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
@@ -548,8 +555,10 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     if (first) {
         const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds));
         if constexpr (MODE == kSyrkX) s_final = sc * sc;
-        else if constexpr (MODE == kSyrkA) s_final *= sc;
-        else s_init *= sc;
+        else if constexpr (MODE == kSyrkA) {
+            s_final *= sc;
+            s_diag *= sc;
+        }
     }
 
     f32x16 acc[C::NBM][C::NBN];
@@ -564,7 +573,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         const int nk = do_product ? mp * ES / C::ROWB : 0;
         tile_product<T, C>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk, lds, acc);
     } else {
-        init_acc<T, C>(xc, ldx * ES, row0, col0, s_init, lds, acc);
+        zero_acc<C>(acc);
         const int ldb = ldt * ES, ldq = ldxt * ES;
         tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
                            mp * ES / C::ROWB, lds, acc);
@@ -586,8 +595,11 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
                 const int r = wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e) {
                     v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : s_final * acc[i][j][4 * q + e];
+                    if constexpr (MODE == kSyrkA)
+                        if (tr.ti == tr.tj && r + e == c && row0 + r + e < pr.m) v[e] += s_diag;
+                }
                 stage4<T, BM>(lds, r, c, v);
             }
         }
@@ -667,8 +679,14 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
     if (bid >= count) return;
     const TileRef tr = tiles[bid];
     const NsProb &pr = probs[tr.prob];
-    if (threadIdx.x < tr.npiece) band[threadIdx.x] = pieces[tr.piece + threadIdx.x];
-    __syncthreads();
+    // A tile inside one piece (the usual case) reads it straight from the
+    // table, in parallel with the descriptor; more pieces go through LDS.
+    const RowPiece one = pieces[tr.piece];
+    const bool multi = tr.npiece > 1;
+    if (multi) {
+        if (threadIdx.x < tr.npiece) band[threadIdx.x] = pieces[tr.piece + threadIdx.x];
+        __syncthreads();
+    }
     const int i0 = tr.ti * TE, j0 = tr.tj * TE;        // X rows / cols of the tile
     const bool tall = pr.tall;
     // as stored: row r of the tile is input row r0 + r, column c is input column c0 + c
@@ -686,14 +704,15 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         const int64_t gr = r0 + r, gc = c0 + c;
         i32x4 w = {0, 0, 0, 0};
         if (gr < rows) {
-            const RowPiece &pc = find_piece(band, tr.npiece, gr);
+            RowPiece pc = one;   // by value: the reads below stay global loads
+            if (multi) pc = find_piece(band, tr.npiece, gr);
             const char *src = pc.in + ((gr - pc.row0) * cols + gc) * ES;
             if (vec_in && gc + E <= cols) {
-                w = *reinterpret_cast<const i32x4 *>(src);
+                w = *(const NSQ_GLOBAL i32x4 *)src;
             } else {
                 T vals[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) vals[e] = gc + e < cols ? reinterpret_cast<const T *>(src)[e] : T(0);
+                for (int e = 0; e < E; ++e) vals[e] = gc + e < cols ? gp<T>(src)[e] : T(0);
                 __builtin_memcpy(&w, vals, 16);
             }
         }
@@ -766,9 +785,9 @@ __global__ __launch_bounds__(kPrepThreads) void ns_scale_out_kernel(const NsProb
     for (int e = threadIdx.x; e < kPrepTile * kPrepTile; e += kPrepThreads) {
         const int64_t r = r0 + e / kPrepTile, c = c0 + e % kPrepTile;
         if (r < rows && c < cols) {
-            const RowPiece &pc = find_piece(pieces + tr.piece, tr.npiece, r);
+            const RowPiece pc = find_piece(pieces + tr.piece, tr.npiece, r);
             const int64_t k = (r - pc.row0) * cols + c;
-            reinterpret_cast<T *>(pc.out)[k] = from_f32<T>(to_f32<T>(reinterpret_cast<const T *>(pc.in)[k]) * sc);
+            gp<T>(pc.out)[k] = from_f32<T>(to_f32<T>(gp<T>(pc.in)[k]) * sc);
         }
     }
 }
@@ -922,20 +941,21 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 
 template <typename T, class C>
 void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
-                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, int32_t do_product,
+                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, float s_diag,
+                    int32_t do_product,
                     int32_t first, float eps, const RowPiece *pieces) {
     if (mode == kSyrkX)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
+                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
     else if (mode == kSyrkA)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
+                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
     else if (!last)
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
+                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
     else
         hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, do_product, first, eps, pieces);
+                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
 }
 
 template <typename T>
@@ -1056,9 +1076,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     NSQ_HIP(hipGetLastError());
     int cur = 0;
     const double work[3] = {f_syrk_x, f_syrk_a, f_gemm};
-    // B = b A + c A A as c (b / c A + A A): the accumulators of the A A product
-    // start at (b / c) A. With c == 0, or b / c out of fp32 range (c A A is then
-    // below fp32 resolution of b A), B = b A and the product is skipped.
+    // B' = a I + b A + c A A as c (b / c A + A A) + a I: the accumulators of the
+    // A A product start at (b / c) A. With c == 0, or b / c out of fp32 range
+    // (c A A is then below fp32 resolution of b A), B' = b A + a I and the
+    // product is skipped.
     const float ratio = c != 0.f ? b / c : 0.f;
     const bool sa_fused = c != 0.f && std::isfinite(ratio);
     const float sa_init = sa_fused ? ratio : b, sa_final = sa_fused ? c : 1.f;
@@ -1071,18 +1092,19 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
             TimedScope ts(kind, st, work[mode]);
-            const float s_init = mode == kSyrkX ? 1.f : mode == kSyrkA ? sa_init : a;
+            const float s_init = mode == kSyrkA ? sa_init : 1.f;
             const float s_final = mode == kSyrkA ? sa_final : 1.f;
+            const float s_diag = mode == kSyrkA ? a : 0.f;
             const int32_t do_product = mode == kSyrkA ? sa_product : 1;
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
                     launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                           do_product, s == 0, eps, d_pieces);
+                                           s_diag, do_product, s == 0, eps, d_pieces);
                     continue;
                 }
             }
             launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                     do_product, s == 0, eps, d_pieces);
+                                     s_diag, do_product, s == 0, eps, d_pieces);
         }
         NSQ_HIP(hipGetLastError());
         cur ^= 1;
