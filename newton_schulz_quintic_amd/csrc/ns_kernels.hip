@@ -227,12 +227,60 @@ __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *regio
     return *reinterpret_cast<const frag *>(region + row * ROWB + ((c ^ swz<ROWB>(row)) << 4));
 }
 
+// acc += s * P[r][k0 + c] for the accumulator blocks whose 32 columns lie in
+// the P stage `sp` (stage columns k0 .. k0 + KW, KW = ROWB / es), where the
+// tile's column c0 + wn BM/WN + 32 j maps to stage column
+// (wn BM/WN + 32 j) % KW when (wn BM/WN + 32 j) / KW == rel. Reads four
+// consecutive rows of one column per lane: bf16 by LDS transpose reads (in
+// each 16-lane group lane t addresses row r0 + t / 4, columns c0 + 4 (t % 4)
+// .. + 4, and receives column c0 + t, rows r0 .. r0 + 3), f32 by four 4-byte
+// reads.
+template <typename T, class C>
+__device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s, f32x16 (&acc)[C::NBM][C::NBN]) {
+    constexpr int ES = sizeof(T), ROWB = C::ROWB, KW = ROWB / ES;
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    auto at = [&](int r, int k) -> const char * {   // byte address of P[r][k] in the stage
+        const int byte = k * ES;
+        return sp + r * ROWB + ((((byte >> 4) ^ swz<ROWB>(r))) << 4) + (byte & 15);
+    };
+#pragma unroll
+    for (int j = 0; j < C::NBN; ++j) {
+        const int cj = wn * (C::BM / C::WN) + 32 * j;
+        if (cj / KW != rel) continue;
+        const int kc = cj % KW;
+#pragma unroll
+        for (int i = 0; i < C::NBM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rb = wm * (C::BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
+                float old[4];
+                if constexpr (ES == 2) {
+                    const int t = lane & 15, k0 = kc + 16 * ((lane >> 4) & 1);
+                    const s16x4 w =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), k0 + 4 * (t & 3)));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, kc + (lane & 31)));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += s * old[e];
+            }
+    }
+}
+
 // acc += P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
 // first operand row; ldp, ldq are row strides in bytes; `extent_*` is the byte
-// size the buffer resources may address from P and Q.
-template <typename T, class C>
+// size the buffer resources may address from P and Q. SEED: P holds rows
+// row0 .. row0 + BM of a matrix whose tile at (row0, c0) is to be added, times
+// s_seed; stages seed_kb .. seed_kb + BM / KW carry its columns, and each wave
+// adds its part while such a stage is resident (seed_from_stage).
+template <typename T, class C, bool SEED = false>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
-                                             int extent_q, int nk, char *lds, f32x16 (&acc)[C::NBM][C::NBN]) {
+                                             int extent_q, int nk, char *lds, f32x16 (&acc)[C::NBM][C::NBN],
+                                             int seed_kb = 0, float s_seed = 0.f) {
     typedef typename Mfma<T>::frag frag;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -313,6 +361,10 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
             for (int i = 0; i < C::NBM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
+        }
+        if constexpr (SEED) {
+            const int rel = kb - seed_kb;
+            if (rel >= 0 && rel < C::BM * (int)sizeof(T) / ROWB) seed_from_stage<T, C>(sp, rel, s_seed, acc);
         }
     }
 }
@@ -568,10 +620,16 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                            np * ES / C::ROWB, lds, acc);
     } else if constexpr (MODE == kSyrkA) {
-        init_acc<T, C>(A, ldt * ES, row0, col0, s_init, lds, acc);
         const int ld = ldt * ES;
-        const int nk = do_product ? mp * ES / C::ROWB : 0;
-        tile_product<T, C>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk, lds, acc);
+        if (do_product) {
+            // the old tile A[row0.., col0..] passes through the P stages of
+            // columns col0 .. col0 + BM: seed s_init A from there
+            zero_acc<C>(acc);
+            tile_product<T, C, true>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+                                     mp * ES / C::ROWB, lds, acc, col0 * ES / C::ROWB, s_init);
+        } else {
+            init_acc<T, C>(A, ld, row0, col0, s_init, lds, acc);
+        }
     } else {
         zero_acc<C>(acc);
         const int ldb = ldt * ES, ldq = ldxt * ES;
