@@ -196,6 +196,94 @@ def cpu_baseline(ms, budget_s: float):
                       f"{elapsed:.1f} s of work ({total:.1f} s wall)"}
 
 
+def wave_bench(ms, slots: int, tokens: int, reps: int) -> dict:
+    """Wave dispatch against one NS call after the whole backward, on one GPU.
+
+    The backward pass is simulated per tensor, in reverse index order (the
+    order gradients become ready): two bf16 products of `tokens` rows with the
+    tensor's shape (standing in for its weight- and input-gradient GEMMs),
+    then the momentum update M = 0.95 M + G. Sequential: backward, then one
+    ns_orthogonalize_batched call, on one stream. Waves: the backward on one
+    stream records an event when each wave's last momentum is complete, and
+    ns_orthogonalize_waves on a second stream starts each wave on its event.
+    `tail` is the time from the end of the backward to the end of the NS work.
+    """
+    import torch
+    import newton_schulz_quintic_amd as nsq
+    from workloads import device_matrix
+    dev = torch.device("cuda:0")
+    mats = [device_matrix(ms.seed, i, s, std=ms.std) for i, s in enumerate(ms.shapes)]
+    grads = [device_matrix(ms.seed + 1, i, s, std=ms.std) for i, s in enumerate(ms.shapes)]
+    acts = {}
+    for s in ms.shapes:
+        acts.setdefault(s[0], torch.randn(tokens, s[0], device=dev).to(torch.bfloat16) * 0.02)
+    outs = [torch.empty_like(m) for m in mats]
+    wave_of, num = nsq.ns_wave_plan(ms.shapes, slots)
+    order = list(range(ms.n - 1, -1, -1))
+    last_of_wave = {}
+    for i in order:
+        last_of_wave[wave_of[i]] = i
+    need, _ = nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    bwd, nss = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def backward(stream, events):
+        with torch.cuda.stream(stream):
+            for i in order:
+                x = acts[ms.shapes[i][0]]
+                w2 = mats[i].reshape(ms.shapes[i][0], -1)
+                y = x @ w2                      # input-gradient stand-in
+                _ = x.t().contiguous() @ y      # weight-gradient stand-in
+                mats[i].mul_(0.95).add_(grads[i])
+                if events is not None and last_of_wave.get(wave_of[i]) == i:
+                    events[wave_of[i]].record(stream)
+
+    def timed(fn):
+        start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda.synchronize()
+        start.record(torch.cuda.current_stream())
+        fn(mid)
+        end_ev = end
+        torch.cuda.current_stream().wait_stream(bwd)
+        torch.cuda.current_stream().wait_stream(nss)
+        end_ev.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return start.elapsed_time(end_ev), start.elapsed_time(mid)
+
+    def sequential(mid):
+        bwd.wait_stream(torch.cuda.current_stream())
+        backward(bwd, None)
+        mid.record(bwd)
+        nsq.ns_orthogonalize_batched(mats, outs, steps=ms.steps, coeffs=ms.coeffs, workspace=ws, stream=bwd)
+
+    def waves(mid):
+        bwd.wait_stream(torch.cuda.current_stream())
+        nss.wait_stream(torch.cuda.current_stream())
+        events = [torch.cuda.Event() for _ in range(num)]
+        backward(bwd, events)
+        mid.record(bwd)
+        nsq.ns_orthogonalize_waves(mats, outs, wave_of, num, ready_events=events, steps=ms.steps,
+                                   coeffs=ms.coeffs, workspace=ws, stream=nss)
+
+    def backward_only(mid):
+        bwd.wait_stream(torch.cuda.current_stream())
+        backward(bwd, None)
+        mid.record(bwd)
+
+    res = {}
+    for name, fn in (("backward_only", backward_only), ("sequential", sequential), ("waves", waves)):
+        fn_times = [timed(fn) for _ in range(reps + 1)][1:]    # first run warms up
+        tot = sorted(t[0] for t in fn_times)[len(fn_times) // 2]
+        bw = sorted(t[1] for t in fn_times)[len(fn_times) // 2]
+        res[name] = {"total_ms": round(tot, 3), "backward_end_ms": round(bw, 3),
+                     "tail_ms": round(tot - bw, 3)}
+    return {"metric": "NS tail after the last gradient (wave dispatch vs one call after backward)",
+            "unit": "ms", "config": {"workload": ms.name, "matrices": ms.n, "slots": slots,
+                                     "num_waves": num, "tokens": tokens, "reps": reps},
+            "backward_only_ms": res["backward_only"]["total_ms"], "sequential": res["sequential"],
+            "waves": res["waves"], "data": "synthetic"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +295,10 @@ def main():
                     help="pack: pack -> batched NS on the home buffers -> unpack (three calls); fused: "
                          "ns_orthogonalize_routed reads and writes the shard buffers directly. The other "
                          "mode is timed too and reported under `other_routing`")
+    ap.add_argument("--waves", type=int, metavar="SLOTS",
+                    help="measure wave dispatch (tensors per wave = SLOTS) against one NS call after a "
+                         "simulated backward; prints its own JSON line and exits")
+    ap.add_argument("--tokens", type=int, default=4096, help="tokens of the simulated backward (--waves)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -236,6 +328,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ms = build_workload(args.workload)
+    if args.waves:
+        print(json.dumps(wave_bench(ms, args.waves, args.tokens, max(1, args.steps))), flush=True)
+        return
     S = ms.num_shards
     big = args.workload != "routed-square"
     shards_in = make_shards(ms, device_gen=big)

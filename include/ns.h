@@ -247,6 +247,37 @@ ns_status ns_orthogonalize_routed(const ns_route_plan *plan, const void *const *
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * Wave dispatch: Newton-Schulz started wave by wave as gradients become ready
+ * [issue, "Current Progress": backward/forward overlap with dynamic wave
+ *  dispatch]
+ * ------------------------------------------------------------------------ */
+
+/* Static wave partition (host only). Eligible tensors (ndim >= 2) are taken in
+ * the order their gradients become ready -- ready_order [n], a permutation, or
+ * NULL for reverse index order (the order a backward pass produces them) --
+ * and each run of `slots` consecutive ones forms a wave (e.g. 3000 tensors on
+ * 1000 slots: 3 waves). wave_of [n] receives each tensor's wave (-1 for
+ * tensors with ndim < 2); *num_waves the number of waves.
+ * Errors: INVALID_ARG (slots < 1, bad order, NULL outputs), OVERFLOW. */
+ns_status ns_wave_plan(int32_t n, const ns_shape *shapes, const int32_t *ready_order, int32_t slots,
+                       int32_t *wave_of, int32_t *num_waves);
+
+/* ns_orthogonalize_batched run wave by wave on `stream`: for w = 0 ..
+ * num_waves-1 the stream first waits for ready_events[w] (a hipEvent_t passed
+ * as void*, recorded on any stream when wave w's inputs are complete; the
+ * array or an entry may be NULL for no wait), then orthogonalises the tensors
+ * with wave_of[i] == w. Tensors with wave_of[i] < 0 are left alone. Results
+ * are bit-identical to ns_orthogonalize_batched on the same tensors (no
+ * result depends on which tensors share a call). The workspace minimum is that
+ * of ns_workspace_bytes on all n shapes; the waves reuse it in stream order.
+ * Other arguments and errors as for ns_orthogonalize_batched. */
+ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *const *in,
+                                 void *const *out, ns_dtype dtype, int32_t steps, float a, float b,
+                                 float c, float eps, const int32_t *wave_of, int32_t num_waves,
+                                 void *const *ready_events, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* ------------------------------------------------------------------------ *
  * Measurement support
  * ------------------------------------------------------------------------ */
 

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     ns_last_error,
     ns_orthogonalize_batched,
     ns_orthogonalize_routed,
+    ns_orthogonalize_waves,
     ns_pack_shards,
     ns_plan,
     ns_route_plan_create,
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
     ns_timing_read,
     ns_unpack_shards,
     ns_version,
+    ns_wave_plan,
     ns_routed_workspace_bytes,
     ns_workspace_bytes,
 )

@@ -26,7 +26,8 @@ EXPORTS = [
     "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
     "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_routed_workspace_bytes",
-    "ns_orthogonalize_routed", "ns_timing_enable", "ns_timing_read",
+    "ns_orthogonalize_routed", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
+    "ns_timing_read",
 ]
 
 
@@ -62,6 +63,9 @@ _SIGS = {
                                         _SZ, _P]),
     "ns_routed_workspace_bytes": (_I32, [_P, _I32, _P, _P]),
     "ns_orthogonalize_routed": (_I32, [_P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P, _SZ, _P]),
+    "ns_wave_plan": (_I32, [_I32, _P, _P, _I32, _P, _P]),
+    "ns_orthogonalize_waves": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _I32, _P,
+                                      _P, _SZ, _P]),
     "ns_timing_enable": (_I32, [_I32]),
     "ns_timing_read": (_I32, [_I32, _P, _P, _P]),
 }
@@ -310,6 +314,54 @@ def ns_orthogonalize_routed(plan: RoutePlan, shard_in, shard_out, dtype: int, st
                                          float(b), float(c), float(eps),
                                          None if ord_arr is None else _addr(ord_arr),
                                          workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ns_wave_plan(shapes, slots: int, ready_order=None) -> tuple[list[int], int]:
+    """(wave_of, num_waves): tensors in gradient-ready order, ``slots`` per wave (see ns.h)."""
+    n = len(shapes)
+    sh = _shapes(shapes)
+    order = None if ready_order is None else _arr(_I32, ready_order)
+    wave, num = _arr(_I32, [0] * n), _I32(0)
+    _check(lib().ns_wave_plan(n, _addr(sh), None if order is None else _addr(order), slots, _addr(wave),
+                              ctypes.addressof(num)))
+    return list(wave)[:n], num.value
+
+
+def ns_orthogonalize_waves(inputs, outputs, wave_of, num_waves: int, ready_events=None, steps: int = 5,
+                           coeffs=(3.4445, -4.7750, 2.0315), eps: float = 1e-7, workspace=None, stream=None):
+    """ns_orthogonalize_batched wave by wave; wave w waits for ready_events[w]
+    (torch.cuda.Event or None). Returns the workspace."""
+    n = len(inputs)
+    if len(outputs) != n or len(wave_of) != n:
+        raise ValueError("inputs, outputs and wave_of differ in length")
+    if n == 0:
+        return workspace
+    dtype = _dtype_code(inputs[0])
+    for x, y in zip(inputs, outputs):
+        if _dtype_code(x) != dtype or _dtype_code(y) != dtype:
+            raise TypeError("all tensors must share one dtype")
+        if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+            raise ValueError("tensors must be contiguous and outputs shaped like inputs")
+    shapes = [tuple(x.shape) for x in inputs]
+    if workspace is None:
+        import torch
+        need, _ = ns_workspace_bytes(shapes, dtype)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+    evs = None
+    if ready_events is not None:
+        if len(ready_events) != num_waves:
+            raise ValueError("one event (or None) per wave")
+        evs = _arr(_P, [None if e is None else e.cuda_event for e in ready_events])
+    a, b, c = coeffs
+    sh = _shapes(shapes)
+    ins = _arr(_P, [x.data_ptr() for x in inputs])
+    outs = _arr(_P, [y.data_ptr() for y in outputs])
+    waves = _arr(_I32, wave_of)
+    _check(lib().ns_orthogonalize_waves(n, _addr(sh), _addr(ins), _addr(outs), dtype, steps, float(a),
+                                        float(b), float(c), float(eps), _addr(waves), num_waves,
+                                        None if evs is None else _addr(evs), workspace.data_ptr(),
+                                        workspace.numel(), _stream(stream)))
     return workspace
 
 

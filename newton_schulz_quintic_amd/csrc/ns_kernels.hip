@@ -1336,3 +1336,47 @@ extern "C" ns_status ns_orthogonalize_routed(const ns_route_plan *plan, const vo
     return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
                          reinterpret_cast<hipStream_t>(stream));
 }
+
+extern "C" ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *const *in,
+                                            void *const *out, ns_dtype dtype, int32_t steps, float a,
+                                            float b, float c, float eps, const int32_t *wave_of,
+                                            int32_t num_waves, void *const *ready_events, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (num_waves < 0) return fail(NS_ERR_INVALID_ARG, "num_waves = %d < 0", num_waves);
+    if (n > 0 && !wave_of) return fail(NS_ERR_INVALID_ARG, "wave_of is NULL");
+    if (n > 0 && (!in || !out)) return fail(NS_ERR_INVALID_ARG, "in and out are required");
+    const size_t es = dtype == NS_BF16 ? 2 : 4;
+    PieceLists pieces(n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (wave_of[i] >= num_waves)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: wave %d >= num_waves %d", i, wave_of[i], num_waves);
+        if (!info[i].active || wave_of[i] < 0) continue;
+        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
+        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i])});
+    }
+    size_t all, need;
+    workspace_need(info, &all, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(NS_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, need);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t w = 0; w < num_waves; ++w) {
+        std::vector<MatInfo> wi = info;
+        bool any = false;
+        for (int32_t i = 0; i < n; ++i) {
+            wi[i].active = info[i].active && wave_of[i] == w;
+            any = any || wi[i].active;
+        }
+        if (ready_events && ready_events[w])
+            NSQ_HIP(hipStreamWaitEvent(hs, reinterpret_cast<hipEvent_t>(ready_events[w]), 0));
+        if (!any) continue;
+        if ((st = orthogonalize(wi, pieces, dtype, steps, a, b, c, eps, nullptr, workspace, workspace_bytes, hs)))
+            return st;
+    }
+    return NS_OK;
+}

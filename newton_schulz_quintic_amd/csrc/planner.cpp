@@ -282,3 +282,33 @@ extern "C" ns_status ns_route_plan_query(const ns_route_plan *plan, int64_t *sha
 }
 
 extern "C" void ns_route_plan_destroy(ns_route_plan *plan) { delete plan; }
+
+extern "C" ns_status ns_wave_plan(int32_t n, const ns_shape *shapes, const int32_t *ready_order,
+                                  int32_t slots, int32_t *wave_of, int32_t *num_waves) {
+    if (n < 0) return fail(NS_ERR_INVALID_ARG, "n = %d < 0", n);
+    if (slots < 1) return fail(NS_ERR_INVALID_ARG, "slots = %d < 1", slots);
+    if (!num_waves || (n > 0 && (!shapes || !wave_of)))
+        return fail(NS_ERR_INVALID_ARG, "shapes, wave_of and num_waves are required");
+    std::vector<char> eligible(n, 0), seen(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t rows, cols;
+        ns_status st = matrix_view(shapes[i], i, &rows, &cols);
+        if (st) return st;
+        eligible[i] = rows >= 0;
+    }
+    std::vector<int32_t> order(n);
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t i = ready_order ? ready_order[k] : n - 1 - k;
+        if (i < 0 || i >= n || seen[i])
+            return fail(NS_ERR_INVALID_ARG, "ready_order is not a permutation of 0..%d", n - 1);
+        seen[i] = 1;
+        order[k] = i;
+    }
+    int64_t k = 0;
+    std::vector<int32_t> w(n, -1);
+    for (int32_t i : order)
+        if (eligible[i]) w[i] = (int32_t)(k++ / slots);
+    std::copy(w.begin(), w.end(), wave_of);
+    *num_waves = (int32_t)((k + slots - 1) / slots);
+    return NS_OK;
+}

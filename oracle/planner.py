@@ -187,3 +187,36 @@ def route_offsets(shapes, split_rows, home, num_shards: int):
             home_elems[h] += rows * cols
     return {"shard_offset": shard_offset, "row_start": row_start, "home_offset": home_offset,
             "shard_elems": shard_elems, "home_elems": home_elems}
+
+
+def wave_plan(shapes, slots: int, ready_order=None):
+    """Static partition of the Newton-Schulz work into waves.
+
+    "[GTP][Muon] Optimize Muon step performance" page, "Current Progress",
+    the backward/forward overlap item: the NS work is split statically into
+    waves sized to the available slots (its example: 3000 tensors on 1000
+    slots make 3 waves), and each wave is started as the gradient buckets it
+    needs complete. Reading taken where the page is silent: tensors join waves
+    in the order their gradients become ready -- ``ready_order``, by default
+    reverse index order, the order a backward pass produces them -- and each
+    run of ``slots`` consecutive eligible tensors in that order is one wave.
+    Tensors with fewer than 2 dims take no part (owner_planning page,
+    ``select_ge_2d_params``) and get wave -1.
+
+    Returns (wave_of, num_waves). Pinned by: the page's 3000 / 1000 example,
+    hand cases and counting identities in tests/test_oracle_planner.py.
+    """
+    n = len(shapes)
+    if slots < 1:
+        raise ValueError("slots must be >= 1")
+    order = list(range(n - 1, -1, -1)) if ready_order is None else [int(i) for i in ready_order]
+    if sorted(order) != list(range(n)):
+        raise ValueError("ready_order is not a permutation")
+    wave_of = [-1] * n
+    k = 0
+    for i in order:
+        if matrix_view(shapes[i]) is None:
+            continue
+        wave_of[i] = k // slots
+        k += 1
+    return wave_of, (k + slots - 1) // slots

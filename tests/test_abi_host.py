@@ -235,3 +235,34 @@ def test_routed_workspace_and_errors():
     assert call(plan.handle, ctypes.addressof(ok), ctypes.addressof(ok)) == -7   # no workspace
     empty = nsq.ns_route_plan_create([], 2, [], [], 2)
     assert call(empty.handle, None, None) == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_wave_plan_matches_oracle(seed):
+    rng = random.Random(700 + seed)
+    n = rng.randint(0, 50)
+    shapes = [tuple(rng.randint(0, 9) for _ in range(rng.choice([1, 2, 3]))) for _ in range(n)]
+    slots = rng.randint(1, 10)
+    order = None
+    if rng.random() < 0.5:
+        order = list(range(n))
+        rng.shuffle(order)
+    assert nsq.ns_wave_plan(shapes, slots, order) == tuple(planner.wave_plan(shapes, slots, order))
+
+
+def test_wave_plan_and_waves_errors():
+    assert nsq.ns_wave_plan([(8, 8)] * 3000, 1000)[1] == 3
+    assert _status(nsq.ns_wave_plan, [(2, 2)], 0) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_wave_plan, [(2, 2), (3, 3)], 1, [0, 0]) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_wave_plan, [(2, 2)], 1, [1]) == "NS_ERR_INVALID_ARG"
+    lib = nsq.lib()
+    sh = _lib._shapes([(4, 4)])
+    ptrs = _lib._arr(ctypes.c_void_p, [256])
+    w = _lib._arr(ctypes.c_int32, [1])
+    call = lambda waves, num: lib.ns_orthogonalize_waves(  # noqa: E731
+        1, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs), 0, 5, 3.4, -4.7, 2.0, 1e-7,
+        waves, num, None, None, 0, None)
+    assert call(ctypes.addressof(w), 1) == -1          # wave 1 >= num_waves 1
+    assert call(None, 1) == -1
+    assert call(ctypes.addressof(w), -1) == -1
+    assert call(ctypes.addressof(w), 2) == -7          # no workspace

@@ -156,3 +156,39 @@ def test_route_offsets_worked_example():
     assert off["shard_offset"][0][0] == ex["printed"]["rank1_recv_offsets"][0]["offset"]
     assert d["split_rows"][0][0] * 4 == ex["printed"]["rank0_send_buffer_elems_to_owner1"]
     assert ex["printed"]["layout_size"] == sum(off["home_elems"])
+
+
+def test_wave_plan_page_example_and_hand_cases():
+    # issue page, "Current Progress": 3000 tensors on 1000 slots -> 3 waves.
+    shapes = [(8, 8)] * 3000
+    wave, num = planner.wave_plan(shapes, 1000)
+    assert num == 3
+    assert [wave.count(w) for w in range(3)] == [1000, 1000, 1000]
+    # default ready order is reverse index order: the last 1000 tensors go first
+    assert wave[2999] == 0 and wave[2000] == 0 and wave[1999] == 1 and wave[0] == 2
+    # more slots than tensors: one wave
+    assert planner.wave_plan([(2, 2)] * 5, 8) == ([0] * 5, 1)
+    # a caller-given order, and tensors with < 2 dims left out (no slot used)
+    w, n = planner.wave_plan([(3, 3), (4,), (2, 5), (6, 1), (7,)], 2, ready_order=[0, 1, 2, 3, 4])
+    assert (w, n) == ([0, -1, 0, 1, -1], 2)
+    assert planner.wave_plan([], 3) == ([], 0)
+    assert planner.wave_plan([(5,)], 3) == ([-1], 0)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_wave_plan_counting_identities(seed):
+    rng = random.Random(500 + seed)
+    n = rng.randint(0, 60)
+    shapes = [tuple(rng.randint(1, 9) for _ in range(rng.choice([1, 2, 3]))) for _ in range(n)]
+    slots = rng.randint(1, 12)
+    order = list(range(n))
+    rng.shuffle(order)
+    wave, num = planner.wave_plan(shapes, slots, order)
+    eligible = [i for i in order if len(shapes[i]) >= 2]
+    assert num == -(-len(eligible) // slots)
+    # every wave but the last is full, waves are consecutive runs of the order
+    for w in range(num):
+        members = [i for i in eligible if wave[i] == w]
+        assert len(members) == (slots if w < num - 1 else len(eligible) - slots * (num - 1))
+        assert members == eligible[w * slots:w * slots + len(members)]
+    assert all(wave[i] == -1 for i in range(n) if len(shapes[i]) < 2)
