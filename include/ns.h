@@ -210,6 +210,23 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                    const int32_t *order, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* ns_orthogonalize_batched on strided views: tensor i's input row r starts
+ * at in[i] + r * in_ld[i] elements and its output row at out[i] + r *
+ * out_ld[i] (rows as given, i.e. dims[0]; a row holds dims[1] * ... *
+ * dims[ndim-1] contiguous elements). Row strides must be >= that row length;
+ * in_ld / out_ld may be NULL for contiguous rows. For NS on sub-blocks of a
+ * larger matrix in place, e.g. the Q, K and V blocks of a fused weight split
+ * by rows or by columns ([issue], "Current Progress": split-QKV support).
+ * Views may share memory only as in == out with equal strides (in place);
+ * distinct outputs must not overlap. Results are bit-identical to
+ * ns_orthogonalize_batched on contiguous copies. Other arguments and errors
+ * as for ns_orthogonalize_batched (workspace from ns_workspace_bytes). */
+ns_status ns_orthogonalize_strided(int32_t n, const ns_shape *shapes, const void *const *in,
+                                   const int64_t *in_ld, void *const *out, const int64_t *out_ld,
+                                   ns_dtype dtype, int32_t steps, float a, float b, float c, float eps,
+                                   const int32_t *order, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* ------------------------------------------------------------------------ *
  * Fused routing: Newton-Schulz straight from and back to the shard buffers
  * [layer_sharded, route_to_ns_home / route_from_ns_home around the

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     ns_last_error,
     ns_orthogonalize_batched,
     ns_orthogonalize_routed,
+    ns_orthogonalize_strided,
     ns_orthogonalize_waves,
     ns_pack_shards,
     ns_plan,

@@ -25,7 +25,7 @@ STATUS = {
 EXPORTS = [
     "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
-    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_routed_workspace_bytes",
+    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_orthogonalize_strided", "ns_routed_workspace_bytes",
     "ns_orthogonalize_routed", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
     "ns_timing_read",
 ]
@@ -61,6 +61,8 @@ _SIGS = {
     "ns_workspace_bytes": (_I32, [_I32, _P, _I32, _P, _P]),
     "ns_orthogonalize_batched": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P,
                                         _SZ, _P]),
+    "ns_orthogonalize_strided": (_I32, [_I32, _P, _P, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P,
+                                        _P, _SZ, _P]),
     "ns_routed_workspace_bytes": (_I32, [_P, _I32, _P, _P]),
     "ns_orthogonalize_routed": (_I32, [_P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P, _SZ, _P]),
     "ns_wave_plan": (_I32, [_I32, _P, _P, _I32, _P, _P]),
@@ -283,6 +285,50 @@ def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
                                           float(a), float(b), float(c), float(eps),
                                           None if ord_arr is None else _addr(ord_arr),
                                           workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def _row_stride(t) -> int:
+    """Row stride (elements) of a view whose rows (dims 1..) are contiguous."""
+    if t.dim() < 2:
+        raise ValueError("views need at least 2 dims")
+    inner = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.size(d) > 1 and t.stride(d) != inner:
+            raise ValueError("each row of a view (dims 1..) must be contiguous")
+        inner *= t.size(d)
+    return t.stride(0) if t.size(0) > 1 else inner
+
+
+def ns_orthogonalize_strided(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315),
+                             eps: float = 1e-7, order=None, workspace=None, stream=None):
+    """ns_orthogonalize_batched on torch views with contiguous rows and any row
+    stride (e.g. column blocks of a fused weight); outputs may be views too."""
+    n = len(inputs)
+    if len(outputs) != n:
+        raise ValueError("inputs and outputs differ in length")
+    if n == 0:
+        return workspace
+    dtype = _dtype_code(inputs[0])
+    for x, y in zip(inputs, outputs):
+        if _dtype_code(x) != dtype or _dtype_code(y) != dtype or x.shape != y.shape:
+            raise ValueError("tensors must share one dtype and outputs be shaped like inputs")
+    shapes = [tuple(x.shape) for x in inputs]
+    if workspace is None:
+        import torch
+        need, _ = ns_workspace_bytes(shapes, dtype)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+    a, b, c = coeffs
+    sh = _shapes(shapes)
+    ins = _arr(_P, [x.data_ptr() for x in inputs])
+    outs = _arr(_P, [y.data_ptr() for y in outputs])
+    lds_in = _arr(_I64, [_row_stride(x) for x in inputs])
+    lds_out = _arr(_I64, [_row_stride(y) for y in outputs])
+    ord_arr = None if order is None else _arr(_I32, order)
+    _check(lib().ns_orthogonalize_strided(n, _addr(sh), _addr(ins), _addr(lds_in), _addr(outs), _addr(lds_out),
+                                          dtype, steps, float(a), float(b), float(c), float(eps),
+                                          None if ord_arr is None else _addr(ord_arr), workspace.data_ptr(),
+                                          workspace.numel(), _stream(stream)))
     return workspace
 
 

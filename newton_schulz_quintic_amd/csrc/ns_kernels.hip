@@ -84,9 +84,11 @@ struct NsProb {
 };
 
 // Rows [row0, next piece's row0) of a tensor as stored (rows x cols,
-// row-major): element (r, c) of the input is at in + ((r - row0) cols + c) es,
-// of the output at out + ((r - row0) cols + c) es. An unrouted tensor is one
-// piece; a routed one has a piece per shard buffer that holds some of its rows
+// row-major with row strides ld_in / ld_out elements): element (r, c) of the
+// input is at in + ((r - row0) ld_in + c) es, of the output at
+// out + ((r - row0) ld_out + c) es. An unrouted tensor is one piece (strided
+// for a sub-block of a larger matrix, e.g. one of Q, K, V in a fused weight);
+// a routed one has a piece per shard buffer that holds some of its rows
 // (route_to_ns_home / route_from_ns_home of "core.optimizer.layer_sharded_a2a"
 // move exactly these pieces). Pieces of a tensor are sorted by row0, the first
 // has row0 = 0 and none is empty.
@@ -94,8 +96,9 @@ struct RowPiece {
     int64_t row0;
     const char *in;
     char *out;
+    int64_t ld_in, ld_out;
 };
-static_assert(sizeof(RowPiece) == 24, "RowPiece layout");
+static_assert(sizeof(RowPiece) == 40, "RowPiece layout");
 
 // A tile of one tensor: (ti, tj) in the tile grid of the launch that uses it.
 // pieces[piece .. piece + npiece) are the pieces holding the tensor rows (as
@@ -462,7 +465,7 @@ __device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowP
     constexpr int E = 16 / (int)sizeof(T);
     if (row >= rows || col >= cols) return;
     const RowPiece pc = find_piece(band, nband, row);
-    char *dst = pc.out + (row - pc.row0) * cols * (int64_t)sizeof(T);
+    char *dst = pc.out + (row - pc.row0) * pc.ld_out * (int64_t)sizeof(T);
     if (pr.vec_out && col + E <= cols) {
         store16<T>(dst, col, w);
         return;
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         if (gr < rows) {
             RowPiece pc = one;   // by value: the reads below stay global loads
             if (multi) pc = find_piece(band, tr.npiece, gr);
-            const char *src = pc.in + ((gr - pc.row0) * cols + gc) * ES;
+            const char *src = pc.in + ((gr - pc.row0) * pc.ld_in + gc) * ES;
             if (vec_in && gc + E <= cols) {
                 w = *(const NSQ_GLOBAL i32x4 *)src;
             } else {
@@ -844,8 +847,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_scale_out_kernel(const NsProb
         const int64_t r = r0 + e / kPrepTile, c = c0 + e % kPrepTile;
         if (r < rows && c < cols) {
             const RowPiece pc = find_piece(pieces + tr.piece, tr.npiece, r);
-            const int64_t k = (r - pc.row0) * cols + c;
-            gp<T>(pc.out)[k] = from_f32<T>(to_f32<T>(gp<T>(pc.in)[k]) * sc);
+            gp<T>(pc.out)[(r - pc.row0) * pc.ld_out + c] =
+                from_f32<T>(to_f32<T>(gp<T>(pc.in)[(r - pc.row0) * pc.ld_in + c]) * sc);
         }
     }
 }
@@ -1042,11 +1045,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         base += mi.buf_bytes;
         const std::vector<RowPiece> &pc = pieces[idx];
         const int32_t pbase = (int32_t)gpieces.size();
-        const int64_t row_bytes = (mi.tall ? mi.m : mi.n) * es;   // as stored
-        bool vin = row_bytes % 16 == 0, vout = vin;
+        bool vin = true, vout = true;   // 16-byte accesses: aligned bases and row strides
         for (const RowPiece &q : pc) {
-            vin = vin && reinterpret_cast<uintptr_t>(q.in) % 16 == 0;
-            vout = vout && reinterpret_cast<uintptr_t>(q.out) % 16 == 0;
+            vin = vin && reinterpret_cast<uintptr_t>(q.in) % 16 == 0 && q.ld_in * es % 16 == 0;
+            vout = vout && reinterpret_cast<uintptr_t>(q.out) % 16 == 0 && q.ld_out * es % 16 == 0;
             gpieces.push_back(q);
         }
         p.vec_in = vin;
@@ -1286,7 +1288,39 @@ extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
         if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
         if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
             return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
-        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i])});
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]),
+                                     info[i].cols, info[i].cols});
+    }
+    return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" ns_status ns_orthogonalize_strided(int32_t n, const ns_shape *shapes, const void *const *in,
+                                              const int64_t *in_ld, void *const *out, const int64_t *out_ld,
+                                              ns_dtype dtype, int32_t steps, float a, float b, float c,
+                                              float eps, const int32_t *order, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (n == 0) return NS_OK;
+    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
+    const size_t es = dtype == NS_BF16 ? 2 : 4;
+    PieceLists pieces(n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!info[i].active) continue;
+        const int64_t li = in_ld ? in_ld[i] : info[i].cols, lo = out_ld ? out_ld[i] : info[i].cols;
+        if (li < info[i].cols || lo < info[i].cols)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: row stride (%lld, %lld) < cols %lld", i, (long long)li,
+                        (long long)lo, (long long)info[i].cols);
+        int64_t span;   // elements from a row's start to the last row's end fit in 63 bits
+        if (__builtin_mul_overflow(std::max(li, lo), info[i].rows, &span))
+            return fail(NS_ERR_OVERFLOW, "tensor %d: strided extent overflows", i);
+        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
+        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]), li, lo});
     }
     return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
                          reinterpret_cast<hipStream_t>(stream));
@@ -1329,7 +1363,7 @@ extern "C" ns_status ns_orthogonalize_routed(const ns_route_plan *plan, const vo
             if (r == 0) continue;
             const int64_t off = plan->shard_offset[(size_t)i * S + s] * es;
             pieces[i].push_back(RowPiece{row0, static_cast<const char *>(shard_in[s]) + off,
-                                         static_cast<char *>(shard_out[s]) + off});
+                                         static_cast<char *>(shard_out[s]) + off, info[i].cols, info[i].cols});
             row0 += r;
         }
     }
@@ -1358,7 +1392,8 @@ extern "C" ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, c
         if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
         if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
             return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
-        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i])});
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]),
+                                     info[i].cols, info[i].cols});
     }
     size_t all, need;
     workspace_need(info, &all, &need);

@@ -266,3 +266,20 @@ def test_wave_plan_and_waves_errors():
     assert call(None, 1) == -1
     assert call(ctypes.addressof(w), -1) == -1
     assert call(ctypes.addressof(w), 2) == -7          # no workspace
+
+
+def test_strided_errors():
+    lib = nsq.lib()
+    sh = _lib._shapes([(4, 6)])
+    ptrs = _lib._arr(ctypes.c_void_p, [256])
+    call = lambda li, lo: lib.ns_orthogonalize_strided(  # noqa: E731
+        1, ctypes.addressof(sh), ctypes.addressof(ptrs), li, ctypes.addressof(ptrs), lo, 0, 5, 3.4, -4.7, 2.0,
+        1e-7, None, None, 0, None)
+    short = _lib._arr(ctypes.c_int64, [5])
+    ok = _lib._arr(ctypes.c_int64, [8])
+    assert call(ctypes.addressof(short), None) == -1      # row stride below the row length
+    assert call(None, ctypes.addressof(short)) == -1
+    huge = _lib._arr(ctypes.c_int64, [2 ** 62])
+    assert call(ctypes.addressof(huge), None) == -5
+    assert call(ctypes.addressof(ok), ctypes.addressof(ok)) == -7   # valid; no workspace
+    assert call(None, None) == -7
