@@ -129,8 +129,9 @@ def build_workload(name: str):
     return ms
 
 
-def make_shards(ms, device_gen: bool):
-    """Shard buffers (device) holding every matrix's row pieces, end to end."""
+def make_shards(ms, device_gen: bool, shard_dim: int = 0):
+    """Shard buffers (device) holding every matrix's slices along shard_dim
+    (row pieces for 0), end to end."""
     import numpy as np
     import torch
     from workloads import device_matrix, host_matrix
@@ -142,10 +143,11 @@ def make_shards(ms, device_gen: bool):
         else:
             bits = host_matrix(ms.seed, i, shape, std=ms.std)
             full = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        full = full.reshape(shape)
         r0 = 0
         for s in range(S):
             r = ms.split_rows[i][s]
-            parts[s].append(full[r0:r0 + r].reshape(-1))
+            parts[s].append(full.narrow(shard_dim, r0, r).reshape(-1))
             r0 += r
     shards = []
     for s in range(S):
@@ -299,6 +301,9 @@ def main():
                     help="measure wave dispatch (tensors per wave = SLOTS) against one NS call after a "
                          "simulated backward; prints its own JSON line and exits")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens of the simulated backward (--waves)")
+    ap.add_argument("--shard-dim", type=int, default=0,
+                    help="cut every tensor's shards along this dimension (0 = rows; 1 = the TP stage's "
+                         "column shards, evenly over the workload's shard count); pack / unpack routing only")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -328,16 +333,23 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ms = build_workload(args.workload)
+    if args.shard_dim:
+        from workloads import even_split_rows
+        if args.routing == "fused":
+            raise SystemExit("fused routing reads row shards only; use --routing pack with --shard-dim")
+        ms.split_rows = [even_split_rows(shape[args.shard_dim], ms.num_shards) for shape in ms.shapes]
+        ms.name += f"-shard-dim{args.shard_dim}"
     if args.waves:
         print(json.dumps(wave_bench(ms, args.waves, args.tokens, max(1, args.steps))), flush=True)
         return
     S = ms.num_shards
     big = args.workload != "routed-square"
-    shards_in = make_shards(ms, device_gen=big)
+    shards_in = make_shards(ms, device_gen=big, shard_dim=args.shard_dim)
 
     # route plan: built once, reused every step
-    p = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
-    plan = nsq.ns_route_plan_create(ms.shapes, S, ms.split_rows, p["home"], 2)
+    # homes: LPT over the row holders (ns_plan's candidates are row shards)
+    p = nsq.ns_plan(ms.shapes, ms.steps, S, None if args.shard_dim else ms.split_rows)
+    plan = nsq.ns_route_plan_create_axis(ms.shapes, S, ms.split_rows, [args.shard_dim] * ms.n, p["home"], 2)
     q = nsq.ns_route_plan_query(plan)
     nsq.ns_route_plan_upload(plan)
     homes = [torch.empty(n, dtype=torch.bfloat16, device=dev) if n else None for n in q["home_elems"]]
@@ -350,20 +362,23 @@ def main():
         for d in shape:
             numel *= d
         views.append(homes[h][off:off + numel].view(shape))
-    need = max(nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)[0],
-               nsq.ns_routed_workspace_bytes(plan, nsq.NS_BF16)[0])
+    need = nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)[0]
+    if not args.shard_dim:
+        need = max(need, nsq.ns_routed_workspace_bytes(plan, nsq.NS_BF16)[0])
     workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
+    plan_split = None if args.shard_dim else ms.split_rows
+
     def step_pack():
-        pl = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
+        pl = nsq.ns_plan(ms.shapes, ms.steps, S, plan_split)
         nsq.ns_pack_shards(plan, shards_in, homes, stream)
         nsq.ns_orthogonalize_batched(views, views, steps=ms.steps, coeffs=ms.coeffs, order=pl["order"],
                                      workspace=workspace, stream=stream)
         nsq.ns_unpack_shards(plan, homes, shards_out, stream)
 
     def step_fused():
-        pl = nsq.ns_plan(ms.shapes, ms.steps, S, ms.split_rows)
+        pl = nsq.ns_plan(ms.shapes, ms.steps, S, plan_split)
         nsq.ns_orthogonalize_routed(plan, shards_in, shards_out, nsq.NS_BF16, steps=ms.steps,
                                     coeffs=ms.coeffs, order=pl["order"], workspace=workspace, stream=stream)
 
@@ -397,14 +412,16 @@ def main():
         nsq.ns_timing_enable(False)
         breakdown = {name: nsq.ns_timing_read(k) for k, name in TIMING_KINDS.items()}
     # The other routing mode, same inputs and step count, no instrumentation.
-    for _ in range(args.warmup):
-        other()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        other()
-    torch.cuda.synchronize()
-    ms_other = (time.perf_counter() - t2) * 1e3 / args.steps
+    ms_other = None
+    if not args.shard_dim:
+        for _ in range(args.warmup):
+            other()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            other()
+        torch.cuda.synchronize()
+        ms_other = (time.perf_counter() - t2) * 1e3 / args.steps
 
     flops = sum(alg_flops(*oriented(s), ms.steps, ms.coeffs[2] != 0.0) for s in ms.shapes)
     dense = sum(ms.steps * (4 * m * m * n + 2 * m ** 3) for m, n in (oriented(s) for s in ms.shapes))
@@ -424,14 +441,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": ms.name, "matrices": ms.n, "distinct_shapes": len(set(ms.shapes)),
                    "shards": S, "ns_steps": ms.steps, "coeffs": list(ms.coeffs),
-                   "homes_used": len(set(p["home"])), "routing": args.routing},
+                   "homes_used": len(set(p["home"])), "routing": args.routing,
+                   "shard_dim": args.shard_dim},
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "alg_flops_per_step": flops,
         "dense_equiv_flops_per_step": float(dense),
-        "other_routing": {"routing": "fused" if args.routing == "pack" else "pack",
-                          "ms_per_step": round(ms_other, 4),
-                          "value": round(ms.n / (ms_other * 1e-3), 3)},
+        "other_routing": None if ms_other is None else {
+            "routing": "fused" if args.routing == "pack" else "pack", "ms_per_step": round(ms_other, 4),
+            "value": round(ms.n / (ms_other * 1e-3), 3)},
     }
     if not args.no_kernel_timing:
         t = breakdown

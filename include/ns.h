@@ -122,6 +122,24 @@ ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int32_t num_sh
                                const int64_t *split_rows, const int32_t *home,
                                int32_t elem_bytes, ns_route_plan **out);
 
+/* Route plan for shards cut along any dimension [layer_sharded,
+ * route_to_ns_home / route_from_ns_home: `shard_dim`, 0 for the GTP_remat
+ * stage, the param's partition_dim for the TP stage]. Tensor i is split along
+ * shard_dim[i] (0 <= shard_dim[i] < ndim; NULL = all 0, which is
+ * ns_route_plan_create) into split_sizes[i * num_shards + s] slices, summing
+ * to dims[shard_dim[i]]. Shard buffer s holds, for every tensor in increasing
+ * index order, its slice along that dimension (the slices follow each other
+ * in buffer order), flattened row-major; home buffers are as above. Pack and
+ * unpack move a slice along dimension d > 0 as strided runs in the home
+ * buffer. The two-stage exchange (rows within the GTP_remat group, then
+ * partition_dim within the TP group) is two plans applied in turn.
+ * ns_orthogonalize_routed accepts only plans whose tensors are split along
+ * dimension 0 or held by a single shard. Errors as ns_route_plan_create, plus
+ * INVALID_ARG for a shard_dim out of range. */
+ns_status ns_route_plan_create_axis(int32_t n, const ns_shape *shapes, int32_t num_shards,
+                                    const int64_t *split_sizes, const int32_t *shard_dim,
+                                    const int32_t *home, int32_t elem_bytes, ns_route_plan **out);
+
 /* Any output pointer may be NULL.
  * shard_elems [S], home_elems [S]: buffer sizes in elements.
  * home_offset [n]: element offset of tensor i in its home buffer.

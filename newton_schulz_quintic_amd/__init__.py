@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     ns_pack_shards,
     ns_plan,
     ns_route_plan_create,
+    ns_route_plan_create_axis,
     ns_route_plan_destroy,
     ns_route_plan_query,
     ns_route_plan_upload,

@@ -23,7 +23,8 @@ STATUS = {
     -7: "NS_ERR_WORKSPACE", -8: "NS_ERR_DTYPE", -9: "NS_ERR_HIP",
 }
 EXPORTS = [
-    "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_query",
+    "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_create_axis",
+    "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
     "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_orthogonalize_strided", "ns_routed_workspace_bytes",
     "ns_orthogonalize_routed", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
@@ -53,6 +54,7 @@ _SIGS = {
     "ns_version": (ctypes.c_char_p, []),
     "ns_plan": (_I32, [_I32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "ns_route_plan_create": (_I32, [_I32, _P, _I32, _P, _P, _I32, ctypes.POINTER(_P)]),
+    "ns_route_plan_create_axis": (_I32, [_I32, _P, _I32, _P, _P, _P, _I32, ctypes.POINTER(_P)]),
     "ns_route_plan_query": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
     "ns_route_plan_upload": (_I32, [_P, _P, _P]),
     "ns_route_plan_destroy": (None, [_P]),
@@ -186,6 +188,21 @@ def ns_route_plan_create(shapes, num_shards: int, split_rows, home, elem_bytes: 
     split, homes = _arr(_I64, flat), _arr(_I32, home)     # held alive across the call
     _check(lib().ns_route_plan_create(n, _addr(sh), num_shards, _addr(split), _addr(homes),
                                       elem_bytes, ctypes.byref(out)))
+    return RoutePlan(out.value, n, num_shards, elem_bytes)
+
+
+def ns_route_plan_create_axis(shapes, num_shards: int, split_sizes, shard_dim, home,
+                              elem_bytes: int) -> RoutePlan:
+    """Route plan with tensor i split along shard_dim[i] (see ns.h)."""
+    n = len(shapes)
+    sh = _shapes(shapes)
+    flat = [int(r) for row in split_sizes for r in row]
+    if len(flat) != n * num_shards or len(shard_dim) != n:
+        raise ValueError("split_sizes must be n x num_shards and shard_dim n long")
+    out = _P()
+    split, dims, homes = _arr(_I64, flat), _arr(_I32, shard_dim), _arr(_I32, home)
+    _check(lib().ns_route_plan_create_axis(n, _addr(sh), num_shards, _addr(split), _addr(dims), _addr(homes),
+                                           elem_bytes, ctypes.byref(out)))
     return RoutePlan(out.value, n, num_shards, elem_bytes)
 
 

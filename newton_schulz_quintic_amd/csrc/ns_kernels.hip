@@ -1249,6 +1249,10 @@ ns_status describe_routed(const ns_route_plan *plan, ns_dtype dtype, std::vector
     for (int32_t i = 0; i < plan->n; ++i) {
         int64_t k = 0;
         for (int32_t s = 0; s < S; ++s) k += plan->split_rows[(size_t)i * S + s] > 0;
+        if (plan->shard_dim[i] != 0 && k > 1 && info[i].active)
+            return fail(NS_ERR_PLAN_MISMATCH,
+                        "tensor %d is split along dim %d: fused routing reads row shards only (pack first)", i,
+                        plan->shard_dim[i]);
         info[i].npieces = std::max<int64_t>(k, 1);
     }
     return NS_OK;

@@ -157,9 +157,12 @@ extern "C" ns_status ns_plan(int32_t n, const ns_shape *shapes, int32_t steps, i
     return NS_OK;
 }
 
-extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int32_t num_shards,
-                                          const int64_t *split_rows, const int32_t *home,
-                                          int32_t elem_bytes, ns_route_plan **out) {
+// Route plan for shards cut along a per-tensor dimension (0 = rows). Shard s
+// holds, for every tensor in index order, its slice of width split[i][s] along
+// shard_dim[i], flattened row-major; homes hold complete tensors in index order.
+static ns_status route_plan_build(int32_t n, const ns_shape *shapes, int32_t num_shards,
+                                  const int64_t *split, const int32_t *shard_dim, const int32_t *home,
+                                  int32_t elem_bytes, ns_route_plan **out) {
     if (!out) return fail(NS_ERR_INVALID_ARG, "out is NULL");
     if (n < 0) return fail(NS_ERR_INVALID_ARG, "n = %d < 0", n);
     if (num_shards < 1 || num_shards > NS_MAX_SHARDS)
@@ -167,8 +170,8 @@ extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int
                     NS_MAX_SHARDS);
     if (elem_bytes != 2 && elem_bytes != 4)
         return fail(NS_ERR_DTYPE, "elem_bytes = %d (must be 2 or 4)", elem_bytes);
-    if (n > 0 && (!shapes || !split_rows || !home))
-        return fail(NS_ERR_INVALID_ARG, "shapes, split_rows and home are required");
+    if (n > 0 && (!shapes || !split || !home))
+        return fail(NS_ERR_INVALID_ARG, "shapes, split sizes and home are required");
 
     const int32_t S = num_shards;
     auto plan = new ns_route_plan();
@@ -177,50 +180,64 @@ extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int
     plan->elem_bytes = elem_bytes;
     if (n > 0) {
         plan->shapes.assign(shapes, shapes + n);
-        plan->split_rows.assign(split_rows, split_rows + (size_t)n * S);
+        plan->split_rows.assign(split, split + (size_t)n * S);
     }
+    plan->shard_dim.assign(n, 0);
     plan->shard_elems.assign(S, 0);
     plan->home_elems.assign(S, 0);
     plan->home_offset.assign(n, 0);
     plan->shard_offset.assign((size_t)n * S, 0);
-    std::vector<int64_t> rows(n), cols(n);
+    // per tensor: runs (product of the dims before shard_dim), extent of
+    // shard_dim, inner (product of the dims after it)
+    std::vector<int64_t> outer(n), extent(n), inner(n);
 
     auto bad = [&](ns_status st) {
         delete plan;
         return st;
     };
     for (int32_t i = 0; i < n; ++i) {
-        ns_status st = matrix_view(shapes[i], i, &rows[i], &cols[i]);
+        int64_t rows, cols;
+        ns_status st = matrix_view(shapes[i], i, &rows, &cols);
         if (st) return bad(st);
-        if (rows[i] < 0)
+        if (rows < 0)
             return bad(fail(NS_ERR_INVALID_ARG, "tensor %d: routed tensors need ndim >= 2", i));
         if (home[i] < 0 || home[i] >= S)
             return bad(fail(NS_ERR_HOME_RANGE, "tensor %d: home %d outside [0, %d)", i, home[i], S));
+        const int32_t d = shard_dim ? shard_dim[i] : 0;
+        if (d < 0 || d >= shapes[i].ndim)
+            return bad(fail(NS_ERR_INVALID_ARG, "tensor %d: shard_dim %d outside [0, %d)", i, d, shapes[i].ndim));
+        plan->shard_dim[i] = d;
+        int64_t o = 1, in = 1;   // no overflow: their product with the extent is the element count
+        for (int32_t k = 0; k < d; ++k) o *= shapes[i].dims[k];
+        for (int32_t k = d + 1; k < shapes[i].ndim; ++k) in *= shapes[i].dims[k];
+        outer[i] = o;
+        extent[i] = shapes[i].dims[d];
+        inner[i] = in;
         int64_t sum = 0;
         for (int32_t s = 0; s < S; ++s) {
-            int64_t r = split_rows[(int64_t)i * S + s];
-            if (r < 0) return bad(fail(NS_ERR_INVALID_ARG, "tensor %d: negative split rows", i));
+            int64_t r = split[(int64_t)i * S + s];
+            if (r < 0) return bad(fail(NS_ERR_INVALID_ARG, "tensor %d: negative split size", i));
             if (__builtin_add_overflow(sum, r, &sum))
-                return bad(fail(NS_ERR_OVERFLOW, "tensor %d: split rows overflow", i));
+                return bad(fail(NS_ERR_OVERFLOW, "tensor %d: split sizes overflow", i));
         }
-        if (sum != rows[i])
-            return bad(fail(NS_ERR_SPLIT_SUM, "tensor %d: split rows sum to %lld, not %lld", i,
-                            (long long)sum, (long long)rows[i]));
+        if (sum != extent[i])
+            return bad(fail(NS_ERR_SPLIT_SUM, "tensor %d: split sizes sum to %lld, not %lld (dim %d)", i,
+                            (long long)sum, (long long)extent[i], d));
     }
-    // Offsets: shard buffers hold the tensors' row pieces in index order; home
+    // Offsets: shard buffers hold the tensors' slices in index order; home
     // buffers hold the complete tensors homed there in index order.
     for (int32_t i = 0; i < n; ++i) {
-        const int64_t numel = rows[i] * cols[i];
+        const int64_t numel = outer[i] * extent[i] * inner[i];
         int64_t &ho = plan->home_elems[home[i]];
         plan->home_offset[i] = ho;
         if (__builtin_add_overflow(ho, numel, &ho))
             return bad(fail(NS_ERR_OVERFLOW, "home buffer size overflows"));
-        int64_t row0 = 0;
+        int64_t start = 0;
         for (int32_t s = 0; s < S; ++s) {
-            const int64_t r = split_rows[(int64_t)i * S + s];
+            const int64_t w = split[(int64_t)i * S + s];
             int64_t &so = plan->shard_elems[s];
             plan->shard_offset[(size_t)i * S + s] = so;
-            const int64_t piece = r * cols[i];  // <= numel, no overflow
+            const int64_t piece = outer[i] * w * inner[i];   // <= numel, no overflow
             if (__builtin_add_overflow(so, piece, &so))
                 return bad(fail(NS_ERR_OVERFLOW, "shard buffer size overflows"));
             if (piece > 0) {
@@ -228,11 +245,13 @@ extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int
                 g.shard = s;
                 g.home = home[i];
                 g.shard_off = plan->shard_offset[(size_t)i * S + s] * elem_bytes;
-                g.home_off = (plan->home_offset[i] + row0 * cols[i]) * elem_bytes;
+                g.home_off = (plan->home_offset[i] + start * inner[i]) * elem_bytes;
                 g.len = piece * elem_bytes;
+                g.run_len = w * inner[i] * elem_bytes;
+                g.home_stride = extent[i] * inner[i] * elem_bytes;
                 plan->segs.push_back(g);
             }
-            row0 += r;
+            start += w;
         }
     }
     for (int32_t s = 0; s < S; ++s) {
@@ -258,11 +277,24 @@ extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int
         h = fnv1a(h, &shapes[i].ndim, sizeof(int32_t));
         h = fnv1a(h, shapes[i].dims, sizeof(int64_t) * shapes[i].ndim);
         h = fnv1a(h, &home[i], sizeof(int32_t));
+        h = fnv1a(h, &plan->shard_dim[i], sizeof(int32_t));
     }
-    if (n > 0) h = fnv1a(h, split_rows, sizeof(int64_t) * (size_t)n * S);
+    if (n > 0) h = fnv1a(h, split, sizeof(int64_t) * (size_t)n * S);
     plan->fingerprint = h;
     *out = plan;
     return NS_OK;
+}
+
+extern "C" ns_status ns_route_plan_create(int32_t n, const ns_shape *shapes, int32_t num_shards,
+                                          const int64_t *split_rows, const int32_t *home,
+                                          int32_t elem_bytes, ns_route_plan **out) {
+    return route_plan_build(n, shapes, num_shards, split_rows, nullptr, home, elem_bytes, out);
+}
+
+extern "C" ns_status ns_route_plan_create_axis(int32_t n, const ns_shape *shapes, int32_t num_shards,
+                                               const int64_t *split_sizes, const int32_t *shard_dim,
+                                               const int32_t *home, int32_t elem_bytes, ns_route_plan **out) {
+    return route_plan_build(n, shapes, num_shards, split_sizes, shard_dim, home, elem_bytes, out);
 }
 
 extern "C" ns_status ns_route_plan_query(const ns_route_plan *plan, int64_t *shard_elems,

@@ -11,10 +11,15 @@
 // numbered globally; each workgroup takes a contiguous range of chunks and
 // copies each chunk with 16-byte loads and stores when both ends are 16-byte aligned
 // (narrower accesses otherwise); a full aligned chunk has all of each thread's
-// loads in flight before its stores. HBM-bound: every byte is read once and
-// written once. Plans that move more than the 256 MB last-level cache (MALL)
+// loads in flight before its stores. A piece cut along a dimension other than
+// the first (the TP stage's partition_dim in route_to_ns_home) is contiguous
+// in its shard buffer and a run of equal strided blocks in the home buffer;
+// its chunks map each 16-, 4- or 2-byte unit to its run. HBM-bound: every byte
+// is read once and written once. Plans that move more than the 256 MB last-level cache (MALL)
 // store with non-temporal hints; smaller ones keep their output cache-resident
 // for the kernel that reads it next.
+
+#include <type_traits>
 
 #include "hip_util.h"
 
@@ -74,6 +79,48 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
     }
 }
 
+// One chunk of a strided piece: shard bytes [off, off + len) of the piece
+// (contiguous at sp), whose byte p sits in the home at
+// hp + (p / run) * stride + p % run. Units of W bytes never straddle a run:
+// W divides run, stride, off and both bases.
+// IDX is the integer type of byte offsets inside the piece (32-bit when the
+// piece is under 4 GiB: its division is several times cheaper).
+template <int W, bool NT, typename IDX>
+__device__ inline void copy_chunk_strided(char *__restrict__ sp, char *__restrict__ hp, int64_t off, int64_t len,
+                                          int64_t run, int64_t stride, bool to_home) {
+    typedef typename std::conditional<W == 16, uint4, typename std::conditional<W == 4, uint32_t, uint16_t>::type>::type U;
+    constexpr int kPer = (int)(kRouteChunkBytes / W / kRouteThreads);
+    const int64_t nu = len / W;
+    const IDX run_i = (IDX)run;
+    U v[kPer];
+    int64_t hoff[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int64_t u = threadIdx.x + (int64_t)kRouteThreads * k;
+        if (u < nu) {
+            const int64_t p = off + u * W;
+            const IDX r = (IDX)p / run_i;
+            hoff[k] = (int64_t)r * stride + (int64_t)((IDX)p - r * run_i);
+            v[k] = to_home ? *reinterpret_cast<const U *>(sp + p) : *reinterpret_cast<const U *>(hp + hoff[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int64_t u = threadIdx.x + (int64_t)kRouteThreads * k;
+        if (u < nu) {
+            U *dst = reinterpret_cast<U *>(to_home ? hp + hoff[k] : sp + off + u * W);
+            if constexpr (NT && W == 16) {
+                __builtin_nontemporal_store(v[k].x, &dst->x);
+                __builtin_nontemporal_store(v[k].y, &dst->y);
+                __builtin_nontemporal_store(v[k].z, &dst->z);
+                __builtin_nontemporal_store(v[k].w, &dst->w);
+            } else {
+                *dst = v[k];
+            }
+        }
+    }
+}
+
 // to_home = 1: shard -> home (pack); 0: home -> shard (unpack).
 // Workgroup b copies the contiguous chunk range [b per, (b + 1) per): it finds
 // the piece holding its first chunk by binary search over the pieces' first
@@ -101,12 +148,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSe
         const int64_t off = (c - g.chunk_begin) * kRouteChunkBytes;
         const int64_t rem = g.len - off;
         const int64_t len = rem < kRouteChunkBytes ? rem : kRouteChunkBytes;
-        char *sp = shard.p[g.shard] + g.shard_off + off;
-        char *hp = home.p[g.home] + g.home_off + off;
-        if (to_home)
-            copy_chunk<NT>(sp, hp, len);
-        else
-            copy_chunk<NT>(hp, sp, len);
+        if (g.run_len == g.len) {   // one run: contiguous on both sides
+            char *sp = shard.p[g.shard] + g.shard_off + off;
+            char *hp = home.p[g.home] + g.home_off + off;
+            if (to_home)
+                copy_chunk<NT>(sp, hp, len);
+            else
+                copy_chunk<NT>(hp, sp, len);
+        } else {
+            char *sp = shard.p[g.shard] + g.shard_off;
+            char *hp = home.p[g.home] + g.home_off;
+            const uintptr_t mis = reinterpret_cast<uintptr_t>(sp) | reinterpret_cast<uintptr_t>(hp) |
+                                  (uintptr_t)g.run_len | (uintptr_t)g.home_stride;
+            if (g.len <= (int64_t)UINT32_MAX) {
+                if ((mis & 15) == 0)
+                    copy_chunk_strided<16, NT, uint32_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+                else if ((mis & 3) == 0)
+                    copy_chunk_strided<4, NT, uint32_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+                else
+                    copy_chunk_strided<2, NT, uint32_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+            } else {
+                if ((mis & 15) == 0)
+                    copy_chunk_strided<16, NT, int64_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+                else if ((mis & 3) == 0)
+                    copy_chunk_strided<4, NT, int64_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+                else
+                    copy_chunk_strided<2, NT, int64_t>(sp, hp, off, len, g.run_len, g.home_stride, to_home);
+            }
+        }
     }
 }
 

@@ -140,7 +140,7 @@ def params_by_home(num_params: int, home_of, size: int):
     return result
 
 
-def route_offsets(shapes, split_rows, home, num_shards: int):
+def route_offsets(shapes, split_rows, home, num_shards: int, shard_dim=None):
     """Offsets of every piece in the shard buffers and the home buffers.
 
     Shard buffer s holds, for every tensor in increasing index order, the rows
@@ -153,6 +153,11 @@ def route_offsets(shapes, split_rows, home, num_shards: int):
     split over shards in buffer order, so shard s holds rows starting at the
     sum of the rows held by the shards before it (``reconstruct_full``
     concatenates per-rank shards in buffer order).
+
+    With ``shard_dim`` (one dimension per tensor; layer_sharded_a2a page,
+    ``route_to_ns_home``'s axis-generic ``shard_dim``) the split sizes count
+    slices along that dimension instead of rows, and shard s's piece of tensor
+    i is that slice: numel / shape[d] * split elements.
 
     Returns dict with shard_offset[i][s], row_start[i][s], home_offset[i],
     shard_elems[s], home_elems[h] (all in elements).
@@ -170,14 +175,20 @@ def route_offsets(shapes, split_rows, home, num_shards: int):
     home_offset = [0] * n
     home_elems = [0] * num_shards
     for i in range(n):
-        rows, cols = views[i]
-        if sum(split_rows[i]) != rows:
-            raise ValueError(f"split rows of tensor {i} do not sum to {rows}")
+        d = 0 if shard_dim is None else shard_dim[i]
+        shape = tuple(int(x) for x in shapes[i])
+        extent = shape[d]
+        others = 1
+        for k, x in enumerate(shape):
+            if k != d:
+                others *= x
+        if sum(split_rows[i]) != extent:
+            raise ValueError(f"split sizes of tensor {i} do not sum to {extent}")
         r0 = 0
         for s in range(num_shards):
             shard_offset[i][s] = shard_elems[s]
             row_start[i][s] = r0
-            shard_elems[s] += split_rows[i][s] * cols
+            shard_elems[s] += split_rows[i][s] * others
             r0 += split_rows[i][s]
     groups = params_by_home(n, home, num_shards)
     for h in range(num_shards):

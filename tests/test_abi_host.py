@@ -283,3 +283,41 @@ def test_strided_errors():
     assert call(ctypes.addressof(huge), None) == -5
     assert call(ctypes.addressof(ok), ctypes.addressof(ok)) == -7   # valid; no workspace
     assert call(None, None) == -7
+
+
+@pytest.mark.parametrize("seed", range(15))
+def test_route_offsets_axis_random(seed):
+    rng = random.Random(300 + seed)
+    S = rng.randint(1, 6)
+    n = rng.randint(0, 20)
+    shapes, split, dims = [], [], []
+    for _ in range(n):
+        nd = rng.randint(2, 4)
+        s = tuple(rng.randint(0, 9) for _ in range(nd))
+        d = rng.randrange(nd)
+        cuts = sorted(rng.randint(0, s[d]) for _ in range(S - 1))
+        split.append([b - a for a, b in zip([0] + cuts, cuts + [s[d]])])
+        shapes.append(s)
+        dims.append(d)
+    home = [rng.randrange(S) for _ in range(n)]
+    elem = rng.choice([2, 4])
+    q = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis(shapes, S, split, dims, home, elem))
+    want = planner.route_offsets(shapes, split, home, S, shard_dim=dims)
+    for key in ("shard_elems", "home_elems", "home_offset", "shard_offset"):
+        assert q[key] == want[key], key
+
+
+def test_route_plan_axis_errors():
+    assert _status(nsq.ns_route_plan_create_axis, [(4, 6)], 2, [[3, 3]], [2], [0], 2) == "NS_ERR_INVALID_ARG"
+    assert _status(nsq.ns_route_plan_create_axis, [(4, 6)], 2, [[3, 2]], [1], [0], 2) == "NS_ERR_SPLIT_SUM"
+    # dim 0 through the axis entry point equals the row plan, fingerprint included
+    a = nsq.ns_route_plan_query(nsq.ns_route_plan_create([(4, 6)], 2, [[1, 3]], [1], 2))
+    b = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(4, 6)], 2, [[1, 3]], [0], [1], 2))
+    assert a == b
+    c = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(4, 6)], 2, [[3, 3]], [1], [1], 2))
+    assert c["fingerprint"] != a["fingerprint"]
+    # fused routing refuses a tensor split along dim 1 over several shards
+    plan = nsq.ns_route_plan_create_axis([(4, 6)], 2, [[3, 3]], [1], [0], 2)
+    assert _status(nsq.ns_routed_workspace_bytes, plan, nsq.NS_BF16) == "NS_ERR_PLAN_MISMATCH"
+    whole = nsq.ns_route_plan_create_axis([(4, 6)], 2, [[0, 6]], [1], [0], 2)
+    assert nsq.ns_routed_workspace_bytes(whole, nsq.NS_BF16)[0] > 0

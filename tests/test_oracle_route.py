@@ -100,3 +100,98 @@ def test_single_shard_is_identity_copy():
 def test_offsets_reject_bad_split():
     with pytest.raises(ValueError):
         planner.route_offsets([(4, 2)], [[1, 1]], [0], 2)
+
+
+def _random_axis_case(rng, S, n):
+    shapes, fulls, split, dims = [], [], [], []
+    for _ in range(n):
+        nd = int(rng.integers(2, 5))
+        shape = tuple(int(rng.integers(0, 6)) for _ in range(nd))
+        d = int(rng.integers(0, nd))
+        cuts = np.sort(rng.integers(0, shape[d] + 1, size=S - 1))
+        split.append(np.diff(np.concatenate([[0], cuts, [shape[d]]])).astype(int).tolist())
+        shapes.append(shape)
+        dims.append(d)
+        fulls.append(rng.integers(0, 65535, size=shape, dtype=np.uint16))
+    return shapes, fulls, split, dims
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_pack_axis_matches_split_construction_and_brute_force(seed):
+    rng = np.random.default_rng(900 + seed)
+    S = int(rng.integers(1, 5))
+    n = int(rng.integers(1, 7))
+    shapes, fulls, split, dims = _random_axis_case(rng, S, n)
+    home = [int(rng.integers(0, S)) for _ in range(n)]
+    # shards built with np.split along each tensor's axis
+    shards = [[] for _ in range(S)]
+    for f, sp, d in zip(fulls, split, dims):
+        for s, blk in enumerate(np.split(f, np.cumsum(sp)[:-1], axis=d)):
+            shards[s].append(blk.ravel())
+    shards = [np.concatenate(p) if p else np.zeros(0, np.uint16) for p in shards]
+    homes = route.pack_axis(shards, shapes, split, dims, home, S)
+    for h in range(S):
+        want = [fulls[i].ravel() for i in range(n) if home[i] == h]
+        assert np.array_equal(homes[h], np.concatenate(want) if want else np.zeros(0, np.uint16))
+    # brute force: walk every element of every shard slice with plain index arithmetic
+    cursor = [0] * S
+    hpos = {}
+    for h in range(S):
+        pos = 0
+        for i in range(n):
+            if home[i] == h:
+                hpos[i] = pos
+                pos += int(np.prod(shapes[i]))
+    for i in range(n):
+        shape, d = shapes[i], dims[i]
+        lo = 0
+        for s in range(S):
+            w = split[i][s]
+            sub = list(shape)
+            sub[d] = w
+            for flat_sub, idx in enumerate(np.ndindex(*sub)):
+                full_idx = list(idx)
+                full_idx[d] += lo
+                flat_full = int(np.ravel_multi_index(full_idx, shape))
+                assert homes[home[i]][hpos[i] + flat_full] == shards[s][cursor[s] + flat_sub]
+            cursor[s] += int(np.prod(sub))
+            lo += w
+    back = route.unpack_axis(homes, shapes, split, dims, home, S)
+    assert all(np.array_equal(a, b) for a, b in zip(back, shards))
+
+
+def test_pack_axis_dim0_equals_row_pack():
+    rng = np.random.default_rng(5)
+    S, n = 3, 5
+    shapes = [(int(rng.integers(1, 9)), int(rng.integers(1, 6))) for _ in range(n)]
+    split = []
+    for s in shapes:
+        cuts = np.sort(rng.integers(0, s[0] + 1, size=S - 1))
+        split.append(np.diff(np.concatenate([[0], cuts, [s[0]]])).astype(int).tolist())
+    fulls = [rng.integers(0, 65535, size=s, dtype=np.uint16) for s in shapes]
+    shards = _make_shards(fulls, split, S)
+    home = [2, 0, 0, 1, 2]
+    a = route.pack(shards, shapes, split, home, S)
+    b = route.pack_axis(shards, shapes, split, [0] * n, home, S)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_two_stage_rows_then_columns():
+    # layer_sharded_a2a page: one exchange over the GTP_remat group along dim 0,
+    # then one over the TP group along partition_dim. A tensor cut into an
+    # R x C grid of blocks (R row groups, C column groups) is rebuilt by packing
+    # the R row blocks of each column group (dim 0), then the C column blocks (dim 1).
+    rng = np.random.default_rng(11)
+    P, Q, R, C = 7, 9, 3, 2
+    full = rng.integers(0, 65535, size=(P, Q), dtype=np.uint16)
+    rsplit, csplit = [3, 0, 4], [5, 4]
+    rows = np.split(full, np.cumsum(rsplit)[:-1], axis=0)
+    # stage 1: within column group t, the R ranks hold (rows_r, cols_t) blocks
+    stage1 = []
+    for t, cb in enumerate(np.split(np.arange(Q), np.cumsum(csplit)[:-1])):
+        shards = [rows[r][:, cb].ravel() for r in range(R)]
+        homes = route.pack_axis(shards, [(P, len(cb))], [rsplit], [0], [0], R)
+        stage1.append(homes[0])
+    # stage 2: the C column blocks, now complete in rows, gathered along dim 1
+    homes = route.pack_axis(stage1, [(P, Q)], [csplit], [1], [1], C)
+    assert np.array_equal(homes[1].reshape(P, Q), full)
