@@ -286,6 +286,59 @@ def wave_bench(ms, slots: int, tokens: int, reps: int) -> dict:
             "waves": res["waves"], "data": "synthetic"}
 
 
+PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
+
+
+def gram_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
+    """Algorithmic flops of Gram-space NS on one matrix: the Gram m(m+1)n; step
+    0 (Q0 = I) one symmetric product G G; every later step four symmetric
+    m x m products (Q G, (Q G) Q, A A, B' Q), m^2(m+1) each (A A skipped when
+    c == 0); the output Q X0, 2 m^2 n."""
+    sym = m * m * (m + 1)
+    per_step = (4 if c_nonzero else 3) * sym
+    return float(m * (m + 1) * n + (sym if c_nonzero else 0) + max(0, steps - 1) * per_step + 2 * m * m * n)
+
+
+def gram_bench(ms, ridge: float, reps: int) -> dict:
+    """Gram-space NS (fp32) and the standard bf16 NS on the same matrices, one
+    call each over the whole set, inputs resident in HBM."""
+    import torch
+    import newton_schulz_quintic_amd as nsq
+    from workloads import device_matrix
+    mats = [device_matrix(ms.seed, i, s, std=ms.std) for i, s in enumerate(ms.shapes)]
+    outs = [torch.empty_like(m) for m in mats]
+    ws = torch.empty(max(nsq.ns_gram_workspace_bytes(ms.shapes, nsq.NS_BF16)[0],
+                         nsq.ns_workspace_bytes(ms.shapes, nsq.NS_BF16)[0]), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            times.append(s.elapsed_time(e))
+        return sorted(times)[len(times) // 2]
+
+    t_gram = timed(lambda: nsq.ns_orthogonalize_gram(mats, outs, steps=ms.steps, coeffs=ms.coeffs, ridge=ridge,
+                                                     workspace=ws))
+    t_std = timed(lambda: nsq.ns_orthogonalize_batched(mats, outs, steps=ms.steps, coeffs=ms.coeffs, workspace=ws))
+    flops = sum(gram_flops(*oriented(s), ms.steps, ms.coeffs[2] != 0.0) for s in ms.shapes)
+    tf = flops / (t_gram * 1e-3) / 1e12
+    return {"metric": "Gram-space NS matrices/s (fp32 products), beside the bf16 NS on the same set",
+            "value": round(ms.n / (t_gram * 1e-3), 3), "unit": "matrices/s", "ms_per_call": round(t_gram, 3),
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": ms.name, "matrices": ms.n, "ns_steps": ms.steps, "ridge": ridge, "reps": reps},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_F32_TFLOPS, 4), "traffic": None,
+                         "note": "whole call: algorithmic flops / call time"},
+            "alg_flops_per_call": flops,
+            "standard_bf16_ns": {"ms_per_call": round(t_std, 3), "value": round(ms.n / (t_std * 1e-3), 3)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +353,9 @@ def main():
     ap.add_argument("--waves", type=int, metavar="SLOTS",
                     help="measure wave dispatch (tensors per wave = SLOTS) against one NS call after a "
                          "simulated backward; prints its own JSON line and exits")
+    ap.add_argument("--gram", type=float, metavar="RIDGE",
+                    help="time Gram-space NS (fp32, this trace ridge) beside the bf16 NS on the workload's "
+                         "matrices; prints its own JSON line and exits")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens of the simulated backward (--waves)")
     ap.add_argument("--shard-dim", type=int, default=0,
                     help="cut every tensor's shards along this dimension (0 = rows; 1 = the TP stage's "
@@ -341,6 +397,9 @@ def main():
         ms.name += f"-shard-dim{args.shard_dim}"
     if args.waves:
         print(json.dumps(wave_bench(ms, args.waves, args.tokens, max(1, args.steps))), flush=True)
+        return
+    if args.gram is not None:
+        print(json.dumps(gram_bench(ms, args.gram, max(1, args.steps))), flush=True)
         return
     S = ms.num_shards
     big = args.workload != "routed-square"

@@ -246,6 +246,34 @@ ns_status ns_orthogonalize_strided(int32_t n, const ns_shape *shapes, const void
                                    void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * Gram-space Newton-Schulz [issue, "Secondary (parked)": gram_once, the exact
+ * Gram-space reformulation hardened with an fp32 Gram and a trace ridge]
+ * ------------------------------------------------------------------------ */
+
+/* Workspace for ns_orthogonalize_gram (fp32 X0, X0^T and six m x m arrays
+ * per tensor), as for ns_workspace_bytes. Errors: INVALID_ARG, DTYPE, OVERFLOW. */
+ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype, size_t *bytes,
+                                  size_t *min_bytes);
+
+/* The same iteration as ns_orthogonalize_batched, evaluated in the m x m Gram
+ * space, all in fp32 (f32 MFMA; bf16 inputs are widened exactly): with X0 the
+ * normalised, wide-oriented input, G = X0 X0^T + ridge (tr(G) / m) I is formed
+ * once; then Q_0 = I and, per step, A = Q G Q^T, Q = a Q + (b A + c A A) Q,
+ * evaluated as Q' = (a I + b A + c A A) Q; the output is Q_k X0 in the input's
+ * shape and dtype. ridge = 0 is exactly the NS iteration (in exact
+ * arithmetic); ridge > 0 regularises a near-singular Gram and changes the
+ * result. In this plain form every Q_k is a polynomial in G, so the m x m
+ * products are symmetric and computed as upper tiles. The products are m^3
+ * per step instead of m^2 n: cheaper when n >> m, but in fp32 (157 TFLOP/s
+ * dense on MI355X, against 2.5 PFLOP/s bf16).
+ * ridge: finite, >= 0. Other arguments and errors as for
+ * ns_orthogonalize_batched (workspace from ns_gram_workspace_bytes). */
+ns_status ns_orthogonalize_gram(int32_t n, const ns_shape *shapes, const void *const *in, void *const *out,
+                                ns_dtype dtype, int32_t steps, float a, float b, float c, float eps,
+                                float ridge, const int32_t *order, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* ------------------------------------------------------------------------ *
  * Fused routing: Newton-Schulz straight from and back to the shard buffers
  * [layer_sharded, route_to_ns_home / route_from_ns_home around the
  *  orthogonalisation; owner_planning, OwnerGatherPlan.reconstruct_full and

@@ -17,7 +17,9 @@ from ._lib import (  # noqa: F401
     RoutePlan,
     lib,
     ns_last_error,
+    ns_gram_workspace_bytes,
     ns_orthogonalize_batched,
+    ns_orthogonalize_gram,
     ns_orthogonalize_routed,
     ns_orthogonalize_strided,
     ns_orthogonalize_waves,

@@ -27,7 +27,7 @@ EXPORTS = [
     "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
     "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_orthogonalize_strided", "ns_routed_workspace_bytes",
-    "ns_orthogonalize_routed", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
+    "ns_orthogonalize_routed", "ns_gram_workspace_bytes", "ns_orthogonalize_gram", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
     "ns_timing_read",
 ]
 
@@ -67,6 +67,9 @@ _SIGS = {
                                         _P, _SZ, _P]),
     "ns_routed_workspace_bytes": (_I32, [_P, _I32, _P, _P]),
     "ns_orthogonalize_routed": (_I32, [_P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P, _SZ, _P]),
+    "ns_gram_workspace_bytes": (_I32, [_I32, _P, _I32, _P, _P]),
+    "ns_orthogonalize_gram": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _F32, _P, _P, _SZ,
+                                     _P]),
     "ns_wave_plan": (_I32, [_I32, _P, _P, _I32, _P, _P]),
     "ns_orthogonalize_waves": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _I32, _P,
                                       _P, _SZ, _P]),
@@ -377,6 +380,44 @@ def ns_orthogonalize_routed(plan: RoutePlan, shard_in, shard_out, dtype: int, st
                                          float(b), float(c), float(eps),
                                          None if ord_arr is None else _addr(ord_arr),
                                          workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ns_gram_workspace_bytes(shapes, dtype: int) -> tuple[int, int]:
+    sh = _shapes(shapes)
+    b, mb = _SZ(0), _SZ(0)
+    _check(lib().ns_gram_workspace_bytes(len(shapes), _addr(sh), dtype, ctypes.addressof(b), ctypes.addressof(mb)))
+    return b.value, mb.value
+
+
+def ns_orthogonalize_gram(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
+                          ridge: float = 0.0, order=None, workspace=None, stream=None):
+    """Gram-space Newton-Schulz in fp32 on every tensor of ``inputs`` (see ns.h)."""
+    n = len(inputs)
+    if len(outputs) != n:
+        raise ValueError("inputs and outputs differ in length")
+    if n == 0:
+        return workspace
+    dtype = _dtype_code(inputs[0])
+    for x, y in zip(inputs, outputs):
+        if _dtype_code(x) != dtype or _dtype_code(y) != dtype:
+            raise TypeError("all tensors must share one dtype")
+        if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+            raise ValueError("tensors must be contiguous and outputs shaped like inputs")
+    shapes = [tuple(x.shape) for x in inputs]
+    if workspace is None:
+        import torch
+        need, _ = ns_gram_workspace_bytes(shapes, dtype)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+    a, b, c = coeffs
+    sh = _shapes(shapes)
+    ins = _arr(_P, [x.data_ptr() for x in inputs])
+    outs = _arr(_P, [y.data_ptr() for y in outputs])
+    ord_arr = None if order is None else _arr(_I32, order)
+    _check(lib().ns_orthogonalize_gram(n, _addr(sh), _addr(ins), _addr(outs), dtype, steps, float(a), float(b),
+                                       float(c), float(eps), float(ridge),
+                                       None if ord_arr is None else _addr(ord_arr), workspace.data_ptr(),
+                                       workspace.numel(), _stream(stream)))
     return workspace
 
 

@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "hip_util.h"
@@ -71,6 +72,7 @@ struct NsProb {
     char *xt0, *xt1;   // X^T ping/pong: np x mp (row stride ldxt)
     char *a;           // A: mp x mp (row stride ldt)
     char *b;           // B: mp x mp (row stride ldt)
+    char *g, *q0, *q1, *t;   // Gram-space only: G, Q ping/pong, Q G; mp x mp fp32 (row stride ldt)
     float *partials;   // nparts fp32 sums of squares, one per staging tile
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
@@ -161,7 +163,24 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-enum Mode { kSyrkX = 0, kSyrkA = 1, kGemmBX = 2 };
+// Product launches. NS: kSyrkX, kSyrkA, kGemmBX. Gram-space NS ("[GTP][Muon]
+// Optimize Muon step performance", "Secondary (parked)", gram_once): the
+// iterate is X_k = Q_k X0 with the m x m Gram G = X0 X0^T computed once, so a
+// step is A = Q G Q^T, Q' = (a I + b A + c A A) Q on m x m matrices, and the
+// result is Q_k X0. Q_k is a polynomial in G, hence symmetric and commuting
+// with G, so Q G, (Q G) Q and B' Q are symmetric and computed as upper tiles.
+enum Mode {
+    kSyrkX = 0,    // A = s_final X X^T
+    kSyrkA = 1,    // B' = s_final (s_init A + A A) + s_diag I
+    kGemmBX = 2,   // X' = B' X
+    kGramG = 3,    // G = s^2 X0 X0^T + ridge (tr G / m) I
+    kGramB0 = 4,   // Q1 = s_final (s_init G + G G) + s_diag I   (step 0: Q0 = I)
+    kGramQG = 5,   // T = Q G
+    kGramTQ = 6,   // A = T Q
+    kGramBQ = 7,   // Q' = B' Q
+    kGramOut = 8,  // out = s Q X0 (last launch, the caller's output)
+};
+constexpr bool symmetric_mode(int mode) { return mode != kGemmBX && mode != kGramOut; }
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
 // (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
@@ -551,7 +570,8 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
 // binary tree. Independent of the workgroup size (>= kScaleSlots threads), so
 // every kernel that needs it gets the same bits. `red` is kScaleSlots floats of
 // LDS; ends with a barrier.
-__device__ __forceinline__ float norm_scale(const float *partials, int nparts, float eps, float *red) {
+__device__ __forceinline__ float norm_scale(const float *partials, int nparts, float eps, float *red,
+                                            float *total_out = nullptr) {
     const int t = threadIdx.x;
     if (t < kScaleSlots) {
         float v = 0.f;
@@ -566,6 +586,7 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
     }
     const float total = red[0];
     __syncthreads();
+    if (total_out) *total_out = total;
     return 1.0f / (sqrtf(total) + eps);
 }
 
@@ -586,12 +607,13 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
 // A0 = s^2 (G G^T), and B0' is stored scaled by s, so X1 = (s B0') G.
 // LAST (kGemmBX only): the final step writes B' X straight to the caller's
 // output in the input's orientation instead of into the workspace.
-template <typename T, class C, int MODE, bool LAST>
+template <typename T, class C, int MODE, bool LAST, typename TO = T>
 __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
     const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
     float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
     const RowPiece *__restrict__ pieces) {
-    static_assert(!LAST || MODE == kGemmBX, "only the B X step writes the output");
+    static_assert(!LAST || MODE == kGemmBX || MODE == kGramOut, "only B X or the Gram-space output writes out");
+    static_assert(MODE != kGramOut || LAST, "the Gram-space output launch is a last launch");
     constexpr int BM = C::BM, ES = sizeof(T);
     constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -606,43 +628,63 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     char *xn = cur ? pr.x0 : pr.x1;
     char *xtc = cur ? pr.xt1 : pr.xt0;
     char *xtn = cur ? pr.xt0 : pr.xt1;
+    char *qc = cur ? pr.q1 : pr.q0;
+    char *qn = cur ? pr.q0 : pr.q1;
     char *A = pr.a, *B = pr.b;
     if (first) {
-        const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds));
+        float total;
+        const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds), &total);
         if constexpr (MODE == kSyrkX) s_final = sc * sc;
         else if constexpr (MODE == kSyrkA) {
             s_final *= sc;
             s_diag *= sc;
+        } else if constexpr (MODE == kGramG) {
+            s_final = sc * sc;
+            s_diag *= sc * sc * total / (float)pr.m;   // ridge * tr(G) / m, tr(G) = s^2 ||input||^2
+        } else if constexpr (MODE == kGramOut) {
+            s_final = sc;
         }
     }
 
     f32x16 acc[C::NBM][C::NBN];
-    if constexpr (MODE == kSyrkX) {
+    if constexpr (MODE == kSyrkX || MODE == kGramG) {
         zero_acc<C>(acc);
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                            np * ES / C::ROWB, lds, acc);
-    } else if constexpr (MODE == kSyrkA) {
+    } else if constexpr (MODE == kSyrkA || MODE == kGramB0) {
         const int ld = ldt * ES;
+        char *S = MODE == kSyrkA ? A : pr.g;
         if (do_product) {
-            // the old tile A[row0.., col0..] passes through the P stages of
-            // columns col0 .. col0 + BM: seed s_init A from there
+            // the old tile S[row0.., col0..] passes through the P stages of
+            // columns col0 .. col0 + BM: seed s_init S from there
             zero_acc<C>(acc);
-            tile_product<T, C, true>(A + (int64_t)row0 * ld, A + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+            tile_product<T, C, true>(S + (int64_t)row0 * ld, S + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                                      mp * ES / C::ROWB, lds, acc, col0 * ES / C::ROWB, s_init);
         } else {
-            init_acc<T, C>(A, ld, row0, col0, s_init, lds, acc);
+            init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
         }
-    } else {
+    } else if constexpr (MODE == kGemmBX) {
         zero_acc<C>(acc);
         const int ldb = ldt * ES, ldq = ldxt * ES;
         tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
+                           mp * ES / C::ROWB, lds, acc);
+    } else {   // Gram-space products, all with K = mp
+        char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
+        char *Q = MODE == kGramQG ? pr.g : MODE == kGramOut ? pr.xt0 : qc;
+        const int ldp = ldt * ES, ldq = (MODE == kGramOut ? ldxt : ldt) * ES;
+        zero_acc<C>(acc);
+        tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
                            mp * ES / C::ROWB, lds, acc);
     }
 
     // Epilogue, part 1: scaling, rounding, staging. Accumulator element
     // (i, j, v) of this lane sits at tile row wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32)
-    // + v%4 and tile column wn*BM/WN + 32 j + lane%32.
+    // + v%4 and tile column wn*BM/WN + 32 j + lane%32. The tile is staged in
+    // the type it is stored in: the workspace type, or the output's.
+    typedef typename std::conditional<LAST, TO, T>::type TS;
+    constexpr int SES = sizeof(TS);
+    constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     __syncthreads();   // every wave is done reading operand panels
@@ -658,21 +700,22 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : s_final * acc[i][j][4 * q + e];
-                    if constexpr (MODE == kSyrkA)
+                    if constexpr (kDiag)
                         if (tr.ti == tr.tj && r + e == c && row0 + r + e < pr.m) v[e] += s_diag;
                 }
-                stage4<T, BM>(lds, r, c, v);
+                stage4<TS, BM>(lds, r, c, v);
             }
         }
     }
     __syncthreads();
 
     // Epilogue, part 2: write the staged tile.
-    constexpr int NU = BM * ES / 16;                 // 16-byte units per staged column
+    constexpr int NU = BM * SES / 16;                // 16-byte units per staged column
     constexpr int COL_CHUNKS = BM * NU;
     if constexpr (!LAST) {
-        // row-major: the tile itself (A, B or X'), at (row0, col0)
-        char *D = MODE == kSyrkX ? A : MODE == kSyrkA ? B : xn;
+        // row-major: the tile itself, at (row0, col0)
+        char *D = MODE == kSyrkX ? A : MODE == kSyrkA ? B : MODE == kGemmBX ? xn : MODE == kGramG ? pr.g
+                : MODE == kGramQG ? pr.t : MODE == kGramTQ ? A : qn;   // kGramB0, kGramBQ: the next Q
         const int ldd = MODE == kGemmBX ? ldx : ldt;
         for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
             int r, c;
@@ -680,7 +723,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
             store16<T>(D, (int64_t)(row0 + r) * ldd + col0 + c, w);
         }
         // column-major: the mirror tile at (col0, row0), or X'^T
-        if (MODE == kGemmBX || tr.ti != tr.tj) {
+        if (!symmetric_mode(MODE) || tr.ti != tr.tj) {
             char *E = MODE == kGemmBX ? xtn : D;
             const int lde = MODE == kGemmBX ? ldxt : ldt;
             for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
@@ -693,16 +736,16 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         const int m = pr.m, n = pr.n;
         const RowPiece *band = pieces + tr.piece;
         if (!pr.tall) {   // out is m x n: row-major chunks
-            for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
+            for (int blk = wave; blk < RowChunks<TS, BM>::BLOCKS; blk += C::WAVES) {
                 int r, c;
-                const i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
-                store_chunk_checked<T>(pr, band, tr.npiece, m, n, row0 + r, col0 + c, w);
+                const i32x4 w = row_chunk<TS, BM>(lds, blk, lane, r, c);
+                store_chunk_checked<TS>(pr, band, tr.npiece, m, n, row0 + r, col0 + c, w);
             }
         } else {          // out is n x m: column-major chunks
             for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
                 int c, r;
-                const i32x4 w = col_chunk<T, BM>(lds, idx, c, r);
-                store_chunk_checked<T>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
+                const i32x4 w = col_chunk<TS, BM>(lds, idx, c, r);
+                store_chunk_checked<TS>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
             }
         }
     }
@@ -721,16 +764,20 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 // This is the first kernel of a call: its descriptor and tile list are read
 // from the pinned host staging buffer, and the workgroups also copy the whole
 // table block (table_units 16-byte units) from there into the workspace for
-// the kernels that follow.
-template <typename T>
+// the kernels that follow. TI is the input's element type, T the workspace's
+// (fp32 workspaces of bf16 inputs hold the exact values; the sums of squares
+// come out bit-identical to the bf16 workspace's).
+template <typename TI, typename T = TI>
 __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles, int32_t count,
                                                                  const i32x4 *__restrict__ table_src,
                                                                  i32x4 *__restrict__ table_dst,
                                                                  int32_t table_units,
                                                                  const RowPiece *__restrict__ pieces) {
-    constexpr int ES = sizeof(T), E = 16 / ES, TE = kPrepTile;
-    constexpr int RB = TE * ES, CPR = TE / E;           // staged row bytes, 16-byte chunks per row
+    constexpr int ES = sizeof(T), EI = sizeof(TI), E = 16 / EI, TE = kPrepTile;
+    constexpr int RB = TE * ES, CPR = TE / E;           // staged row bytes, 16-byte input loads per row
+    constexpr int UPL = E * ES / 16;                    // 16-byte workspace units per input load
+    static_assert(ES >= EI && UPL >= 1, "the workspace type is at least as wide as the input's");
     __shared__ __attribute__((aligned(16))) char lds[TE * RB];
     __shared__ float red[kPrepThreads];
     __shared__ RowPiece band[kPrepTile];   // the pieces holding the tile's input rows
@@ -767,25 +814,39 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         if (gr < rows) {
             RowPiece pc = one;   // by value: the reads below stay global loads
             if (multi) pc = find_piece(band, tr.npiece, gr);
-            const char *src = pc.in + ((gr - pc.row0) * pc.ld_in + gc) * ES;
+            const char *src = pc.in + ((gr - pc.row0) * pc.ld_in + gc) * EI;
             if (vec_in && gc + E <= cols) {
                 w = *(const NSQ_GLOBAL i32x4 *)src;
             } else {
-                T vals[E];
+                TI vals[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) vals[e] = gc + e < cols ? gp<T>(src)[e] : T(0);
+                for (int e = 0; e < E; ++e) vals[e] = gc + e < cols ? gp<TI>(src)[e] : TI(0);
                 __builtin_memcpy(&w, vals, 16);
             }
         }
-        T vals[E];
+        TI vals[E];
         __builtin_memcpy(vals, &w, 16);
+        float fv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float v = to_f32<T>(vals[e]);
-            ss += v * v;
+            fv[e] = to_f32<TI>(vals[e]);
+            ss += fv[e] * fv[e];
         }
-        store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
-        *reinterpret_cast<i32x4 *>(lds + r * RB + ((u ^ (2 * (r & 3))) << 4)) = w;
+        if constexpr (UPL == 1) {
+            store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
+            *reinterpret_cast<i32x4 *>(lds + r * RB + ((u ^ (2 * (r & 3))) << 4)) = w;
+        } else {   // exact widening to the workspace type, 16 bytes at a time
+#pragma unroll
+            for (int h = 0; h < UPL; ++h) {
+                T wv[16 / ES];
+#pragma unroll
+                for (int e = 0; e < 16 / ES; ++e) wv[e] = (T)fv[h * (16 / ES) + e];
+                i32x4 o;
+                __builtin_memcpy(&o, wv, 16);
+                store16<T>(direct, (int64_t)gr * ld_direct + gc + h * (16 / ES), o);
+                *reinterpret_cast<i32x4 *>(lds + r * RB + (((u * UPL + h) ^ (2 * (r & 3))) << 4)) = o;
+            }
+        }
     }
     // fixed-order block sum of the squares
     red[threadIdx.x] = ss;
@@ -797,16 +858,17 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
     }
     if (threadIdx.x == 0) pr.partials[tr.ti * (pr.np / TE) + tr.tj] = red[0];
 
-    // transpose: output row c (tile column), 16 bytes = E consecutive tile rows
+    // transpose: output row c (tile column), 16 bytes = ET consecutive tile rows
+    constexpr int ET = 16 / ES;
     auto at = [&](int r, int c) -> const char * {
         const int byte = c * ES;
         return lds + r * RB + (((byte >> 4) ^ (2 * (r & 3))) << 4) + (byte & 15);
     };
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 15, g = lane >> 4;
-    constexpr int BR = 4 * E;                          // tile rows per block (4 lane groups x E)
+    constexpr int BR = 4 * ET;                         // tile rows per block (4 lane groups x ET)
     constexpr int BLOCKS = (TE / 16) * (TE / BR);
     for (int blk = wave; blk < BLOCKS; blk += kPrepThreads / 64) {
-        const int cb = (blk % (TE / 16)) * 16, rb = (blk / (TE / 16)) * BR + E * g;
+        const int cb = (blk % (TE / 16)) * 16, rb = (blk / (TE / 16)) * BR + ET * g;
         const int c = cb + t;
         i32x4 w;
         if constexpr (ES == 2) {
@@ -878,11 +940,14 @@ inline size_t x_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(
 inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.np * ld_t(mi, es) * es)); }
 inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
 
-ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info) {
+// gram: the Gram-space workspace (fp32 X0, X0^T, G, Q ping/pong, Q G, A, B)
+// instead of the NS one (X and X^T ping/pong, A, B in the input's type).
+ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info,
+                   bool gram = false) {
     if (n < 0) return fail(NS_ERR_INVALID_ARG, "n = %d < 0", n);
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
     if (dtype != NS_BF16 && dtype != NS_F32) return fail(NS_ERR_DTYPE, "dtype %d", (int)dtype);
-    const int64_t es = dtype == NS_BF16 ? 2 : 4;
+    const int64_t es = gram ? 4 : dtype == NS_BF16 ? 2 : 4;   // workspace element size
     info.assign(n, MatInfo{});
     for (int32_t i = 0; i < n; ++i) {
         MatInfo &mi = info[i];
@@ -907,7 +972,8 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.gemm_tiles = tm * tn;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.npieces = 1;
-        mi.buf_bytes = 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
+        mi.buf_bytes = gram ? x_bytes(mi, es) + xt_bytes(mi, es) + 6 * a_bytes(mi, es)
+                            : 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
 }
@@ -1019,12 +1085,23 @@ void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRe
                            tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
 }
 
-template <typename T>
+template <typename T, class C, int MODE, bool LAST = false, typename TO = T>
+void launch_mode(int32_t nt, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t cur, float s_init,
+                 float s_final, float s_diag, int32_t do_product, int32_t first, float eps, const RowPiece *pieces) {
+    hipLaunchKernelGGL((ns_product_kernel<T, C, MODE, LAST, TO>), dim3((unsigned)nt), dim3(C::THREADS), 0, st, probs,
+                       tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+}
+
+// One group of matrices: tables, input staging, then the product launches.
+// TI is the input's type, T the workspace's. gram: the Gram-space iteration
+// in fp32 (T = float) with the trace ridge `ridge`; else NS in TI.
+template <typename TI, typename T>
 ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo> &info,
                     const PieceLists &pieces, int32_t steps, float a, float b,
-                    float c, float eps, char *ws, const TableSizes &tsz, hipStream_t st) {
-    const int64_t es = sizeof(T);
-    const int bm = pick_tile(group, info, es);
+                    float c, float eps, bool gram, float ridge, char *ws, const TableSizes &tsz, hipStream_t st) {
+    static_assert(sizeof(T) >= sizeof(TI), "workspace type");
+    const int64_t es = sizeof(T), esi = sizeof(TI);
+    const int bm = gram ? 128 : pick_tile(group, info, es);
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, ptiles;
     std::vector<RowPiece> gpieces;
@@ -1036,19 +1113,30 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         const MatInfo &mi = info[idx];
         NsProb p{};
         const size_t xb = x_bytes(mi, es), xtb = xt_bytes(mi, es), ab = a_bytes(mi, es);
-        p.x0 = base;
-        p.x1 = p.x0 + xb;
-        p.xt0 = p.x1 + xb;
-        p.xt1 = p.xt0 + xtb;
-        p.a = p.xt1 + xtb;
-        p.b = p.a + ab;
+        if (!gram) {
+            p.x0 = base;
+            p.x1 = p.x0 + xb;
+            p.xt0 = p.x1 + xb;
+            p.xt1 = p.xt0 + xtb;
+            p.a = p.xt1 + xtb;
+            p.b = p.a + ab;
+        } else {   // X0, X0^T, G, Q ping/pong, Q G, A, B'
+            p.x0 = base;
+            p.xt0 = p.x0 + xb;
+            p.g = p.xt0 + xtb;
+            p.q0 = p.g + ab;
+            p.q1 = p.q0 + ab;
+            p.t = p.q1 + ab;
+            p.a = p.t + ab;
+            p.b = p.a + ab;
+        }
         base += mi.buf_bytes;
         const std::vector<RowPiece> &pc = pieces[idx];
         const int32_t pbase = (int32_t)gpieces.size();
         bool vin = true, vout = true;   // 16-byte accesses: aligned bases and row strides
         for (const RowPiece &q : pc) {
-            vin = vin && reinterpret_cast<uintptr_t>(q.in) % 16 == 0 && q.ld_in * es % 16 == 0;
-            vout = vout && reinterpret_cast<uintptr_t>(q.out) % 16 == 0 && q.ld_out * es % 16 == 0;
+            vin = vin && reinterpret_cast<uintptr_t>(q.in) % 16 == 0 && q.ld_in * esi % 16 == 0;
+            vout = vout && reinterpret_cast<uintptr_t>(q.out) % 16 == 0 && q.ld_out * esi % 16 == 0;
             gpieces.push_back(q);
         }
         p.vec_in = vin;
@@ -1087,10 +1175,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                 set_band(ptiles.back(), kPrepTile);
             }
         const double m = (double)mi.m, n = (double)mi.n;
-        f_syrk_x += m * (m + 1) * n;
-        f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;
-        f_gemm += 2 * m * m * n;
-        norm_bytes += m * n * es + 2.0 * (double)mi.mp * (double)mi.np * es;
+        f_syrk_x += m * (m + 1) * n;                                            // X X^T, or G
+        f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
+        f_gemm += 2 * m * m * n;                                                // B X, or Q X0
+        norm_bytes += m * n * esi + 2.0 * (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
 
@@ -1121,7 +1209,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
 
     {
         TimedScope ts(kTimeNorm, st, norm_bytes);
-        hipLaunchKernelGGL(ns_prepare_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st,
+        hipLaunchKernelGGL((ns_prepare_kernel<TI, T>), dim3((unsigned)npt), dim3(kPrepThreads), 0, st,
                            reinterpret_cast<const NsProb *>(hdev),
                            reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
                            reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
@@ -1130,10 +1218,59 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         if ((sst = staging_release(slot, st, le == hipSuccess))) return sst;
         if (le != hipSuccess) return fail(NS_ERR_HIP, "launch failed: %s", hipGetErrorString(le));
         if (steps == 0)
-            hipLaunchKernelGGL(ns_scale_out_kernel<T>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
+            hipLaunchKernelGGL(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
                                d_ptiles, npt, eps, d_pieces);
     }
     NSQ_HIP(hipGetLastError());
+    if (gram) {
+        if constexpr (sizeof(T) == 4) {
+            if (steps > 0) {
+                const float ratio = c != 0.f ? b / c : 0.f;
+                const bool fused = c != 0.f && std::isfinite(ratio);
+                const float si = fused ? ratio : b, sf = fused ? c : 1.f;
+                const int32_t prod = fused ? 1 : 0;
+                const int32_t nsy = (int32_t)syrk.size(), nge = (int32_t)gemm.size();
+                {
+                    TimedScope ts(kTimeSyrkX, st, f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
+                    launch_mode<T, Small, kGramG>(nsy, st, d_probs, d_syrk, 0, 1.f, 1.f, ridge, 1, 1, eps, d_pieces);
+                }
+                {
+                    TimedScope ts(kTimeSyrkA, st, f_syrk_a);   // Q1 = a I + b G + c G G
+                    launch_mode<T, Small, kGramB0>(nsy, st, d_probs, d_syrk, 0, si, sf, a, prod, 0, eps, d_pieces);
+                }
+                NSQ_HIP(hipGetLastError());
+                int qcur = 1;
+                for (int32_t k = 1; k < steps; ++k) {
+                    {
+                        TimedScope ts(kTimeProduct, st, 2 * f_syrk_a);   // T = Q G, A = T Q
+                        launch_mode<T, Small, kGramQG>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
+                                                       d_pieces);
+                        launch_mode<T, Small, kGramTQ>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
+                                                       d_pieces);
+                    }
+                    {
+                        TimedScope ts(kTimeSyrkA, st, f_syrk_a);   // B' = a I + b A + c A A
+                        launch_mode<T, Small, kSyrkA>(nsy, st, d_probs, d_syrk, qcur, si, sf, a, prod, 0, eps,
+                                                      d_pieces);
+                    }
+                    {
+                        TimedScope ts(kTimeProduct, st, f_syrk_a);   // Q' = B' Q
+                        launch_mode<T, Small, kGramBQ>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
+                                                       d_pieces);
+                    }
+                    NSQ_HIP(hipGetLastError());
+                    qcur ^= 1;
+                }
+                {
+                    TimedScope ts(kTimeFinal, st, f_gemm);   // out = s Q X0
+                    launch_mode<T, Small, kGramOut, true, TI>(nge, st, d_probs, d_gemm, qcur, 1.f, 1.f, 0.f, 1, 1,
+                                                              eps, d_pieces);
+                }
+                NSQ_HIP(hipGetLastError());
+            }
+        }
+        return NS_OK;
+    }
     int cur = 0;
     const double work[3] = {f_syrk_x, f_syrk_a, f_gemm};
     // B' = a I + b A + c A A as c (b / c A + A A) + a I: the accumulators of the
@@ -1172,11 +1309,13 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     return NS_OK;
 }
 
-// The common path of both entry points: every active tensor's input and output
-// rows are given as row pieces.
+// The common path of the entry points: every active tensor's input and output
+// rows are given as row pieces. gram: Gram-space iteration (info described
+// with the Gram workspace).
 ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype,
                         int32_t steps, float a, float b, float c, float eps, const int32_t *order,
-                        void *workspace, size_t workspace_bytes, hipStream_t hs) {
+                        void *workspace, size_t workspace_bytes, hipStream_t hs, bool gram = false,
+                        float ridge = 0.f) {
     const int32_t n = (int32_t)info.size();
     // Dispatch order: caller's permutation, else descending cost (ties by index).
     std::vector<int32_t> ord(n);
@@ -1211,11 +1350,18 @@ ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &piec
     size_t used = 0;
     auto flush = [&]() -> ns_status {
         if (group.empty()) return NS_OK;
-        ns_status r = dtype == NS_BF16
-                          ? run_group<__bf16>(group, info, pieces, steps, a, b, c, eps,
-                                              static_cast<char *>(workspace), tsz, hs)
-                          : run_group<float>(group, info, pieces, steps, a, b, c, eps,
-                                             static_cast<char *>(workspace), tsz, hs);
+        char *ws = static_cast<char *>(workspace);
+        ns_status r;
+        if (gram)
+            r = dtype == NS_BF16 ? run_group<__bf16, float>(group, info, pieces, steps, a, b, c, eps, true, ridge, ws,
+                                                            tsz, hs)
+                                 : run_group<float, float>(group, info, pieces, steps, a, b, c, eps, true, ridge, ws,
+                                                           tsz, hs);
+        else
+            r = dtype == NS_BF16 ? run_group<__bf16, __bf16>(group, info, pieces, steps, a, b, c, eps, false, 0.f,
+                                                             ws, tsz, hs)
+                                 : run_group<float, float>(group, info, pieces, steps, a, b, c, eps, false, 0.f, ws,
+                                                           tsz, hs);
         group.clear();
         used = 0;
         return r;
@@ -1418,4 +1564,39 @@ extern "C" ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, c
             return st;
     }
     return NS_OK;
+}
+
+extern "C" ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype, size_t *bytes,
+                                             size_t *min_bytes) {
+    if (!bytes) return fail(NS_ERR_INVALID_ARG, "bytes is NULL");
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info, true);
+    if (st) return st;
+    workspace_need(info, bytes, min_bytes);
+    return NS_OK;
+}
+
+extern "C" ns_status ns_orthogonalize_gram(int32_t n, const ns_shape *shapes, const void *const *in,
+                                           void *const *out, ns_dtype dtype, int32_t steps, float a, float b,
+                                           float c, float eps, float ridge, const int32_t *order, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    std::vector<MatInfo> info;
+    ns_status st = describe(n, shapes, dtype, info, true);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (!(ridge >= 0.f) || !std::isfinite(ridge)) return fail(NS_ERR_INVALID_ARG, "ridge must be finite and >= 0");
+    if (n == 0) return NS_OK;
+    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
+    const size_t es = dtype == NS_BF16 ? 2 : 4;
+    PieceLists pieces(n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!info[i].active) continue;
+        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
+        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]),
+                                     info[i].cols, info[i].cols});
+    }
+    return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream), true, ridge);
 }

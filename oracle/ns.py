@@ -61,3 +61,45 @@ def newton_schulz(g, steps: int, a: float, b: float, c: float, eps: float) -> np
     if transposed:
         x = x.T
     return np.ascontiguousarray(x).reshape(shape)
+
+
+def newton_schulz_gram(g, steps: int, a: float, b: float, c: float, eps: float,
+                       ridge: float = 0.0) -> np.ndarray:
+    """Newton-Schulz evaluated in the m x m Gram space, in float64.
+
+    "[GTP][Muon] Optimize Muon step performance" page, "Secondary (parked)",
+    gram_once: an exact Gram-space reformulation of the iteration, hardened
+    with an fp32 Gram and a trace ridge. With X0 the normalised (and, if tall,
+    transposed) input, every iterate is X_k = Q_k X0 for an m x m matrix Q_k
+    (Q_0 = I), so X_k X_k^T = Q_k G Q_k^T with the Gram G = X0 X0^T, computed
+    once. Each step is then
+        A = Q G Q^T,   Q = a Q + (b A + c A A) Q
+    and the result is Q_k X0. Reading taken for the ridge, which the page
+    names but does not define: G is replaced by G + ridge (tr(G) / m) I before
+    the iteration; ridge = 0 is the exact reformulation.
+
+    Pinned by (tests/test_oracle_ns.py): equality with ``newton_schulz`` for
+    ridge = 0, and a scalar closed form for Gram matrices that are multiples of
+    the identity (with and without ridge).
+    """
+    g = np.asarray(g, dtype=np.float64)
+    if g.ndim < 2:
+        raise ValueError("Newton-Schulz needs a tensor with at least 2 dims")
+    shape = g.shape
+    x = g.reshape(shape[0], -1)
+    transposed = x.shape[0] > x.shape[1]
+    if transposed:
+        x = x.T
+    x0 = x / (np.sqrt(np.sum(x * x)) + eps)
+    m = x0.shape[0]
+    G = x0 @ x0.T
+    if ridge:
+        G = G + ridge * (np.trace(G) / m) * np.eye(m)
+    Q = np.eye(m)
+    for _ in range(steps):
+        A = Q @ G @ Q.T
+        Q = a * Q + (b * A + c * (A @ A)) @ Q
+    out = Q @ x0
+    if transposed:
+        out = out.T
+    return np.ascontiguousarray(out).reshape(shape)

@@ -321,3 +321,21 @@ def test_route_plan_axis_errors():
     assert _status(nsq.ns_routed_workspace_bytes, plan, nsq.NS_BF16) == "NS_ERR_PLAN_MISMATCH"
     whole = nsq.ns_route_plan_create_axis([(4, 6)], 2, [[0, 6]], [1], [0], 2)
     assert nsq.ns_routed_workspace_bytes(whole, nsq.NS_BF16)[0] > 0
+
+
+def test_gram_workspace_and_errors():
+    b, mb = nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_BF16)
+    # fp32: X0 (1024 x 4096) + X0^T + six 1024 x 1024 arrays, rows padded by 256 bytes
+    one = 1024 * (4096 * 4 + 256) + 4096 * (1024 * 4 + 256) + 6 * 1024 * (1024 * 4 + 256)
+    assert mb >= one and b >= 2 * one
+    assert b == nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_F32)[0]
+    lib = nsq.lib()
+    sh = _lib._shapes([(4, 4)])
+    ptrs = _lib._arr(ctypes.c_void_p, [256])
+    call = lambda ridge, steps=5: lib.ns_orthogonalize_gram(  # noqa: E731
+        1, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs), 0, steps, 3.4, -4.7, 2.0, 1e-7,
+        ridge, None, None, 0, None)
+    assert call(-1.0) == -1
+    assert call(float("inf")) == -1
+    assert call(0.0, steps=-2) == -1
+    assert call(1e-3) == -7      # valid; no workspace

@@ -122,3 +122,37 @@ def test_zero_steps_is_normalised_input():
     g = np.random.default_rng(8).standard_normal((5, 9))
     got = ns.newton_schulz(g, 0, A, B, C, EPS)
     assert np.max(np.abs(got - g / (np.linalg.norm(g) + EPS))) < 1e-15
+
+
+@pytest.mark.parametrize("shape", [(8, 13), (13, 8), (16, 16), (5, 3, 4), (1, 7), (24, 64)])
+@pytest.mark.parametrize("coeffs,steps", [(QUINTIC, 5), (CUBIC, 7), ((2.0, -1.5, 0.5), 3)])
+def test_gram_space_equals_standard(shape, coeffs, steps):
+    # the reformulation is exact: X_k = Q_k X0 in exact arithmetic
+    rng = np.random.default_rng(abs(hash(("gram", shape, steps))) % 2 ** 32)
+    g = rng.standard_normal(shape)
+    got = ns.newton_schulz_gram(g, steps, *coeffs, EPS)
+    want = ns.newton_schulz(g, steps, *coeffs, EPS)
+    assert got.shape == g.shape
+    assert np.max(np.abs(got - want)) < 1e-11
+
+
+@pytest.mark.parametrize("ridge", [0.0, 1e-3, 0.25])
+def test_gram_space_ridge_scalar_closed_form(ridge):
+    # rows of X0 orthogonal with equal norms: G = s^2 I, so with the ridge the
+    # iteration sees g = s^2 (1 + ridge) and Q_k = q_k I with
+    # q_{k+1} = q_k (a + b g q_k^2 + c g^2 q_k^4); the result is q_k X0.
+    m, n, steps = 6, 15, 5
+    rng = np.random.default_rng(3)
+    u, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    g0 = 2.5 * u.T                           # m x n, orthogonal rows of norm 2.5
+    x0 = g0 / (np.sqrt(np.sum(g0 * g0)) + EPS)
+    s2 = float(np.sum(x0 * x0)) / m
+    gg = s2 * (1.0 + ridge)
+    q = 1.0
+    for _ in range(steps):
+        q = q * (A + B * gg * q * q + C * gg * gg * q ** 4)
+    got = ns.newton_schulz_gram(g0, steps, A, B, C, EPS, ridge=ridge)
+    assert np.max(np.abs(got - q * x0)) < 1e-12
+    # and its transpose goes through the tall path to the same numbers
+    got_t = ns.newton_schulz_gram(np.ascontiguousarray(g0.T), steps, A, B, C, EPS, ridge=ridge)
+    assert np.max(np.abs(got_t - (q * x0).T)) < 1e-12
