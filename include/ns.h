@@ -347,7 +347,9 @@ ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *
 /* Kernel timing: for the kinds enabled (bit k of `kinds` enables kind k;
  * -1 enables all, 0 disables), the library records a HIP event pair on the
  * launch stream around every launch of that kind. Each pair adds a little
- * time to the stream, so enable only the kinds being measured.
+ * time to the stream, so enable only the kinds being measured. Enabling
+ * creates a pool of 4096 events up front (so no measured loop pays for event
+ * creation); it needs the GPU and returns NS_ERR_HIP if event creation fails.
  * ns_timing_read waits for the events of one kind, returns their sums and
  * clears them. Not thread-safe against concurrent batched calls.
  * kind: 0 = the B X product kernel (every step but the last),

@@ -82,41 +82,61 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
 // One chunk of a strided piece: shard bytes [off, off + len) of the piece
 // (contiguous at sp), whose byte p sits in the home at
 // hp + (p / run) * stride + p % run. Units of W bytes never straddle a run:
-// W divides run, stride, off and both bases.
-// IDX is the integer type of byte offsets inside the piece (32-bit when the
-// piece is under 4 GiB: its division is several times cheaper).
+// W divides run, stride, off and both bases. IDX is the integer type of byte
+// offsets inside the piece (32-bit when the piece is under 4 GiB: its
+// division is several times cheaper). 16-byte units keep each thread's four
+// loads in flight before the stores; narrower ones (pieces at odd offsets)
+// copy unit by unit, so the kernel's register budget stays that of the
+// contiguous path.
 template <int W, bool NT, typename IDX>
 __device__ inline void copy_chunk_strided(char *__restrict__ sp, char *__restrict__ hp, int64_t off, int64_t len,
                                           int64_t run, int64_t stride, bool to_home) {
     typedef typename std::conditional<W == 16, uint4, typename std::conditional<W == 4, uint32_t, uint16_t>::type>::type U;
-    constexpr int kPer = (int)(kRouteChunkBytes / W / kRouteThreads);
     const int64_t nu = len / W;
     const IDX run_i = (IDX)run;
-    U v[kPer];
-    int64_t hoff[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int64_t u = threadIdx.x + (int64_t)kRouteThreads * k;
-        if (u < nu) {
-            const int64_t p = off + u * W;
-            const IDX r = (IDX)p / run_i;
-            hoff[k] = (int64_t)r * stride + (int64_t)((IDX)p - r * run_i);
-            v[k] = to_home ? *reinterpret_cast<const U *>(sp + p) : *reinterpret_cast<const U *>(hp + hoff[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int64_t u = threadIdx.x + (int64_t)kRouteThreads * k;
-        if (u < nu) {
-            U *dst = reinterpret_cast<U *>(to_home ? hp + hoff[k] : sp + off + u * W);
-            if constexpr (NT && W == 16) {
-                __builtin_nontemporal_store(v[k].x, &dst->x);
-                __builtin_nontemporal_store(v[k].y, &dst->y);
-                __builtin_nontemporal_store(v[k].z, &dst->z);
-                __builtin_nontemporal_store(v[k].w, &dst->w);
+    auto home_off = [&](int64_t p) -> int64_t {
+        const IDX r = (IDX)p / run_i;
+        return (int64_t)r * stride + (int64_t)((IDX)p - r * run_i);
+    };
+    static_assert(kRouteChunkBytes == 4 * 16 * kRouteThreads, "four 16-byte units per thread in a full chunk");
+    if (W == 16 && nu == 4 * kRouteThreads) {   // full chunk: the four loads in flight before the stores
+        const int64_t p0 = off + (int64_t)threadIdx.x * 16, step = 16 * kRouteThreads;
+        const int64_t h0 = home_off(p0), h1 = home_off(p0 + step), h2 = home_off(p0 + 2 * step),
+                      h3 = home_off(p0 + 3 * step);
+        const char *src = to_home ? sp : hp;
+        char *dst = to_home ? hp : sp;
+        const int64_t s0 = to_home ? p0 : h0, s1 = to_home ? p0 + step : h1, s2 = to_home ? p0 + 2 * step : h2,
+                      s3 = to_home ? p0 + 3 * step : h3;
+        const int64_t d0 = to_home ? h0 : p0, d1 = to_home ? h1 : p0 + step, d2 = to_home ? h2 : p0 + 2 * step,
+                      d3 = to_home ? h3 : p0 + 3 * step;
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(src + s0);
+        const uint4 v1 = *reinterpret_cast<const uint4 *>(src + s1);
+        const uint4 v2 = *reinterpret_cast<const uint4 *>(src + s2);
+        const uint4 v3 = *reinterpret_cast<const uint4 *>(src + s3);
+        auto put = [&](int64_t d, const uint4 &v) {
+            uint4 *q = reinterpret_cast<uint4 *>(dst + d);
+            if constexpr (NT) {
+                __builtin_nontemporal_store(v.x, &q->x);
+                __builtin_nontemporal_store(v.y, &q->y);
+                __builtin_nontemporal_store(v.z, &q->z);
+                __builtin_nontemporal_store(v.w, &q->w);
             } else {
-                *dst = v[k];
+                *q = v;
             }
+        };
+        put(d0, v0);
+        put(d1, v1);
+        put(d2, v2);
+        put(d3, v3);
+    } else {
+        for (int64_t u = threadIdx.x; u < nu; u += kRouteThreads) {
+            const int64_t p = off + u * W;
+            U *h = reinterpret_cast<U *>(hp + home_off(p));
+            U *sh = reinterpret_cast<U *>(sp + p);
+            if (to_home)
+                *h = *sh;
+            else
+                *sh = *h;
         }
     }
 }

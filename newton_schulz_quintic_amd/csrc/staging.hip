@@ -3,7 +3,9 @@
 // straight from this buffer (it is mapped into the device's address space) and
 // copies them into the workspace for the later kernels. A buffer is reused only
 // after the event recorded behind that kernel has completed, so the host never
-// overwrites data a pending kernel still reads.
+// overwrites data a pending kernel still reads. All kMaxSlots buffers are made
+// on the first call: a host that runs calls ahead of the GPU then never pays
+// for pinned allocation (several ms each) in its steady state.
 
 #include <mutex>
 #include <vector>
@@ -34,6 +36,15 @@ bool idle(Slot &s) {
 
 ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr) {
     std::lock_guard<std::mutex> lk(g_mu);
+    while (g_slots.size() < kMaxSlots) {
+        g_slots.emplace_back();
+        Slot &s = g_slots.back();
+        NSQ_HIP(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
+        const size_t cap = std::max<size_t>(bytes, 1 << 20);
+        NSQ_HIP(hipHostMalloc(&s.ptr, cap, hipHostMallocDefault));
+        NSQ_HIP(hipHostGetDevicePointer(&s.dev, s.ptr, 0));
+        s.cap = cap;
+    }
     int pick = -1;
     for (size_t i = 0; i < g_slots.size(); ++i)
         if (idle(g_slots[i]) && (pick < 0 || g_slots[i].cap >= bytes)) {

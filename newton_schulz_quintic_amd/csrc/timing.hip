@@ -58,9 +58,18 @@ void timing_stop(int slot, hipStream_t stream) {
 
 using namespace nsq;
 
+// Events are made ahead, when timing is switched on: creating them on demand
+// inside a measured loop costs host time that the loop would then report.
+constexpr size_t kPoolEvents = 4096;
+
 extern "C" ns_status ns_timing_enable(int32_t kinds) {
     std::lock_guard<std::mutex> lk(g_mu);
     g_mask = kinds == -1 ? (1u << kTimeKinds) - 1 : (uint32_t)kinds & ((1u << kTimeKinds) - 1);
+    while (g_mask && g_pool.size() + 2 * g_recs.size() < kPoolEvents) {
+        hipEvent_t e = nullptr;
+        NSQ_HIP(hipEventCreate(&e));
+        g_pool.push_back(e);
+    }
     return NS_OK;
 }
 
