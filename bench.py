@@ -26,6 +26,7 @@ a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -452,6 +453,10 @@ def main():
     # so the step time carries as little instrumentation as possible.
     if not args.no_kernel_timing:
         nsq.ns_timing_enable([0])
+    # The timed loops run with Python's collector paused (after a collection):
+    # a full collection landing inside a loop stalls the host for tens of ms.
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -481,6 +486,7 @@ def main():
             other()
         torch.cuda.synchronize()
         ms_other = (time.perf_counter() - t2) * 1e3 / args.steps
+    gc.enable()
 
     flops = sum(alg_flops(*oriented(s), ms.steps, ms.coeffs[2] != 0.0) for s in ms.shapes)
     dense = sum(ms.steps * (4 * m * m * n + 2 * m ** 3) for m, n in (oriented(s) for s in ms.shapes))
