@@ -185,3 +185,17 @@ def test_routed_equals_unrouted_bitwise():
         for i, split in enumerate(ms.split_rows):
             want.append(np.split(direct[i], np.cumsum(split)[:-1], axis=0)[s].ravel())
         assert np.array_equal(to_host(shards[s], "bf16"), np.concatenate(want))
+
+
+def test_tile_size_does_not_change_bits(monkeypatch):
+    """The product tile (256 or 128, picked per call from the batch's size) must
+    not change a matrix's bits: batch invariance across tile choices."""
+    shapes = [(1024, 1024), (512, 1536), (1536, 512), (300, 700)]
+    hosts = [host_matrix(16, i, s) for i, s in enumerate(shapes)]
+    log("ns: 256 vs 128 product tiles")
+    monkeypatch.setenv("NS_TILE", "256")
+    big = _run_gpu(hosts, "bf16")
+    monkeypatch.setenv("NS_TILE", "128")
+    small = _run_gpu(hosts, "bf16")
+    for x, y in zip(big, small):
+        assert np.array_equal(x, y)
