@@ -291,13 +291,13 @@ PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
 
 
 def gram_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
-    """Algorithmic flops of Gram-space NS on one matrix: the Gram m(m+1)n; step
-    0 (Q0 = I) one symmetric product G G; every later step four symmetric
-    m x m products (Q G, (Q G) Q, A A, B' Q), m^2(m+1) each (A A skipped when
-    c == 0); the output Q X0, 2 m^2 n."""
-    sym = m * m * (m + 1)
-    per_step = (4 if c_nonzero else 3) * sym
-    return float(m * (m + 1) * n + (sym if c_nonzero else 0) + max(0, steps - 1) * per_step + 2 * m * m * n)
+    """Algorithmic flops of Gram-space NS on one matrix: the Gram m(m+1)n
+    (symmetric, counted once); step 0 (Q0 = I) one product G G; every later
+    step four full m x m products (Q G, (Q G) Q, A A, B' Q), 2 m^3 each (A A
+    skipped when c == 0); the output Q X0, 2 m^2 n."""
+    full = 2 * m * m * m
+    per_step = (4 if c_nonzero else 3) * full
+    return float(m * (m + 1) * n + (full if c_nonzero else 0) + max(0, steps - 1) * per_step + 2 * m * m * n)
 
 
 def gram_bench(ms, ridge: float, reps: int) -> dict:

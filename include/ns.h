@@ -250,7 +250,7 @@ ns_status ns_orthogonalize_strided(int32_t n, const ns_shape *shapes, const void
  * Gram-space reformulation hardened with an fp32 Gram and a trace ridge]
  * ------------------------------------------------------------------------ */
 
-/* Workspace for ns_orthogonalize_gram (fp32 X0, X0^T and six m x m arrays
+/* Workspace for ns_orthogonalize_gram (fp32 X0, X0^T and nine m x m arrays
  * per tensor), as for ns_workspace_bytes. Errors: INVALID_ARG, DTYPE, OVERFLOW. */
 ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype, size_t *bytes,
                                   size_t *min_bytes);
@@ -262,10 +262,12 @@ ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dt
  * evaluated as Q' = (a I + b A + c A A) Q; the output is Q_k X0 in the input's
  * shape and dtype. ridge = 0 is exactly the NS iteration (in exact
  * arithmetic); ridge > 0 regularises a near-singular Gram and changes the
- * result. In this plain form every Q_k is a polynomial in G, so the m x m
- * products are symmetric and computed as upper tiles. The products are m^3
- * per step instead of m^2 n: cheaper when n >> m, but in fp32 (157 TFLOP/s
- * dense on MI355X, against 2.5 PFLOP/s bf16).
+ * result. Every Q_k is a polynomial in G, so in exact arithmetic the m x m
+ * products are symmetric; in fp32 they are not, and are computed as full
+ * products (forcing symmetry loses about a decimal digit on ill-conditioned
+ * inputs); only G is formed as an upper-tile product. The products are
+ * 4 (2 m^3) per step instead of about 4 m^2 n: cheaper when n >> m, but in
+ * fp32 (157 TFLOP/s dense on MI355X, against 2.5 PFLOP/s bf16).
  * ridge: finite, >= 0. Other arguments and errors as for
  * ns_orthogonalize_batched (workspace from ns_gram_workspace_bytes). */
 ns_status ns_orthogonalize_gram(int32_t n, const ns_shape *shapes, const void *const *in, void *const *out,

@@ -73,6 +73,7 @@ struct NsProb {
     char *a;           // A: mp x mp (row stride ldt)
     char *b;           // B: mp x mp (row stride ldt)
     char *g, *q0, *q1, *t;   // Gram-space only: G, Q ping/pong, Q G; mp x mp fp32 (row stride ldt)
+    char *qt0, *qt1, *at;    // Gram-space only: Q^T ping/pong, A^T
     float *partials;   // nparts fp32 sums of squares, one per staging tile
     int32_t m, n;      // oriented sizes (m <= n)
     int32_t mp, np;    // padded to kPad
@@ -167,20 +168,30 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 // Optimize Muon step performance", "Secondary (parked)", gram_once): the
 // iterate is X_k = Q_k X0 with the m x m Gram G = X0 X0^T computed once, so a
 // step is A = Q G Q^T, Q' = (a I + b A + c A A) Q on m x m matrices, and the
-// result is Q_k X0. Q_k is a polynomial in G, hence symmetric and commuting
-// with G, so Q G, (Q G) Q and B' Q are symmetric and computed as upper tiles.
+// result is Q_k X0. In exact arithmetic Q_k is a polynomial in G, so all of
+// these are symmetric; in fp32 they are not, and forcing them symmetric
+// (copying one triangle over the other, or averaging) multiplies the error on
+// ill-conditioned inputs about tenfold. So only G (exactly symmetric: its
+// (i, j) and (j, i) sum the same products) is an upper-tile product; the
+// others are full products, and each matrix that is later a right operand
+// is also written transposed, so every product reads K-major rows.
 enum Mode {
-    kSyrkX = 0,    // A = s_final X X^T
-    kSyrkA = 1,    // B' = s_final (s_init A + A A) + s_diag I
-    kGemmBX = 2,   // X' = B' X
-    kGramG = 3,    // G = s^2 X0 X0^T + ridge (tr G / m) I
-    kGramB0 = 4,   // Q1 = s_final (s_init G + G G) + s_diag I   (step 0: Q0 = I)
+    kSyrkX = 0,    // A = s_final X X^T                             upper tiles
+    kSyrkA = 1,    // B' = s_final (s_init A + A A) + s_diag I      upper tiles
+    kGemmBX = 2,   // X' = B' X, also X'^T
+    kGramG = 3,    // G = s^2 X0 X0^T + ridge (tr G / m) I          upper tiles
+    kGramB0 = 4,   // Q1 = s_final (s_init G + G G) + s_diag I, also Q1^T   (step 0: Q0 = I)
     kGramQG = 5,   // T = Q G
-    kGramTQ = 6,   // A = T Q
-    kGramBQ = 7,   // Q' = B' Q
-    kGramOut = 8,  // out = s Q X0 (last launch, the caller's output)
+    kGramTQ = 6,   // A = T Q, also A^T
+    kGramAA = 7,   // B' = s_final (s_init A + A A) + s_diag I
+    kGramBQ = 8,   // Q' = B' Q, also Q'^T
+    kGramOut = 9,  // out = s Q X0 (last launch, the caller's output)
 };
-constexpr bool symmetric_mode(int mode) { return mode != kGemmBX && mode != kGramOut; }
+constexpr bool symmetric_mode(int mode) { return mode == kSyrkX || mode == kSyrkA || mode == kGramG; }
+// Modes that also write their result transposed (the next products' K-major operand).
+constexpr bool writes_transpose(int mode) {
+    return mode == kGemmBX || mode == kGramB0 || mode == kGramTQ || mode == kGramBQ;
+}
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
 // (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
@@ -249,6 +260,10 @@ __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *regio
     return *reinterpret_cast<const frag *>(region + row * ROWB + ((c ^ swz<ROWB>(row)) << 4));
 }
 
+// Rounding is spelled out wherever a product meets a sum (an explicit fused
+// multiply-add here, separate rounded multiply and add in the epilogue), so
+// that no tile configuration's instruction choice can change a result bit.
+//
 // acc += s * P[r][k0 + c] for the accumulator blocks whose 32 columns lie in
 // the P stage `sp` (stage columns k0 .. k0 + KW, KW = ROWB / es), where the
 // tile's column c0 + wn BM/WN + 32 j maps to stage column
@@ -288,7 +303,7 @@ __device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s
                     for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, kc + (lane & 31)));
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += s * old[e];
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = __builtin_fmaf(s, old[e], acc[i][j][4 * q + e]);
             }
     }
 }
@@ -652,14 +667,17 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                            np * ES / C::ROWB, lds, acc);
-    } else if constexpr (MODE == kSyrkA || MODE == kGramB0) {
+    } else if constexpr (MODE == kSyrkA || MODE == kGramB0 || MODE == kGramAA) {
+        // S S with S symmetric (A, G): the Q operand is S's rows; the general
+        // A A of the Gram space reads A^T's rows instead
         const int ld = ldt * ES;
-        char *S = MODE == kSyrkA ? A : pr.g;
+        char *S = MODE == kSyrkA ? A : MODE == kGramB0 ? pr.g : A;
+        char *SQ = MODE == kGramAA ? pr.at : S;
         if (do_product) {
             // the old tile S[row0.., col0..] passes through the P stages of
             // columns col0 .. col0 + BM: seed s_init S from there
             zero_acc<C>(acc);
-            tile_product<T, C, true>(S + (int64_t)row0 * ld, S + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+            tile_product<T, C, true>(S + (int64_t)row0 * ld, SQ + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                                      mp * ES / C::ROWB, lds, acc, col0 * ES / C::ROWB, s_init);
         } else {
             init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
@@ -670,8 +688,9 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
                            mp * ES / C::ROWB, lds, acc);
     } else {   // Gram-space products, all with K = mp
+        char *qtc = cur ? pr.qt1 : pr.qt0;
         char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
-        char *Q = MODE == kGramQG ? pr.g : MODE == kGramOut ? pr.xt0 : qc;
+        char *Q = MODE == kGramQG ? pr.g : MODE == kGramOut ? pr.xt0 : qtc;   // G symmetric; else K-major transposes
         const int ldp = ldt * ES, ldq = (MODE == kGramOut ? ldxt : ldt) * ES;
         zero_acc<C>(acc);
         tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
@@ -684,7 +703,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     // the type it is stored in: the workspace type, or the output's.
     typedef typename std::conditional<LAST, TO, T>::type TS;
     constexpr int SES = sizeof(TS);
-    constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG;
+    constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG || MODE == kGramAA;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     __syncthreads();   // every wave is done reading operand panels
@@ -699,15 +718,24 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : s_final * acc[i][j][4 * q + e];
+                    v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : __fmul_rn(s_final, acc[i][j][4 * q + e]);
                     if constexpr (kDiag)
-                        if (tr.ti == tr.tj && r + e == c && row0 + r + e < pr.m) v[e] += s_diag;
+                        if (tr.ti == tr.tj && r + e == c && row0 + r + e < pr.m) v[e] = __fadd_rn(v[e], s_diag);
                 }
                 stage4<TS, BM>(lds, r, c, v);
             }
         }
     }
     __syncthreads();
+    // A diagonal tile of the seeded A A product writes its lower half from its
+    // upper half, so every element (i, j) carries the value computed at
+    // (min(i, j), max(i, j)) whatever the tile size: computed directly, the
+    // lower half would differ in the last bit, as (b / c) A is added at the
+    // stage of the element's column. (X X^T and G need no such step: their
+    // (i, j) and (j, i) sum the same products in the same order.) Row r's
+    // elements left of the diagonal are staged column r's, which the row
+    // stores below pick up with one extra 16-byte read per chunk.
+    const bool mirror_lower = MODE == kSyrkA && tr.ti == tr.tj;
 
     // Epilogue, part 2: write the staged tile.
     constexpr int NU = BM * SES / 16;                // 16-byte units per staged column
@@ -715,16 +743,28 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     if constexpr (!LAST) {
         // row-major: the tile itself, at (row0, col0)
         char *D = MODE == kSyrkX ? A : MODE == kSyrkA ? B : MODE == kGemmBX ? xn : MODE == kGramG ? pr.g
-                : MODE == kGramQG ? pr.t : MODE == kGramTQ ? A : qn;   // kGramB0, kGramBQ: the next Q
+                : MODE == kGramQG ? pr.t : MODE == kGramTQ ? A : MODE == kGramAA ? B : qn;   // B0, BQ: next Q
         const int ldd = MODE == kGemmBX ? ldx : ldt;
         for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
             int r, c;
-            const i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
+            i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
+            if (mirror_lower && c < r) {   // elements c .. c + 16/es - 1 of row r; those left of r mirrored
+                constexpr int E = 16 / ES;
+                const i32x4 lo = *reinterpret_cast<const i32x4 *>(lds + r * (BM * ES) + (((c * ES >> 4) ^ swt(r)) << 4));
+                T up[E], dn[E];
+                __builtin_memcpy(up, &w, 16);
+                __builtin_memcpy(dn, &lo, 16);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (c + e < r) up[e] = dn[e];
+                __builtin_memcpy(&w, up, 16);
+            }
             store16<T>(D, (int64_t)(row0 + r) * ldd + col0 + c, w);
         }
-        // column-major: the mirror tile at (col0, row0), or X'^T
-        if (!symmetric_mode(MODE) || tr.ti != tr.tj) {
-            char *E = MODE == kGemmBX ? xtn : D;
+        // column-major: the mirror tile at (col0, row0), or the transpose
+        if (writes_transpose(MODE) || (symmetric_mode(MODE) && tr.ti != tr.tj)) {
+            char *qtn = cur ? pr.qt0 : pr.qt1;
+            char *E = MODE == kGemmBX ? xtn : MODE == kGramTQ ? pr.at : MODE == kGramB0 || MODE == kGramBQ ? qtn : D;
             const int lde = MODE == kGemmBX ? ldxt : ldt;
             for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
                 int c, r;
@@ -830,7 +870,7 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             fv[e] = to_f32<TI>(vals[e]);
-            ss += fv[e] * fv[e];
+            ss = __builtin_fmaf(fv[e], fv[e], ss);
         }
         if constexpr (UPL == 1) {
             store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
@@ -926,6 +966,7 @@ struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
     int64_t nparts, syrk_tiles, gemm_tiles;
+    int64_t sq_tiles;  // full m x m grid (Gram-space products only)
     int64_t npieces;   // row pieces its input / output is split into
     size_t buf_bytes;
 };
@@ -970,9 +1011,10 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         const int64_t tm = mi.mp / 128, tn = mi.np / 128;
         mi.syrk_tiles = tm * (tm + 1) / 2;
         mi.gemm_tiles = tm * tn;
+        mi.sq_tiles = gram ? tm * tm : 0;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.npieces = 1;
-        mi.buf_bytes = gram ? x_bytes(mi, es) + xt_bytes(mi, es) + 6 * a_bytes(mi, es)
+        mi.buf_bytes = gram ? x_bytes(mi, es) + xt_bytes(mi, es) + 9 * a_bytes(mi, es)
                             : 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
@@ -980,21 +1022,23 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
 
 // Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, ptiles, pieces, partials, total;
+    size_t probs, syrk, gemm, sq, ptiles, pieces, partials, total;
     size_t o_syrk() const { return probs; }
     size_t o_gemm() const { return o_syrk() + syrk; }
-    size_t o_ptiles() const { return o_gemm() + gemm; }
+    size_t o_sq() const { return o_gemm() + gemm; }
+    size_t o_ptiles() const { return o_sq() + sq; }
     size_t o_pieces() const { return o_ptiles() + ptiles; }
     size_t o_partials() const { return o_pieces() + pieces; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, pa = 0, pc = 0;
+    int64_t np = 0, sy = 0, ge = 0, sq = 0, pa = 0, pc = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
         sy += mi.syrk_tiles;
         ge += mi.gemm_tiles;
+        sq += mi.sq_tiles;
         pa += mi.nparts;
         pc += mi.npieces;
     }
@@ -1002,6 +1046,7 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
     t.probs = align256(np * sizeof(NsProb));
     t.syrk = align256(sy * sizeof(TileRef));
     t.gemm = align256(ge * sizeof(TileRef));
+    t.sq = align256(sq * sizeof(TileRef));
     t.ptiles = align256(pa * sizeof(TileRef));
     t.pieces = align256(pc * sizeof(RowPiece));
     t.partials = align256(pa * sizeof(float));
@@ -1103,7 +1148,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const int64_t es = sizeof(T), esi = sizeof(TI);
     const int bm = gram ? 128 : pick_tile(group, info, es);
     std::vector<NsProb> probs;
-    std::vector<TileRef> syrk, gemm, ptiles;
+    std::vector<TileRef> syrk, gemm, sq, ptiles;
     std::vector<RowPiece> gpieces;
     char *base = ws + tsz.total;
     float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
@@ -1120,15 +1165,18 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             p.xt1 = p.xt0 + xtb;
             p.a = p.xt1 + xtb;
             p.b = p.a + ab;
-        } else {   // X0, X0^T, G, Q ping/pong, Q G, A, B'
+        } else {   // X0, X0^T, G, Q and Q^T ping/pong, Q G, A, A^T, B'
             p.x0 = base;
             p.xt0 = p.x0 + xb;
             p.g = p.xt0 + xtb;
             p.q0 = p.g + ab;
             p.q1 = p.q0 + ab;
-            p.t = p.q1 + ab;
+            p.qt0 = p.q1 + ab;
+            p.qt1 = p.qt0 + ab;
+            p.t = p.qt1 + ab;
             p.a = p.t + ab;
-            p.b = p.a + ab;
+            p.at = p.a + ab;
+            p.b = p.at + ab;
         }
         base += mi.buf_bytes;
         const std::vector<RowPiece> &pc = pieces[idx];
@@ -1168,6 +1216,11 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         for (size_t k = s0; k < syrk.size(); ++k) syrk[k].piece = pbase;   // unused by the SYRK steps
         grouped_tiles(pid, tm, tn, false, gemm);
         for (size_t k = g0; k < gemm.size(); ++k) set_band(gemm[k], bm);
+        if (gram) {
+            const size_t q0 = sq.size();
+            grouped_tiles(pid, tm, tm, false, sq);
+            for (size_t k = q0; k < sq.size(); ++k) sq[k].piece = pbase;   // no caller memory touched
+        }
         const int pm = (int)(mi.mp / kPrepTile), pn = (int)(mi.np / kPrepTile);
         for (int ti = 0; ti < pm; ++ti)   // partial index ti * pn + tj
             for (int tj = 0; tj < pn; ++tj) {
@@ -1196,6 +1249,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     put(0, probs.data(), probs.size() * sizeof(NsProb));
     put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
     put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
+    put(tsz.o_sq(), sq.data(), sq.size() * sizeof(TileRef));
     put(tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
     put(tsz.o_pieces(), gpieces.data(), gpieces.size() * sizeof(RowPiece));
     const char *hdev = static_cast<const char *>(staging_dev);
@@ -1203,6 +1257,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
     const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
+    const TileRef *d_sq = reinterpret_cast<const TileRef *>(ws + tsz.o_sq());
     const TileRef *d_ptiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ptiles());
     const RowPiece *d_pieces = reinterpret_cast<const RowPiece *>(ws + tsz.o_pieces());
     const int32_t npt = (int32_t)ptiles.size();
@@ -1229,34 +1284,32 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                 const bool fused = c != 0.f && std::isfinite(ratio);
                 const float si = fused ? ratio : b, sf = fused ? c : 1.f;
                 const int32_t prod = fused ? 1 : 0;
-                const int32_t nsy = (int32_t)syrk.size(), nge = (int32_t)gemm.size();
+                const int32_t nsy = (int32_t)syrk.size(), nge = (int32_t)gemm.size(), nsq = (int32_t)sq.size();
+                double f_sq = 0;   // one full m x m product per matrix: 2 m^3
+                for (int32_t idx : group) f_sq += 2.0 * (double)info[idx].m * info[idx].m * info[idx].m;
                 {
                     TimedScope ts(kTimeSyrkX, st, f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
                     launch_mode<T, Small, kGramG>(nsy, st, d_probs, d_syrk, 0, 1.f, 1.f, ridge, 1, 1, eps, d_pieces);
                 }
                 {
-                    TimedScope ts(kTimeSyrkA, st, f_syrk_a);   // Q1 = a I + b G + c G G
-                    launch_mode<T, Small, kGramB0>(nsy, st, d_probs, d_syrk, 0, si, sf, a, prod, 0, eps, d_pieces);
+                    TimedScope ts(kTimeSyrkA, st, fused ? f_sq : 0.0);   // Q1 = a I + b G + c G G
+                    launch_mode<T, Small, kGramB0>(nsq, st, d_probs, d_sq, 0, si, sf, a, prod, 0, eps, d_pieces);
                 }
                 NSQ_HIP(hipGetLastError());
                 int qcur = 1;
                 for (int32_t k = 1; k < steps; ++k) {
                     {
-                        TimedScope ts(kTimeProduct, st, 2 * f_syrk_a);   // T = Q G, A = T Q
-                        launch_mode<T, Small, kGramQG>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
-                                                       d_pieces);
-                        launch_mode<T, Small, kGramTQ>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
-                                                       d_pieces);
+                        TimedScope ts(kTimeProduct, st, 2 * f_sq);   // T = Q G, A = T Q (and A^T)
+                        launch_mode<T, Small, kGramQG>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
+                        launch_mode<T, Small, kGramTQ>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
                     }
                     {
-                        TimedScope ts(kTimeSyrkA, st, f_syrk_a);   // B' = a I + b A + c A A
-                        launch_mode<T, Small, kSyrkA>(nsy, st, d_probs, d_syrk, qcur, si, sf, a, prod, 0, eps,
-                                                      d_pieces);
+                        TimedScope ts(kTimeSyrkA, st, fused ? f_sq : 0.0);   // B' = a I + b A + c A A
+                        launch_mode<T, Small, kGramAA>(nsq, st, d_probs, d_sq, qcur, si, sf, a, prod, 0, eps, d_pieces);
                     }
                     {
-                        TimedScope ts(kTimeProduct, st, f_syrk_a);   // Q' = B' Q
-                        launch_mode<T, Small, kGramBQ>(nsy, st, d_probs, d_syrk, qcur, 1.f, 1.f, 0.f, 1, 0, eps,
-                                                       d_pieces);
+                        TimedScope ts(kTimeProduct, st, f_sq);   // Q' = B' Q (and Q'^T)
+                        launch_mode<T, Small, kGramBQ>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
                     }
                     NSQ_HIP(hipGetLastError());
                     qcur ^= 1;

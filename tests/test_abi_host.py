@@ -325,8 +325,8 @@ def test_route_plan_axis_errors():
 
 def test_gram_workspace_and_errors():
     b, mb = nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_BF16)
-    # fp32: X0 (1024 x 4096) + X0^T + six 1024 x 1024 arrays, rows padded by 256 bytes
-    one = 1024 * (4096 * 4 + 256) + 4096 * (1024 * 4 + 256) + 6 * 1024 * (1024 * 4 + 256)
+    # fp32: X0 (1024 x 4096) + X0^T + nine 1024 x 1024 arrays, rows padded by 256 bytes
+    one = 1024 * (4096 * 4 + 256) + 4096 * (1024 * 4 + 256) + 9 * 1024 * (1024 * 4 + 256)
     assert mb >= one and b >= 2 * one
     assert b == nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_F32)[0]
     lib = nsq.lib()
