@@ -250,7 +250,7 @@ ns_status ns_orthogonalize_strided(int32_t n, const ns_shape *shapes, const void
  * Gram-space reformulation hardened with an fp32 Gram and a trace ridge]
  * ------------------------------------------------------------------------ */
 
-/* Workspace for ns_orthogonalize_gram (fp32 X0, X0^T and nine m x m arrays
+/* Workspace for ns_orthogonalize_gram (fp32 X0 and nine m x m arrays
  * per tensor), as for ns_workspace_bytes. Errors: INVALID_ARG, DTYPE, OVERFLOW. */
 ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype, size_t *bytes,
                                   size_t *min_bytes);

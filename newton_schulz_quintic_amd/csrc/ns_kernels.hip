@@ -9,15 +9,16 @@
 //
 // Design (one GPU, every matrix of a group in flight at once):
 //  * Workspace per matrix, oriented so m <= n, padded to multiples of 256 in
-//    both dims and kept zero in the padding: X and its transpose X^T (two
-//    copies of each, ping-pong), A and B. Padding removes every bounds check
-//    from the product main loop; zero padding stays zero through every step
-//    (products with zero rows/cols).
-//  * All three products run one MFMA main loop, C = P Q^T over K panels, with
-//    both operands read along their rows (K contiguous):
-//        A   = X X^T  : P = Q = X
-//        A A          : P = Q = A       (A A = A A^T, A symmetric)
-//        B X          : P = B, Q = X^T  (B X = B (X^T)^T)
+//    both dims and kept zero in the padding: X (two copies, ping-pong), A and
+//    B. Padding removes every bounds check from the product main loop; zero
+//    padding stays zero through every step (products with zero rows/cols).
+//  * All three products run one MFMA main loop over K panels:
+//        A   = X X^T  : P = Q = X        (C = P Q^T, both read along rows)
+//        A A          : P = Q = A        (A A = A A^T, A symmetric)
+//        B X          : P = B, Q = X     (C = P Q, Q read K-major: stage kb
+//                                         holds 64 rows of X, and the MFMA
+//                                         fragments come from LDS transpose
+//                                         reads, so X^T is never stored)
 //    Panels of 128 bytes of K per row go global -> LDS with buffer_load ... lds
 //    into two stage buffers; every wave loads a slice of both panels.
 //    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups).
@@ -26,13 +27,14 @@
 //    exactly symmetric.
 //  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X.
 //    The rounded tile is staged in LDS column-major; the tile is then written
-//    row-major through LDS transpose reads and column-major (the mirror, or
-//    X'^T) from plain LDS rows, both as 16-byte stores. The last step's
+//    row-major through LDS transpose reads and, for the symmetric products'
+//    mirror, column-major from plain LDS rows, both as 16-byte stores. The last step's
 //    epilogue writes straight to the caller's output in the input's
 //    orientation, shape and dtype.
-//  * Norm: per-chunk fp32 sums of squares in a fixed order (no atomics), then a
-//    tile pass that reduces the partials, scales, and writes X0 and X0^T
-//    (transposing tall inputs through LDS).
+//  * Input staging: the input goes unscaled into X0 (tall inputs transposed
+//    through LDS) with per-tile fp32 sums of squares; the products reduce
+//    those in a fixed order (no atomics) and fold the scale into the first
+//    step's epilogues.
 //  * Workgroup ids are remapped so consecutive tiles land on the same XCD (the
 //    hardware hands workgroups to the 8 XCDs round-robin), sharing its L2, and
 //    tiles are taken in groups of 4 x 8 so a run of tiles reuses operand panels.
@@ -69,7 +71,7 @@ constexpr int kRowPadBytes = 256;
 // Per-matrix descriptor in device memory.
 struct NsProb {
     char *x0, *x1;     // X ping/pong: mp x np (row stride ldx)
-    char *xt0, *xt1;   // X^T ping/pong: np x mp (row stride ldxt)
+    char *xt0, *xt1;   // X^T ping/pong: np x mp (row stride ldxt); null when kmajor
     char *a;           // A: mp x mp (row stride ldt)
     char *b;           // B: mp x mp (row stride ldt)
     char *g, *q0, *q1, *t;   // Gram-space only: G, Q ping/pong, Q G; mp x mp fp32 (row stride ldt)
@@ -80,6 +82,7 @@ struct NsProb {
     int32_t ldx;       // row stride of X (elements, > np)
     int32_t ldxt;      // row stride of X^T (elements, > mp)
     int32_t ldt;       // row stride of A and B (elements, > mp)
+    int32_t kmajor;    // B X reads X K-major (as stored); X^T is not kept
     int32_t tall;      // input had rows > cols
     int32_t nparts;    // (mp / kPrepTile) * (np / kPrepTile)
     int32_t vec_in;    // every input piece allows 16-byte accesses (aligned base, row bytes % 16 == 0)
@@ -174,11 +177,12 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 // ill-conditioned inputs about tenfold. So only G (exactly symmetric: its
 // (i, j) and (j, i) sum the same products) is an upper-tile product; the
 // others are full products, and each matrix that is later a right operand
-// is also written transposed, so every product reads K-major rows.
+// is also written transposed, so those products read K-major rows (the last
+// one, Q X0, reads X0 as stored, like B' X).
 enum Mode {
     kSyrkX = 0,    // A = s_final X X^T                             upper tiles
     kSyrkA = 1,    // B' = s_final (s_init A + A A) + s_diag I      upper tiles
-    kGemmBX = 2,   // X' = B' X, also X'^T
+    kGemmBX = 2,   // X' = B' X
     kGramG = 3,    // G = s^2 X0 X0^T + ridge (tr G / m) I          upper tiles
     kGramB0 = 4,   // Q1 = s_final (s_init G + G G) + s_diag I, also Q1^T   (step 0: Q0 = I)
     kGramQG = 5,   // T = Q G
@@ -188,9 +192,10 @@ enum Mode {
     kGramOut = 9,  // out = s Q X0 (last launch, the caller's output)
 };
 constexpr bool symmetric_mode(int mode) { return mode == kSyrkX || mode == kSyrkA || mode == kGramG; }
-// Modes that also write their result transposed (the next products' K-major operand).
+// Modes that always write their result transposed (the next products' K-major
+// operand); B X also writes X'^T unless the next B X reads X' K-major.
 constexpr bool writes_transpose(int mode) {
-    return mode == kGemmBX || mode == kGramB0 || mode == kGramTQ || mode == kGramBQ;
+    return mode == kGramB0 || mode == kGramTQ || mode == kGramBQ;
 }
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
@@ -260,6 +265,51 @@ __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *regio
     return *reinterpret_cast<const frag *>(region + row * ROWB + ((c ^ swz<ROWB>(row)) << 4));
 }
 
+// K-major Q panels (the Q operand read from a row-major matrix whose rows run
+// along K, e.g. X for X' = B' X): a stage holds KW = ROWB / es rows of K, each
+// the BM tile columns (BM es bytes). The 16-byte unit u of panel row k sits at
+// unit position u ^ swq(k), which puts the rows read together on distinct
+// banks: bf16 fragments come from LDS transpose reads of four consecutive rows
+// (XOR 4 (k % 4) moves their 64-byte pieces to four bank groups), f32
+// fragments from 4-byte reads of rows k and k + 4 (XOR 8 ((k / 4) % 2)).
+template <int ES> __device__ __forceinline__ int swq(int k) {
+    if constexpr (ES == 2) return 4 * (k & 3);
+    else return 8 * ((k >> 2) & 1);
+}
+
+// MFMA operand fragment of tile columns blk .. blk + 32, k-group kg, from a
+// K-major panel (RB bytes per row): lane l gets column blk + l % 32 and the
+// fragment's consecutive k. bf16: each 16-lane group g takes columns
+// blk + 16 (g % 2) .. + 16, k from 16 kg + 8 (g / 2), four per transpose read
+// (lane t addresses row k0 + t / 4, columns c0 + 4 (t % 4) .. + 4, and
+// receives column c0 + t of rows k0 .. k0 + 3). f32: k = 8 kg + 4 (l / 32) + e.
+template <typename T, int RB>
+__device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region, int lane, int blk, int kg) {
+    constexpr int ES = sizeof(T);
+    auto at = [&](int k, int c) -> const char * {
+        const int byte = c * ES;
+        return region + k * RB + ((((byte >> 4) ^ swq<ES>(k))) << 4) + (byte & 15);
+    };
+    if constexpr (ES == 2) {
+        const int t = lane & 15, g = lane >> 4;
+        const int c0 = blk + 16 * (g & 1), k0 = 16 * kg + 8 * (g >> 1);
+        s16x4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (NSQ_LDS s16x4 *)at(k0 + 4 * h + (t >> 2), c0 + 4 * (t & 3)));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        return __builtin_bit_cast(typename Mfma<T>::frag, w);
+    } else {
+        const int c = blk + (lane & 31), k0 = 8 * kg + 4 * (lane >> 5);
+        typename Mfma<T>::frag f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = *reinterpret_cast<const float *>(at(k0 + e, c));
+        return f;
+    }
+}
+
 // Rounding is spelled out wherever a product meets a sum (an explicit fused
 // multiply-add here, separate rounded multiply and add in the epilogue), so
 // that no tile configuration's instruction choice can change a result bit.
@@ -310,11 +360,13 @@ __device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s
 
 // acc += P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
 // first operand row; ldp, ldq are row strides in bytes; `extent_*` is the byte
-// size the buffer resources may address from P and Q. SEED: P holds rows
+// size the buffer resources may address from P and Q. QK: Q is K-major
+// instead, a row-major matrix with K along its rows (C = P Q): Q points at its
+// row 0, tile column 0, and stage kb reads its rows kb KW .. kb KW + KW. SEED: P holds rows
 // row0 .. row0 + BM of a matrix whose tile at (row0, c0) is to be added, times
 // s_seed; stages seed_kb .. seed_kb + BM / KW carry its columns, and each wave
 // adds its part while such a stage is resident (seed_from_stage).
-template <typename T, class C, bool SEED = false>
+template <typename T, class C, bool SEED = false, bool QK = false>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
                                              int extent_q, int nk, char *lds, f32x16 (&acc)[C::NBM][C::NBN],
                                              int seed_kb = 0, float s_seed = 0.f) {
@@ -336,6 +388,18 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         voff_p[i] = row * ldp + chunk;
         voff_q[i] = row * ldq + chunk;
     }
+    // K-major Q: a 1 KiB wave load covers RPQ panel rows of UPR units; each
+    // wave loads KW / WAVES consecutive rows (the same LDS bytes as a P slice)
+    constexpr int ES = sizeof(T), KW = ROWB / ES, RB = C::BM * ES, UPR = RB / 16, RPQ = 64 / UPR;
+    static_assert(!QK || (KW % C::WAVES == 0 && (KW / C::WAVES) == C::LOADS * RPQ), "K-major Q slices");
+    if constexpr (QK) {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int k = wave * (KW / C::WAVES) + i * RPQ + lane / UPR;
+            voff_q[i] = k * ldq + (((lane % UPR) ^ swq<ES>(k)) << 4);
+        }
+    }
+    const int q_stage = QK ? KW * ldq : ROWB;   // byte step of Q per stage
     const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
     // This wave's loads of stage kb: rows [wave RPW, (wave + 1) RPW) of both
     // panels into ring buffer kb % NBUF, 1 KiB per instruction.
@@ -348,7 +412,7 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)(sp + C::PANEL + i * C::RPI * ROWB), 16,
-                                                     (int)voff_q[i], kb * ROWB, 0, 0);
+                                                     (int)voff_q[i], kb * q_stage, 0, 0);
     };
     // Wait until this wave's loads of the current stage have landed, leaving
     // the n stages issued after it in flight.
@@ -381,7 +445,9 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
 #pragma unroll
         for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, 0);
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j) fb[0][j] = operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, 0);
+        for (int j = 0; j < C::NBN; ++j)
+            fb[0][j] = QK ? kmajor_frag<T, RB>(sq, lane, b_blk + 32 * j, 0)
+                          : operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, 0);
 #pragma unroll
         for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
@@ -391,7 +457,8 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
                     fa[nb][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, kg + 1);
 #pragma unroll
                 for (int j = 0; j < C::NBN; ++j)
-                    fb[nb][j] = operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, kg + 1);
+                    fb[nb][j] = QK ? kmajor_frag<T, RB>(sq, lane, b_blk + 32 * j, kg + 1)
+                                   : operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
@@ -609,7 +676,7 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
 //   kSyrkX : A = X X^T                          P = X, Q = X     upper tiles, mirrored
 //   kSyrkA : B' = s_final (s_init A + A A^T) + s_diag I
 //                                               P = A, Q = A     upper tiles, mirrored
-//   kGemmBX: X' = B' X                          P = B', Q = X^T  writes X' and X'^T
+//   kGemmBX: X' = B' X                          P = B', Q = X read K-major
 // The step X' = a X + B X with B = b A + c A A is computed as X' = B' X with
 // B' = a I + B: the a X term becomes a on B's diagonal (added in fp32 before
 // B' is rounded), so the B X product needs no old tile. The A A product's
@@ -682,16 +749,27 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         } else {
             init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
         }
-    } else if constexpr (MODE == kGemmBX) {
+    } else if constexpr (MODE == kGemmBX || MODE == kGramOut) {
+        // B' X, or Q X0 in the Gram space: X read K-major, as stored, or (B' X
+        // with a long K) the rows of the stored X^T
         zero_acc<C>(acc);
-        const int ldb = ldt * ES, ldq = ldxt * ES;
-        tile_product<T, C>(B + (int64_t)row0 * ldb, xtc + (int64_t)col0 * ldq, ldb, ldq, BM * ldb, BM * ldq,
-                           mp * ES / C::ROWB, lds, acc);
-    } else {   // Gram-space products, all with K = mp
+        char *P = MODE == kGemmBX ? B : qc;
+        const int ldp = ldt * ES;
+        if (MODE == kGramOut || pr.kmajor) {
+            char *X = MODE == kGemmBX ? xc : pr.x0;
+            const int ldq = ldx * ES;
+            tile_product<T, C, false, true>(P + (int64_t)row0 * ldp, X + (int64_t)col0 * ES, ldp, ldq, BM * ldp,
+                                            mp * ldq - col0 * ES, mp * ES / C::ROWB, lds, acc);
+        } else {
+            const int ldq = ldxt * ES;
+            tile_product<T, C>(P + (int64_t)row0 * ldp, xtc + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
+                               mp * ES / C::ROWB, lds, acc);
+        }
+    } else {   // the other Gram-space products, all with K = mp
         char *qtc = cur ? pr.qt1 : pr.qt0;
         char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
-        char *Q = MODE == kGramQG ? pr.g : MODE == kGramOut ? pr.xt0 : qtc;   // G symmetric; else K-major transposes
-        const int ldp = ldt * ES, ldq = (MODE == kGramOut ? ldxt : ldt) * ES;
+        char *Q = MODE == kGramQG ? pr.g : qtc;   // G symmetric; else the transposes kept for this
+        const int ldp = ldt * ES, ldq = ldt * ES;
         zero_acc<C>(acc);
         tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
                            mp * ES / C::ROWB, lds, acc);
@@ -762,7 +840,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
             store16<T>(D, (int64_t)(row0 + r) * ldd + col0 + c, w);
         }
         // column-major: the mirror tile at (col0, row0), or the transpose
-        if (writes_transpose(MODE) || (symmetric_mode(MODE) && tr.ti != tr.tj)) {
+        if (writes_transpose(MODE) || (MODE == kGemmBX && !pr.kmajor) || (symmetric_mode(MODE) && tr.ti != tr.tj)) {
             char *qtn = cur ? pr.qt0 : pr.qt1;
             char *E = MODE == kGemmBX ? xtn : MODE == kGramTQ ? pr.at : MODE == kGramB0 || MODE == kGramBQ ? qtn : D;
             const int lde = MODE == kGemmBX ? ldxt : ldt;
@@ -792,14 +870,15 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 }
 
 // Input staging, one kPrepTile x kPrepTile tile of X (m x n, oriented) per
-// workgroup: the input G goes unscaled into X0 and its transpose into X0^T
-// (zero in the padding), and the tile's fp32 sum of squares goes to
-// partials[ti * (np / kPrepTile) + tj], summed in a fixed order. The tile is read
-// as stored (rows of G; for a tall G those are columns of X), copied straight to
-// the matching workspace array with 16-byte stores, and staged in LDS (rows of
-// kPrepTile * es bytes, the 16-byte unit u of row r at unit position
-// u ^ 2 (r % 4)); the other array's rows come out of LDS with transpose reads
-// (bf16) or 4-byte reads (f32).
+// workgroup: the input G goes unscaled into X0, and into X0^T unless the
+// matrix is kmajor (zero in the padding), and the tile's fp32 sum of squares
+// goes to partials[ti * (np / kPrepTile) + tj], summed in a fixed order. The
+// tile is read as stored (rows of G; for a tall G those are columns of X),
+// copied straight to the matching array (X0, or X0^T for a tall G) with
+// 16-byte stores, and staged in LDS (rows of kPrepTile * es bytes, the 16-byte
+// unit u of row r at unit position u ^ 2 (r % 4)) when the other array is
+// kept; that array's rows come out of LDS with transpose reads (bf16) or
+// 4-byte reads (f32).
 //
 // This is the first kernel of a call: its descriptor and tile list are read
 // from the pinned host staging buffer, and the workgroups also copy the whole
@@ -843,6 +922,7 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
     char *direct = tall ? pr.xt0 : pr.x0;                 // receives the tile as stored
     char *trans = tall ? pr.x0 : pr.xt0;                  // receives its transpose
     const int ld_direct = tall ? pr.ldxt : pr.ldx, ld_trans = tall ? pr.ldx : pr.ldxt;
+    const bool do_direct = direct != nullptr, do_trans = trans != nullptr;   // X0^T is absent when kmajor
     const bool vec_in = pr.vec_in;
     float ss = 0.f;
 #pragma unroll
@@ -873,8 +953,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
             ss = __builtin_fmaf(fv[e], fv[e], ss);
         }
         if constexpr (UPL == 1) {
-            store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
-            *reinterpret_cast<i32x4 *>(lds + r * RB + ((u ^ (2 * (r & 3))) << 4)) = w;
+            if (do_direct) store16<T>(direct, (int64_t)gr * ld_direct + gc, w);
+            if (do_trans) *reinterpret_cast<i32x4 *>(lds + r * RB + ((u ^ (2 * (r & 3))) << 4)) = w;
         } else {   // exact widening to the workspace type, 16 bytes at a time
 #pragma unroll
             for (int h = 0; h < UPL; ++h) {
@@ -883,8 +963,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
                 for (int e = 0; e < 16 / ES; ++e) wv[e] = (T)fv[h * (16 / ES) + e];
                 i32x4 o;
                 __builtin_memcpy(&o, wv, 16);
-                store16<T>(direct, (int64_t)gr * ld_direct + gc + h * (16 / ES), o);
-                *reinterpret_cast<i32x4 *>(lds + r * RB + (((u * UPL + h) ^ (2 * (r & 3))) << 4)) = o;
+                if (do_direct) store16<T>(direct, (int64_t)gr * ld_direct + gc + h * (16 / ES), o);
+                if (do_trans) *reinterpret_cast<i32x4 *>(lds + r * RB + (((u * UPL + h) ^ (2 * (r & 3))) << 4)) = o;
             }
         }
     }
@@ -897,6 +977,7 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         __syncthreads();
     }
     if (threadIdx.x == 0) pr.partials[tr.ti * (pr.np / TE) + tr.tj] = red[0];
+    if (!do_trans) return;
 
     // transpose: output row c (tile column), 16 bytes = ET consecutive tile rows
     constexpr int ET = 16 / ES;
@@ -965,6 +1046,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
+    bool kmajor;       // B X reads X K-major; no X^T arrays
     int64_t nparts, syrk_tiles, gemm_tiles;
     int64_t sq_tiles;  // full m x m grid (Gram-space products only)
     int64_t npieces;   // row pieces its input / output is split into
@@ -976,19 +1058,29 @@ using PieceLists = std::vector<std::vector<RowPiece>>;
 
 // Row strides (elements) and array sizes of one matrix's workspace.
 inline int64_t ld_x(const MatInfo &mi, int64_t es) { return mi.np + kRowPadBytes / es; }
-inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }   // A, B and X^T
+inline int64_t ld_t(const MatInfo &mi, int64_t es) { return mi.mp + kRowPadBytes / es; }   // m x m arrays
 inline size_t x_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_x(mi, es) * es)); }
 inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.np * ld_t(mi, es) * es)); }
 inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
 
-// gram: the Gram-space workspace (fp32 X0, X0^T, G, Q ping/pong, Q G, A, B)
-// instead of the NS one (X and X^T ping/pong, A, B in the input's type).
+// B X reads X K-major (through LDS transpose reads) when its K is at most
+// this: the X'^T stores it saves outweigh its slower operand loads only for
+// short main loops. NS_KMAJOR_MAX overrides (tuning; both ways give the same
+// bits). The Gram-space output product always reads X0 K-major.
+int64_t kmajor_max_k() {
+    if (const char *env = getenv("NS_KMAJOR_MAX")) return atoll(env);
+    return 1024;
+}
+
+// gram: the Gram-space workspace (fp32 X0, G, Q and Q^T ping/pong, Q G, A,
+// A^T, B') instead of the NS one (X ping/pong, A, B' in the input's type).
 ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vector<MatInfo> &info,
                    bool gram = false) {
     if (n < 0) return fail(NS_ERR_INVALID_ARG, "n = %d < 0", n);
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
     if (dtype != NS_BF16 && dtype != NS_F32) return fail(NS_ERR_DTYPE, "dtype %d", (int)dtype);
     const int64_t es = gram ? 4 : dtype == NS_BF16 ? 2 : 4;   // workspace element size
+    const int64_t kmax = kmajor_max_k();
     info.assign(n, MatInfo{});
     for (int32_t i = 0; i < n; ++i) {
         MatInfo &mi = info[i];
@@ -1014,8 +1106,9 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.sq_tiles = gram ? tm * tm : 0;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.npieces = 1;
-        mi.buf_bytes = gram ? x_bytes(mi, es) + xt_bytes(mi, es) + 9 * a_bytes(mi, es)
-                            : 2 * x_bytes(mi, es) + 2 * xt_bytes(mi, es) + 2 * a_bytes(mi, es);
+        mi.kmajor = gram || mi.mp <= kmax;
+        mi.buf_bytes = gram ? x_bytes(mi, es) + 9 * a_bytes(mi, es)
+                            : 2 * x_bytes(mi, es) + (mi.kmajor ? 0 : 2 * xt_bytes(mi, es)) + 2 * a_bytes(mi, es);
     }
     return NS_OK;
 }
@@ -1157,18 +1250,19 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
-        const size_t xb = x_bytes(mi, es), xtb = xt_bytes(mi, es), ab = a_bytes(mi, es);
+        const size_t xb = x_bytes(mi, es), xtb = mi.kmajor ? 0 : xt_bytes(mi, es), ab = a_bytes(mi, es);
         if (!gram) {
             p.x0 = base;
             p.x1 = p.x0 + xb;
-            p.xt0 = p.x1 + xb;
-            p.xt1 = p.xt0 + xtb;
-            p.a = p.xt1 + xtb;
+            if (!mi.kmajor) {
+                p.xt0 = p.x1 + xb;
+                p.xt1 = p.xt0 + xtb;
+            }
+            p.a = p.x1 + xb + 2 * xtb;
             p.b = p.a + ab;
-        } else {   // X0, X0^T, G, Q and Q^T ping/pong, Q G, A, A^T, B'
+        } else {   // X0, G, Q and Q^T ping/pong, Q G, A, A^T, B'
             p.x0 = base;
-            p.xt0 = p.x0 + xb;
-            p.g = p.xt0 + xtb;
+            p.g = p.x0 + xb;
             p.q0 = p.g + ab;
             p.q1 = p.q0 + ab;
             p.qt0 = p.q1 + ab;
@@ -1198,6 +1292,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         p.ldx = (int32_t)ld_x(mi, es);
         p.ldt = (int32_t)ld_t(mi, es);
         p.ldxt = (int32_t)ld_t(mi, es);
+        p.kmajor = mi.kmajor;
         p.tall = mi.tall;
         p.nparts = (int32_t)mi.nparts;
         const int32_t pid = (int32_t)probs.size();

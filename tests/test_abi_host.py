@@ -180,6 +180,9 @@ def test_workspace_and_batched_errors():
     assert b > mb > 0
     one, _ = nsq.ns_workspace_bytes([(1024, 1024)], nsq.NS_BF16)
     assert b > 2 * (one - 4096)
+    # X ping/pong, A and B', rows padded by 256 bytes, plus tables (no X^T)
+    arrays = 4 * 1024 * (1024 * 2 + 256)
+    assert arrays <= one < arrays + (1 << 20)
     # f32 needs about twice the buffers
     b32, _ = nsq.ns_workspace_bytes([(1024, 1024)], nsq.NS_F32)
     assert b32 > 1.8 * one       # fixed 256-byte row pad is not doubled
@@ -325,9 +328,10 @@ def test_route_plan_axis_errors():
 
 def test_gram_workspace_and_errors():
     b, mb = nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_BF16)
-    # fp32: X0 (1024 x 4096) + X0^T + nine 1024 x 1024 arrays, rows padded by 256 bytes
-    one = 1024 * (4096 * 4 + 256) + 4096 * (1024 * 4 + 256) + 9 * 1024 * (1024 * 4 + 256)
+    # fp32: X0 (1024 x 4096) + nine 1024 x 1024 arrays, rows padded by 256 bytes
+    one = 1024 * (4096 * 4 + 256) + 9 * 1024 * (1024 * 4 + 256)
     assert mb >= one and b >= 2 * one
+    assert mb < one + (1 << 20)      # plus tables only
     assert b == nsq.ns_gram_workspace_bytes([(1024, 4096)] * 2, nsq.NS_F32)[0]
     lib = nsq.lib()
     sh = _lib._shapes([(4, 4)])

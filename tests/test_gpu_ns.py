@@ -187,10 +187,38 @@ def test_routed_equals_unrouted_bitwise():
         assert np.array_equal(to_host(shards[s], "bf16"), np.concatenate(want))
 
 
+# m > 1024: B X reads the stored X^T (the K-major read is kept for short K)
+LONG_K = [(1100, 1300), (1300, 1100), (300, 700)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_k_parity(dtype):
+    std = 0.02 if dtype == "bf16" else 1.0
+    hosts = [host_matrix(17, i, s, std=std, dtype=dtype) for i, s in enumerate(LONG_K)]
+    log(f"ns: long-K batch {dtype} {LONG_K}")
+    _check(hosts, dtype, _run_gpu(hosts, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_b_x_operand_layout_does_not_change_bits(dtype, monkeypatch):
+    """B X reads X either K-major (LDS transpose reads) or as the stored X^T's
+    rows: the same products in the same order, so the same bits."""
+    std = 0.02 if dtype == "bf16" else 1.0
+    shapes = [(1100, 1300), (1300, 1100), (700, 500), (64, 64)]
+    hosts = [host_matrix(18, i, s, std=std, dtype=dtype) for i, s in enumerate(shapes)]
+    log(f"ns: K-major vs X^T operand {dtype}")
+    monkeypatch.setenv("NS_KMAJOR_MAX", "0")
+    stored = _run_gpu(hosts, dtype)
+    monkeypatch.setenv("NS_KMAJOR_MAX", "100000")
+    kmajor = _run_gpu(hosts, dtype)
+    for x, y in zip(stored, kmajor):
+        assert np.array_equal(x, y)
+
+
 def test_tile_size_does_not_change_bits(monkeypatch):
     """The product tile (256 or 128, picked per call from the batch's size) must
     not change a matrix's bits: batch invariance across tile choices."""
-    shapes = [(1024, 1024), (512, 1536), (1536, 512), (300, 700)]
+    shapes = [(1024, 1024), (512, 1536), (1536, 512), (300, 700), (1100, 1300)]
     hosts = [host_matrix(16, i, s) for i, s in enumerate(shapes)]
     log("ns: 256 vs 128 product tiles")
     monkeypatch.setenv("NS_TILE", "256")
