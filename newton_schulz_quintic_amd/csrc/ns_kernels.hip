@@ -199,7 +199,8 @@ constexpr bool writes_transpose(int mode) {
 }
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
-// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks. K is staged in
+// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks (rows
+// wm BM/WM .., column blocks col_blk(wn, 0 ..)). K is staged in
 // panels of ROWB bytes per row, in a ring of NBUF stage buffers.
 template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
     static constexpr int BM = BM_, WM = WM_, WN = WN_, ROWB = ROWB_, NBUF = NBUF_;
@@ -215,6 +216,10 @@ template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
     static constexpr int LOADS = RPW / RPI;     // loads per wave per panel
     static constexpr int KG = ROWB / 32;        // k-groups (one 32-byte MFMA K step each) per stage
     static_assert(ROWB == 64 || ROWB == 128, "panel row size");
+    // First tile column of the wave's column block j: the blocks of a wave
+    // are WN apart, so a K stage (64 bf16 columns) holds blocks of several
+    // waves and the A A product's seed work of one stage is spread over them.
+    static __device__ __forceinline__ int col_blk(int wn, int j) { return (j * WN + wn) * 32; }
     static_assert(RPW % RPI == 0, "each wave loads whole row groups");
     static_assert(NBUF >= 2 && NBUF <= 5, "ring depth");
 };
@@ -316,8 +321,8 @@ __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region
 //
 // acc += s * P[r][k0 + c] for the accumulator blocks whose 32 columns lie in
 // the P stage `sp` (stage columns k0 .. k0 + KW, KW = ROWB / es), where the
-// tile's column c0 + wn BM/WN + 32 j maps to stage column
-// (wn BM/WN + 32 j) % KW when (wn BM/WN + 32 j) / KW == rel. Reads four
+// tile's column c0 + col_blk(wn, j) maps to stage column
+// col_blk(wn, j) % KW when col_blk(wn, j) / KW == rel. Reads four
 // consecutive rows of one column per lane: bf16 by LDS transpose reads (in
 // each 16-lane group lane t addresses row r0 + t / 4, columns c0 + 4 (t % 4)
 // .. + 4, and receives column c0 + t, rows r0 .. r0 + 3), f32 by four 4-byte
@@ -333,7 +338,7 @@ __device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s
     };
 #pragma unroll
     for (int j = 0; j < C::NBN; ++j) {
-        const int cj = wn * (C::BM / C::WN) + 32 * j;
+        const int cj = C::col_blk(wn, j);
         if (cj / KW != rel) continue;
         const int kc = cj % KW;
 #pragma unroll
@@ -400,7 +405,7 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         }
     }
     const int q_stage = QK ? KW * ldq : ROWB;   // byte step of Q per stage
-    const int a_blk = wm * (C::BM / C::WM), b_blk = wn * (C::BM / C::WN);
+    const int a_blk = wm * (C::BM / C::WM);
     // This wave's loads of stage kb: rows [wave RPW, (wave + 1) RPW) of both
     // panels into ring buffer kb % NBUF, 1 KiB per instruction.
     auto issue = [&](int kb) {
@@ -446,8 +451,8 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, 0);
 #pragma unroll
         for (int j = 0; j < C::NBN; ++j)
-            fb[0][j] = QK ? kmajor_frag<T, RB>(sq, lane, b_blk + 32 * j, 0)
-                          : operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, 0);
+            fb[0][j] = QK ? kmajor_frag<T, RB>(sq, lane, C::col_blk(wn, j), 0)
+                          : operand_frag<T, ROWB>(sq, lane, C::col_blk(wn, j), 0);
 #pragma unroll
         for (int kg = 0; kg < C::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
@@ -457,8 +462,8 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
                     fa[nb][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, kg + 1);
 #pragma unroll
                 for (int j = 0; j < C::NBN; ++j)
-                    fb[nb][j] = QK ? kmajor_frag<T, RB>(sq, lane, b_blk + 32 * j, kg + 1)
-                                   : operand_frag<T, ROWB>(sq, lane, b_blk + 32 * j, kg + 1);
+                    fb[nb][j] = QK ? kmajor_frag<T, RB>(sq, lane, C::col_blk(wn, j), kg + 1)
+                                   : operand_frag<T, ROWB>(sq, lane, C::col_blk(wn, j), kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
@@ -627,7 +632,7 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int rb = wm * (C::BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
-                const int cb = wn * (C::BM / C::WN) + j * 32;
+                const int cb = C::col_blk(wn, j);
                 float old[4];
                 if constexpr (ES == 2) {
                     const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & 1);
@@ -777,7 +782,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
 
     // Epilogue, part 1: scaling, rounding, staging. Accumulator element
     // (i, j, v) of this lane sits at tile row wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32)
-    // + v%4 and tile column wn*BM/WN + 32 j + lane%32. The tile is staged in
+    // + v%4 and tile column col_blk(wn, j) + lane%32. The tile is staged in
     // the type it is stored in: the workspace type, or the output's.
     typedef typename std::conditional<LAST, TO, T>::type TS;
     constexpr int SES = sizeof(TS);
@@ -789,7 +794,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
     for (int i = 0; i < C::NBM; ++i) {
 #pragma unroll
         for (int j = 0; j < C::NBN; ++j) {
-            const int c = wn * (BM / C::WN) + j * 32 + (lane & 31);
+            const int c = C::col_blk(wn, j) + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
