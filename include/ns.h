@@ -347,15 +347,17 @@ ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *
  * ------------------------------------------------------------------------ */
 
 /* Kernel timing: for the kinds enabled (bit k of `kinds` enables kind k;
- * -1 enables all, 0 disables), the library records a HIP event pair on the
- * launch stream around every launch of that kind. Each pair adds a little
- * time to the stream, so enable only the kinds being measured. Enabling
+ * -1 enables all, 0 disables), every launch of that kind goes out through
+ * hipExtLaunchKernelGGL with a HIP event pair that its dispatch records, so a
+ * pair spans that kernel's execution only (what rocprofv3's kernel trace
+ * reports), not its dispatch. Enable only the kinds being measured. Enabling
  * creates a pool of 4096 events up front (so no measured loop pays for event
  * creation); it needs the GPU and returns NS_ERR_HIP if event creation fails.
  * ns_timing_read waits for the events of one kind, returns their sums and
  * clears them. Not thread-safe against concurrent batched calls.
  * kind: 0 = the B X product kernel (every step but the last),
- *       1 = pack/unpack kernel, 2 = norm kernels (partial + apply, one pair),
+ *       1 = pack/unpack kernel, 2 = input staging (with steps = 0, also the
+ *       scaling kernel after it),
  *       3 = the final B X launch of each call (it writes the caller's output),
  *       4 = the A = X X^T product kernel, 5 = the B = b A + c A A product kernel.
  * total_ms: summed durations; launches: number of launches; work: summed

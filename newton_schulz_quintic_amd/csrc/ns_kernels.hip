@@ -1210,29 +1210,29 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
 }
 
 template <typename T, class C>
-void launch_product(dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t nt,
-                    int32_t mode, int32_t cur, bool last, float s_init, float s_final, float s_diag,
-                    int32_t do_product,
-                    int32_t first, float eps, const RowPiece *pieces) {
+void launch_product(TimedScope &ts, dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles,
+                    int32_t nt, int32_t mode, int32_t cur, bool last, float s_init, float s_final, float s_diag,
+                    int32_t do_product, int32_t first, float eps, const RowPiece *pieces) {
     if (mode == kSyrkX)
-        hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+        ts.launch(ns_product_kernel<T, C, kSyrkX, false>, grid, dim3(C::THREADS), st, probs, tiles, nt, cur, s_init,
+                  s_final, s_diag, do_product, first, eps, pieces);
     else if (mode == kSyrkA)
-        hipLaunchKernelGGL((ns_product_kernel<T, C, kSyrkA, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+        ts.launch(ns_product_kernel<T, C, kSyrkA, false>, grid, dim3(C::THREADS), st, probs, tiles, nt, cur, s_init,
+                  s_final, s_diag, do_product, first, eps, pieces);
     else if (!last)
-        hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, false>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+        ts.launch(ns_product_kernel<T, C, kGemmBX, false>, grid, dim3(C::THREADS), st, probs, tiles, nt, cur, s_init,
+                  s_final, s_diag, do_product, first, eps, pieces);
     else
-        hipLaunchKernelGGL((ns_product_kernel<T, C, kGemmBX, true>), grid, dim3(C::THREADS), 0, st, probs,
-                           tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+        ts.launch(ns_product_kernel<T, C, kGemmBX, true>, grid, dim3(C::THREADS), st, probs, tiles, nt, cur, s_init,
+                  s_final, s_diag, do_product, first, eps, pieces);
 }
 
 template <typename T, class C, int MODE, bool LAST = false, typename TO = T>
-void launch_mode(int32_t nt, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t cur, float s_init,
-                 float s_final, float s_diag, int32_t do_product, int32_t first, float eps, const RowPiece *pieces) {
-    hipLaunchKernelGGL((ns_product_kernel<T, C, MODE, LAST, TO>), dim3((unsigned)nt), dim3(C::THREADS), 0, st, probs,
-                       tiles, nt, cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
+void launch_mode(TimedScope &ts, int32_t nt, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t cur,
+                 float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
+                 const RowPiece *pieces) {
+    ts.launch(ns_product_kernel<T, C, MODE, LAST, TO>, dim3((unsigned)nt), dim3(C::THREADS), st, probs, tiles, nt,
+              cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
 }
 
 // One group of matrices: tables, input staging, then the product launches.
@@ -1331,7 +1331,8 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         f_syrk_x += m * (m + 1) * n;                                            // X X^T, or G
         f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
         f_gemm += 2 * m * m * n;                                                // B X, or Q X0
-        norm_bytes += m * n * esi + 2.0 * (double)mi.mp * (double)mi.np * es;
+        // input read, X0 written (padded), and X0^T when it is kept
+        norm_bytes += m * n * esi + (mi.kmajor ? 1.0 : 2.0) * (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
 
@@ -1363,8 +1364,8 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     const int32_t npt = (int32_t)ptiles.size();
 
     {
-        TimedScope ts(kTimeNorm, st, norm_bytes);
-        hipLaunchKernelGGL((ns_prepare_kernel<TI, T>), dim3((unsigned)npt), dim3(kPrepThreads), 0, st,
+        TimedScope ts(kTimeNorm, norm_bytes);
+        ts.launch(ns_prepare_kernel<TI, T>, dim3((unsigned)npt), dim3(kPrepThreads), st,
                            reinterpret_cast<const NsProb *>(hdev),
                            reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
                            reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
@@ -1373,7 +1374,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         if ((sst = staging_release(slot, st, le == hipSuccess))) return sst;
         if (le != hipSuccess) return fail(NS_ERR_HIP, "launch failed: %s", hipGetErrorString(le));
         if (steps == 0)
-            hipLaunchKernelGGL(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), 0, st, d_probs,
+            ts.launch(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), st, d_probs,
                                d_ptiles, npt, eps, d_pieces);
     }
     NSQ_HIP(hipGetLastError());
@@ -1388,35 +1389,35 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                 double f_sq = 0;   // one full m x m product per matrix: 2 m^3
                 for (int32_t idx : group) f_sq += 2.0 * (double)info[idx].m * info[idx].m * info[idx].m;
                 {
-                    TimedScope ts(kTimeSyrkX, st, f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
-                    launch_mode<T, Small, kGramG>(nsy, st, d_probs, d_syrk, 0, 1.f, 1.f, ridge, 1, 1, eps, d_pieces);
+                    TimedScope ts(kTimeSyrkX, f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
+                    launch_mode<T, Small, kGramG>(ts, nsy, st, d_probs, d_syrk, 0, 1.f, 1.f, ridge, 1, 1, eps, d_pieces);
                 }
                 {
-                    TimedScope ts(kTimeSyrkA, st, fused ? f_sq : 0.0);   // Q1 = a I + b G + c G G
-                    launch_mode<T, Small, kGramB0>(nsq, st, d_probs, d_sq, 0, si, sf, a, prod, 0, eps, d_pieces);
+                    TimedScope ts(kTimeSyrkA, fused ? f_sq : 0.0);   // Q1 = a I + b G + c G G
+                    launch_mode<T, Small, kGramB0>(ts, nsq, st, d_probs, d_sq, 0, si, sf, a, prod, 0, eps, d_pieces);
                 }
                 NSQ_HIP(hipGetLastError());
                 int qcur = 1;
                 for (int32_t k = 1; k < steps; ++k) {
                     {
-                        TimedScope ts(kTimeProduct, st, 2 * f_sq);   // T = Q G, A = T Q (and A^T)
-                        launch_mode<T, Small, kGramQG>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
-                        launch_mode<T, Small, kGramTQ>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
+                        TimedScope ts(kTimeProduct, 2 * f_sq);   // T = Q G, A = T Q (and A^T)
+                        launch_mode<T, Small, kGramQG>(ts, nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
+                        launch_mode<T, Small, kGramTQ>(ts, nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
                     }
                     {
-                        TimedScope ts(kTimeSyrkA, st, fused ? f_sq : 0.0);   // B' = a I + b A + c A A
-                        launch_mode<T, Small, kGramAA>(nsq, st, d_probs, d_sq, qcur, si, sf, a, prod, 0, eps, d_pieces);
+                        TimedScope ts(kTimeSyrkA, fused ? f_sq : 0.0);   // B' = a I + b A + c A A
+                        launch_mode<T, Small, kGramAA>(ts, nsq, st, d_probs, d_sq, qcur, si, sf, a, prod, 0, eps, d_pieces);
                     }
                     {
-                        TimedScope ts(kTimeProduct, st, f_sq);   // Q' = B' Q (and Q'^T)
-                        launch_mode<T, Small, kGramBQ>(nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
+                        TimedScope ts(kTimeProduct, f_sq);   // Q' = B' Q (and Q'^T)
+                        launch_mode<T, Small, kGramBQ>(ts, nsq, st, d_probs, d_sq, qcur, 1.f, 1.f, 0.f, 1, 0, eps, d_pieces);
                     }
                     NSQ_HIP(hipGetLastError());
                     qcur ^= 1;
                 }
                 {
-                    TimedScope ts(kTimeFinal, st, f_gemm);   // out = s Q X0
-                    launch_mode<T, Small, kGramOut, true, TI>(nge, st, d_probs, d_gemm, qcur, 1.f, 1.f, 0.f, 1, 1,
+                    TimedScope ts(kTimeFinal, f_gemm);   // out = s Q X0
+                    launch_mode<T, Small, kGramOut, true, TI>(ts, nge, st, d_probs, d_gemm, qcur, 1.f, 1.f, 0.f, 1, 1,
                                                               eps, d_pieces);
                 }
                 NSQ_HIP(hipGetLastError());
@@ -1441,19 +1442,19 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
             const bool last = mode == kGemmBX && s == steps - 1;
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
-            TimedScope ts(kind, st, work[mode]);
+            TimedScope ts(kind, work[mode]);
             const float s_init = mode == kSyrkA ? sa_init : 1.f;
             const float s_final = mode == kSyrkA ? sa_final : 1.f;
             const float s_diag = mode == kSyrkA ? a : 0.f;
             const int32_t do_product = mode == kSyrkA ? sa_product : 1;
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
-                    launch_product<T, Big>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
+                    launch_product<T, Big>(ts, dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
                                            s_diag, do_product, s == 0, eps, d_pieces);
                     continue;
                 }
             }
-            launch_product<T, Small>(dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
+            launch_product<T, Small>(ts, dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
                                      s_diag, do_product, s == 0, eps, d_pieces);
         }
         NSQ_HIP(hipGetLastError());

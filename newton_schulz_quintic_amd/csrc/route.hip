@@ -227,14 +227,14 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
     const int64_t per = (plan->total_chunks + kRouteMaxGrid - 1) / kRouteMaxGrid;   // chunks per workgroup
     const int64_t grid = (plan->total_chunks + per - 1) / per;
     {
-        TimedScope ts(kTimeRoute, st, 2.0 * (double)plan->total_bytes);
+        TimedScope ts(kTimeRoute, 2.0 * (double)plan->total_bytes);
         const RouteSeg *table = reinterpret_cast<const RouteSeg *>(plan->device_table);
         if (plan->total_bytes > kMallBytes)
-            hipLaunchKernelGGL(route_copy_kernel<true>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
-                               (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
+            ts.launch(route_copy_kernel<true>, dim3((unsigned)grid), dim3(kRouteThreads), st, table,
+                      (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
         else
-            hipLaunchKernelGGL(route_copy_kernel<false>, dim3((unsigned)grid), dim3(kRouteThreads), 0, st, table,
-                               (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
+            ts.launch(route_copy_kernel<false>, dim3((unsigned)grid), dim3(kRouteThreads), st, table,
+                      (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
     }
     NSQ_HIP(hipGetLastError());
     return NS_OK;

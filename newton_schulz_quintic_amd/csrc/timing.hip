@@ -1,5 +1,6 @@
 // Kernel timing hooks (ns_timing_enable / ns_timing_read): HIP event pairs
-// recorded on the launch stream around the library's own kernel launches.
+// recorded by the library's own kernel dispatches (hipExtLaunchKernelGGL), one
+// pair per timed launch.
 
 #include <mutex>
 #include <vector>
@@ -32,26 +33,30 @@ hipEvent_t take_event() {
 }
 }  // namespace
 
-bool timing_enabled() {
+bool timing_on(int kind) {
     std::lock_guard<std::mutex> lk(g_mu);
-    return g_mask != 0;
+    return kind >= 0 && kind < kTimeKinds && (g_mask & (1u << kind));
 }
 
-int timing_start(int kind, hipStream_t stream, double work) {
+int timing_pair(int kind, double work, hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (kind < 0 || kind >= kTimeKinds || !(g_mask & (1u << kind))) return -1;
     Rec r{take_event(), take_event(), kind, work, false};
-    if (!r.start || !r.stop) return -1;
-    if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
+    if (!r.start || !r.stop) {
+        if (r.start) g_pool.push_back(r.start);
+        if (r.stop) g_pool.push_back(r.stop);
+        return -1;
+    }
     g_recs.push_back(r);
+    *start = r.start;
+    *stop = r.stop;
     return (int)g_recs.size() - 1;
 }
 
-void timing_stop(int slot, hipStream_t stream) {
+void timing_close(int slot, bool ok) {
     if (slot < 0) return;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (slot >= (int)g_recs.size()) return;
-    if (hipEventRecord(g_recs[slot].stop, stream) == hipSuccess) g_recs[slot].closed = true;
+    if (slot < (int)g_recs.size()) g_recs[slot].closed = ok;
 }
 
 }  // namespace nsq
