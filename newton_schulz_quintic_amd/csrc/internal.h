@@ -55,6 +55,7 @@ struct ns_route_plan {
     std::vector<nsq::RouteSeg> segs;
     int64_t total_chunks = 0;
     int64_t total_bytes = 0;
+    bool aligned16 = false;   // every piece starts (and every run and stride is) a multiple of 16 bytes
     uint64_t fingerprint = 0;
     void *device_table = nullptr;
 };

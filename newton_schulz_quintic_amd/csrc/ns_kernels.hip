@@ -563,6 +563,18 @@ __device__ __forceinline__ void store16(char *base, int64_t elem, i32x4 w) {
     *(NSQ_GLOBAL i32x4 *)(base + elem * (int64_t)sizeof(T)) = w;
 }
 
+// 16 bytes at an address aligned only to the element size: one access in the
+// GPU's unaligned access mode (caller tensors at arbitrary element offsets).
+typedef i32x4 __attribute__((aligned(2))) i32x4_a2;   // 16 bytes, 2-byte alignment
+template <typename T>
+__device__ __forceinline__ i32x4 load16_unaligned(const char *p) {
+    return *(const NSQ_GLOBAL i32x4_a2 *)p;
+}
+template <typename T>
+__device__ __forceinline__ void store16_unaligned(char *p, i32x4 w) {
+    *(NSQ_GLOBAL i32x4_a2 *)p = w;
+}
+
 // Bounds-checked store of the 16 / es elements of chunk w at [row][col] of the
 // caller's output (rows x cols as stored, rows spread over pieces).
 template <typename T>
@@ -572,8 +584,9 @@ __device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowP
     if (row >= rows || col >= cols) return;
     const RowPiece pc = find_piece(band, nband, row);
     char *dst = pc.out + (row - pc.row0) * pc.ld_out * (int64_t)sizeof(T);
-    if (pr.vec_out && col + E <= cols) {
-        store16<T>(dst, col, w);
+    if (col + E <= cols) {
+        if (pr.vec_out) store16<T>(dst, col, w);
+        else store16_unaligned<T>(dst + col * (int64_t)sizeof(T), w);
         return;
     }
     T vals[E];
@@ -940,8 +953,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
             RowPiece pc = one;   // by value: the reads below stay global loads
             if (multi) pc = find_piece(band, tr.npiece, gr);
             const char *src = pc.in + ((gr - pc.row0) * pc.ld_in + gc) * EI;
-            if (vec_in && gc + E <= cols) {
-                w = *(const NSQ_GLOBAL i32x4 *)src;
+            if (gc + E <= cols) {
+                w = vec_in ? *(const NSQ_GLOBAL i32x4 *)src : load16_unaligned<TI>(src);
             } else {
                 TI vals[E];
 #pragma unroll

@@ -261,11 +261,15 @@ static ns_status route_plan_build(int32_t n, const ns_shape *shapes, int32_t num
             return bad(fail(NS_ERR_OVERFLOW, "buffer byte size overflows"));
     }
     int64_t chunks = 0, bytes = 0;
+    bool aligned = true;
     for (RouteSeg &g : plan->segs) {
         g.chunk_begin = chunks;
         chunks += (g.len + kRouteChunkBytes - 1) / kRouteChunkBytes;
         bytes += g.len;
+        aligned = aligned && (g.shard_off | g.home_off) % 16 == 0 &&
+                  (g.run_len == g.len || (g.run_len | g.home_stride) % 16 == 0);
     }
+    plan->aligned16 = aligned;
     plan->total_chunks = chunks;
     plan->total_bytes = bytes;
 

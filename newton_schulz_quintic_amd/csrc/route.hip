@@ -36,7 +36,10 @@ struct PtrSet {
     char *p[NS_MAX_SHARDS];
 };
 
-template <bool NT>
+// UA: the misaligned branch moves 16 bytes per access (plans with a piece or
+// a buffer off 16-byte alignment); otherwise it moves 2 bytes per access, which
+// keeps the aligned kernel's register budget (64, eight waves per SIMD).
+template <bool NT, bool UA>
 __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict__ dst, int64_t len) {
     const int t = threadIdx.x;
     const uintptr_t mis = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
@@ -67,14 +70,41 @@ __device__ inline void copy_chunk(const char *__restrict__ src, char *__restrict
         }
         for (int64_t i = (n16 << 4) + 2 * t; i < len; i += 2 * kRouteThreads)
             *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
-    } else if ((mis & 3) == 0) {
-        const int64_t n4 = len >> 2;
-        for (int64_t i = t; i < n4; i += kRouteThreads)
-            reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(src)[i];
-        for (int64_t i = (n4 << 2) + 2 * t; i < len; i += 2 * kRouteThreads)
+    } else if constexpr (!UA) {
+        for (int64_t i = 2 * t; i < len; i += 2 * kRouteThreads)
             *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
     } else {
-        for (int64_t i = 2 * t; i < len; i += 2 * kRouteThreads)
+        // Ends 2-byte aligned (elements are 2 or 4 bytes): a 2-byte head up to
+        // the first 16-byte boundary of dst, then 16-byte stores fed by
+        // 16-byte loads at src's own alignment (the GPU's unaligned access
+        // mode serves them as one load; four per thread in flight), then a
+        // 2-byte tail. Every access stays inside [src, src + len).
+        const int n = (int)len;   // a chunk: at most kRouteChunkBytes
+        const int head = min(n, (int)((16 - (reinterpret_cast<uintptr_t>(dst) & 15)) & 15));
+        if (2 * t < head)
+            *reinterpret_cast<uint16_t *>(dst + 2 * t) = *reinterpret_cast<const uint16_t *>(src + 2 * t);
+        const char *s = src + head;
+        char *d = dst + head;
+        const int n16 = (n - head) >> 4;
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        typedef v4i __attribute__((aligned(2))) v4i_u;   // 16 bytes at 2-byte alignment
+        for (int i0 = t; i0 < n16; i0 += 4 * kRouteThreads) {
+            v4i v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * kRouteThreads;
+                if (i < n16) v[k] = *reinterpret_cast<const v4i_u *>(s + 16 * i);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * kRouteThreads;
+                if (i < n16) {
+                    if constexpr (NT) __builtin_nontemporal_store(v[k], reinterpret_cast<v4i *>(d + 16 * i));
+                    else *reinterpret_cast<v4i *>(d + 16 * i) = v[k];
+                }
+            }
+        }
+        for (int i = head + (n16 << 4) + 2 * t; i < n; i += 2 * kRouteThreads)
             *reinterpret_cast<uint16_t *>(dst + i) = *reinterpret_cast<const uint16_t *>(src + i);
     }
 }
@@ -146,7 +176,7 @@ __device__ inline void copy_chunk_strided(char *__restrict__ sp, char *__restric
 // the piece holding its first chunk by binary search over the pieces' first
 // chunk numbers, then walks forward through the pieces.
 constexpr int64_t kMallBytes = 256ll << 20;
-template <bool NT>
+template <bool NT, bool UA>
 __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSeg *__restrict__ segs,
                                                                    int32_t nseg, int64_t total_chunks,
                                                                    int64_t per, PtrSet shard, PtrSet home,
@@ -172,9 +202,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_copy_kernel(const RouteSe
             char *sp = shard.p[g.shard] + g.shard_off + off;
             char *hp = home.p[g.home] + g.home_off + off;
             if (to_home)
-                copy_chunk<NT>(sp, hp, len);
+                copy_chunk<NT, UA>(sp, hp, len);
             else
-                copy_chunk<NT>(hp, sp, len);
+                copy_chunk<NT, UA>(hp, sp, len);
         } else {
             char *sp = shard.p[g.shard] + g.shard_off;
             char *hp = home.p[g.home] + g.home_off;
@@ -208,6 +238,7 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
     if (S > 0 && (!shard_bufs || !home_bufs))
         return fail(NS_ERR_INVALID_ARG, "buffer pointer arrays are required");
     PtrSet sh{}, ho{};
+    bool aligned = plan->aligned16;
     for (int32_t s = 0; s < S; ++s) {
         if (!shard_bufs[s] && plan->shard_elems[s] > 0)
             return fail(NS_ERR_INVALID_ARG, "shard buffer %d is NULL but holds %lld elements", s,
@@ -221,6 +252,7 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
                         plan->elem_bytes);
         sh.p[s] = (char *)shard_bufs[s];
         ho.p[s] = (char *)home_bufs[s];
+        aligned = aligned && align % 16 == 0;
     }
     if (plan->segs.empty()) return NS_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -229,12 +261,13 @@ ns_status route_launch(const ns_route_plan *plan, const void *const *shard_bufs,
     {
         TimedScope ts(kTimeRoute, 2.0 * (double)plan->total_bytes);
         const RouteSeg *table = reinterpret_cast<const RouteSeg *>(plan->device_table);
-        if (plan->total_bytes > kMallBytes)
-            ts.launch(route_copy_kernel<true>, dim3((unsigned)grid), dim3(kRouteThreads), st, table,
-                      (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
-        else
-            ts.launch(route_copy_kernel<false>, dim3((unsigned)grid), dim3(kRouteThreads), st, table,
-                      (int32_t)plan->segs.size(), plan->total_chunks, per, sh, ho, to_home);
+        const bool nt = plan->total_bytes > kMallBytes;
+        auto go = [&](auto kernel) {
+            ts.launch(kernel, dim3((unsigned)grid), dim3(kRouteThreads), st, table, (int32_t)plan->segs.size(),
+                      plan->total_chunks, per, sh, ho, to_home);
+        };
+        if (aligned) nt ? go(route_copy_kernel<true, false>) : go(route_copy_kernel<false, false>);
+        else nt ? go(route_copy_kernel<true, true>) : go(route_copy_kernel<false, true>);
     }
     NSQ_HIP(hipGetLastError());
     return NS_OK;
