@@ -50,10 +50,17 @@ DOMINANT_NAME = "ns_product_kernel<bf16, 256x256 tile / 8 waves, B X step>"
 TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a"}
 
 
-def _sha256(path: str) -> str:
+def _code_sha256(path: str) -> str:
+    """sha256 of a C/C++/HIP source with its comments and whitespace removed,
+    so that only a change to the code itself marks a measurement as stale."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    # string and character literals are kept whole; comments are dropped
+    token = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    code = token.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return hashlib.sha256("".join(code.split()).encode()).hexdigest()
 
 
 def stored_traffic():
@@ -64,7 +71,7 @@ def stored_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != _sha256(KERNEL_SRC):
+    if t.get("source_code_sha256") != _code_sha256(KERNEL_SRC):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -95,7 +102,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
     fw = copy_bytes / 1024.0 / write["copy"]
     traffic = (fetch["bx"] * ff + write["bx"] * fw) * 1024.0
     return {"kernel": DOMINANT_NAME, "kernel_symbol_contains": DOMINANT_SYMBOL,
-            "source": "newton_schulz_quintic_amd/csrc/ns_kernels.hip", "source_sha256": _sha256(KERNEL_SRC),
+            "source": "newton_schulz_quintic_amd/csrc/ns_kernels.hip", "source_code_sha256": _code_sha256(KERNEL_SRC),
             "fetch_kib_per_launch_raw": fetch["bx"], "write_kib_per_launch_raw": write["bx"],
             "copy_kernel_fetch_kib_raw": fetch["copy"], "copy_kernel_write_kib_raw": write["copy"],
             "copy_kernel_bytes_each_way": copy_bytes, "factor_fetch": ff, "factor_write": fw,

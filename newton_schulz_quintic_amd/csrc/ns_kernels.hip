@@ -9,16 +9,19 @@
 //
 // Design (one GPU, every matrix of a group in flight at once):
 //  * Workspace per matrix, oriented so m <= n, padded to multiples of 256 in
-//    both dims and kept zero in the padding: X (two copies, ping-pong), A and
-//    B. Padding removes every bounds check from the product main loop; zero
-//    padding stays zero through every step (products with zero rows/cols).
+//    both dims and kept zero in the padding: X (two copies, ping-pong), for
+//    m > 1024 also X^T (two copies), A and B. Padding removes every bounds
+//    check from the product main loop; zero padding stays zero through every
+//    step (products with zero rows/cols).
 //  * All three products run one MFMA main loop over K panels:
 //        A   = X X^T  : P = Q = X        (C = P Q^T, both read along rows)
 //        A A          : P = Q = A        (A A = A A^T, A symmetric)
-//        B X          : P = B, Q = X     (C = P Q, Q read K-major: stage kb
-//                                         holds 64 rows of X, and the MFMA
-//                                         fragments come from LDS transpose
-//                                         reads, so X^T is never stored)
+//        B X          : P = B, Q = X     (m <= 1024: C = P Q, Q read K-major,
+//                                         stage kb holds 64 rows of X and the
+//                                         MFMA fragments come from LDS
+//                                         transpose reads; longer K: C = P Q^T
+//                                         with Q = X^T, a copy each step
+//                                         writes, as K-major loads are slower)
 //    Panels of 128 bytes of K per row go global -> LDS with buffer_load ... lds
 //    into two stage buffers; every wave loads a slice of both panels.
 //    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups).
@@ -28,11 +31,12 @@
 //  * Epilogues in fp32, rounded once: A; B = b A + c (A A); X' = a X + B X.
 //    The rounded tile is staged in LDS column-major; the tile is then written
 //    row-major through LDS transpose reads and, for the symmetric products'
-//    mirror, column-major from plain LDS rows, both as 16-byte stores. The last step's
-//    epilogue writes straight to the caller's output in the input's
-//    orientation, shape and dtype.
+//    mirror (and X'^T where it is kept), column-major from plain LDS rows,
+//    both as 16-byte stores. The last step's epilogue writes straight to the
+//    caller's output in the input's orientation, shape and dtype.
 //  * Input staging: the input goes unscaled into X0 (tall inputs transposed
-//    through LDS) with per-tile fp32 sums of squares; the products reduce
+//    through LDS; X0^T too where it is kept) with per-tile fp32 sums of
+//    squares; the products reduce
 //    those in a fixed order (no atomics) and fold the scale into the first
 //    step's epilogues.
 //  * Workgroup ids are remapped so consecutive tiles land on the same XCD (the
