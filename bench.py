@@ -387,7 +387,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no cross-GPU "
-              "part in this build; how it would shard is described in the design notes.",
+              "part; how it would shard is described in the design notes.",
               file=sys.stderr)
         sys.exit(2)
 
