@@ -105,3 +105,30 @@ def test_single_shard_and_large_pieces():
     log("route: single shard")
     _run(shapes, [[s[0]] for s in shapes], [0, 0, 0], 1, [np.concatenate([f.ravel() for f in fulls])],
          "bf16")
+
+
+@pytest.mark.parametrize("cols,tail", [(4096, (512, 1024)), (4097, (1000, 333))])
+def test_plan_beyond_last_level_cache(cols, tail):
+    # about 302 MB moved per launch, more than the 256 MB last-level cache: the
+    # kernel that loads and stores with non-temporal hints; 16-byte aligned
+    # pieces (4096 columns), then pieces at 2-byte offsets (odd column counts)
+    rng = np.random.default_rng(12)
+    shapes = [(4096, cols)] * 9 + [tail]
+    split = [[1024, 1100, 972, 1000]] * 9 + [[tail[0] // 4, 0, tail[0] // 2, tail[0] - 3 * (tail[0] // 4)]]
+    home = [0, 1, 2, 3, 0, 1, 2, 3, 0, 1]
+    fulls = [rng.integers(0, 65535, size=s, dtype=np.uint16) for s in shapes]
+    assert sum(s[0] * s[1] for s in shapes) * 2 > 256 << 20
+    log(f"route: beyond the last-level cache, cols={cols}")
+    _run(shapes, split, home, 4, _shards_from_fulls(fulls, split, 4), "bf16")
+
+
+@pytest.mark.parametrize("max_grid", ["1", "3", "7"])
+def test_several_chunks_per_workgroup(monkeypatch, max_grid):
+    # plans under 128 GiB give each workgroup one 16 KiB chunk; a lowered cap
+    # makes workgroups walk several chunks and cross piece boundaries
+    monkeypatch.setenv("NS_ROUTE_MAX_GRID", max_grid)
+    log(f"route: NS_ROUTE_MAX_GRID={max_grid}")
+    test_square_set_four_shards(True)
+    for seed in range(3):
+        test_random_uneven_with_zeros(seed, "bf16")
+    test_random_uneven_with_zeros(3, "f32")

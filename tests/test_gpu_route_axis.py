@@ -114,3 +114,13 @@ def test_two_stage_rows_then_columns():
     homes = _roundtrip([(P, Q)], [csplit], [1], [2], C, stage1, 2, np.uint16)
     assert np.array_equal(_host(homes[2], np.uint16).reshape(P, Q), full)
     assert torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("max_grid", ["1", "5"])
+def test_axes_several_chunks_per_workgroup(monkeypatch, max_grid):
+    # workgroups walking several chunks across strided pieces
+    monkeypatch.setenv("NS_ROUTE_MAX_GRID", max_grid)
+    for seed in range(3):
+        test_random_axes(seed, 2)
+    test_random_axes(3, 4)
+    test_column_shards_wide()
