@@ -124,3 +124,17 @@ def test_axes_several_chunks_per_workgroup(monkeypatch, max_grid):
         test_random_axes(seed, 2)
     test_random_axes(3, 4)
     test_column_shards_wide()
+
+
+@pytest.mark.parametrize("elem", [2, 4])
+def test_banded_strided_pieces_ragged(elem):
+    # strided pieces are moved in bands of home rows (about 256 KiB of rows per
+    # band): row counts that are not a multiple of the band, odd widths (narrow
+    # units), a 3-dimensional tensor cut along its last dimension
+    rng = np.random.default_rng(13 + elem)
+    shapes = [(1000, 4100), (64, 300, 1000), (2047, 2048)]
+    dims = [1, 2, 1]
+    S = 4
+    split, shards, dtype = _case(rng, S, shapes, dims, elem)
+    log(f"route axis: banded strided pieces, elem {elem}, splits {split}")
+    _roundtrip(shapes, split, dims, [1, 0, 3], S, shards, elem, dtype)
