@@ -15,6 +15,15 @@
  * Work is enqueued asynchronously in stream order; calls do not synchronise
  * the host unless stated.
  *
+ * Environment (tuning and tests; read at each call; results are the same bits
+ * whichever is set):
+ *   NS_TILE=128|256      product tile edge for bf16 groups (default: 256 when
+ *                        the group has enough 256-tiles to fill the GPU)
+ *   NS_KMAJOR_MAX=K      largest padded m for which B.X reads X in place
+ *                        (default 1024; larger m keep a transposed copy)
+ *   NS_ROUTE_MAX_GRID=W  cap on pack/unpack workgroups (default 2^23, one
+ *                        16 KiB chunk each; a lower cap gives each several)
+ *
  * Pages cited (by title, then section):
  *   [owner_planning] "core.distributed.fsdp.src.megatron_fsdp.experimental.
  *                     owner_planning" (Megatron-FSDP API docs)
