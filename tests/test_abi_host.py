@@ -343,3 +343,21 @@ def test_gram_workspace_and_errors():
     assert call(float("inf")) == -1
     assert call(0.0, steps=-2) == -1
     assert call(1e-3) == -7      # valid; no workspace
+
+
+def test_route_plan_bands_strided_pieces():
+    # a piece sliced along a later dimension is moved in bands of about
+    # 256 KiB of home rows (one 64-byte table entry per band and shard); row
+    # pieces and small strided ones stay whole
+    entry = 64
+    rows = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(4096, 4096)], 4, [[1024] * 4], [0], [0], 2))
+    assert rows["device_table_bytes"] == 4 * entry
+    # 4096 home rows of 8 KiB: bands of 32 rows, 128 bands x 4 shards
+    cols = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(4096, 4096)], 4, [[1024] * 4], [1], [0], 2))
+    assert cols["device_table_bytes"] == 128 * 4 * entry
+    # 1000 home rows of 8200 bytes: bands of 31 rows, the last one ragged (33 bands), one zero-width shard
+    rag = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(1000, 4100)], 4, [[1025, 0, 2050, 1025]], [1], [0],
+                                                                2))
+    assert rag["device_table_bytes"] == 33 * 3 * entry
+    small = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(30, 64)], 2, [[32, 32]], [1], [0], 2))
+    assert small["device_table_bytes"] == max(16, 2 * entry)
