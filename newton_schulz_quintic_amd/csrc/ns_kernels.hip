@@ -1226,6 +1226,35 @@ void grouped_tiles(int32_t pid, int tm, int tn, bool upper, std::vector<TileRef>
                     if (!upper || tj >= ti) out.push_back(TileRef{pid, (uint16_t)ti, (uint16_t)tj, 0, 1});
 }
 
+#ifndef NSQ_XCD_DEAL
+#define NSQ_XCD_DEAL 1
+#endif
+// A launch's tile list runs in dispatch order: matrices by descending cost,
+// each in tile groups. xcd_remap gives XCD x a contiguous range of it, which
+// would put every long tile on the first XCDs when the group mixes sizes.
+// Deal the list to the XCDs instead, in runs of up to one tile group (which
+// shares operand panels through the XCD's L2), round robin, each XCD taking
+// exactly the number of ids xcd_remap gives it. Lists of equal tiles that
+// fill each XCD with one run keep their order. Only the order changes.
+void deal_to_xcds(std::vector<TileRef> &t) {
+    const int64_t g = (int64_t)t.size();
+    if (!NSQ_XCD_DEAL || g <= kNumXcd) return;
+    const int64_t per = g / kNumXcd, rem = g % kNumXcd;
+    const int64_t run = std::min<int64_t>(kGroupRows * kGroupCols, (g + kNumXcd - 1) / kNumXcd);
+    std::vector<std::vector<TileRef>> q(kNumXcd);
+    int64_t i = 0;
+    for (int x = 0; i < g; x = (x + 1) % kNumXcd) {
+        const int64_t room = per + (x < rem ? 1 : 0) - (int64_t)q[x].size();
+        const int64_t n = std::min(std::min(run, room), g - i);
+        if (n > 0) {
+            q[x].insert(q[x].end(), t.begin() + i, t.begin() + i + n);
+            i += n;
+        }
+    }
+    t.clear();
+    for (const std::vector<TileRef> &v : q) t.insert(t.end(), v.begin(), v.end());
+}
+
 template <typename T, class C>
 void launch_product(TimedScope &ts, dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles,
                     int32_t nt, int32_t mode, int32_t cur, bool last, float s_init, float s_final, float s_diag,
@@ -1352,6 +1381,9 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         norm_bytes += m * n * esi + (mi.kmajor ? 1.0 : 2.0) * (double)mi.mp * (double)mi.np * es;
     }
     if (probs.empty()) return NS_OK;
+    deal_to_xcds(syrk);
+    deal_to_xcds(gemm);
+    deal_to_xcds(sq);
 
     // The tables go to pinned host memory; the first kernel reads its own from
     // there and copies all of them into the workspace head.
