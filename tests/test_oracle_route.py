@@ -195,3 +195,61 @@ def test_two_stage_rows_then_columns():
     # stage 2: the C column blocks, now complete in rows, gathered along dim 1
     homes = route.pack_axis(stage1, [(P, Q)], [csplit], [1], [1], C)
     assert np.array_equal(homes[1].reshape(P, Q), full)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_route_offsets_axis_locate_every_piece(seed):
+    # Pin for planner.route_offsets with a per-tensor shard_dim, built without
+    # its offset arithmetic: every element of every tensor carries a unique
+    # tag; shard buffers are the per-shard concatenations of np.split blocks
+    # along each tensor's axis, home buffers the per-home concatenations of the
+    # whole tensors in index order. Each returned offset must then point at
+    # exactly its piece, and the sizes must be the buffers' lengths.
+    rng = np.random.default_rng(1700 + seed)
+    S = int(rng.integers(1, 6))
+    n = int(rng.integers(1, 8))
+    shapes, fulls, split, dims = [], [], [], []
+    tag = 0
+    for i in range(n):
+        nd = int(rng.integers(2, 5))
+        shape = tuple(int(rng.integers(0 if i == 0 else 1, 6)) for _ in range(nd))
+        d = int(rng.integers(0, nd))
+        cuts = np.sort(rng.integers(0, shape[d] + 1, size=S - 1))
+        split.append(np.diff(np.concatenate([[0], cuts, [shape[d]]])).astype(int).tolist())
+        size = int(np.prod(shape))
+        fulls.append(np.arange(tag, tag + size, dtype=np.int64).reshape(shape))
+        tag += size
+        shapes.append(shape)
+        dims.append(d)
+    home = [int(rng.integers(0, S)) for _ in range(n)]
+    blocks = [np.split(f, np.cumsum(sp)[:-1], axis=d) for f, sp, d in zip(fulls, split, dims)]
+    shards = [np.concatenate([blocks[i][s].ravel() for i in range(n)]) for s in range(S)]
+    homes = []
+    for h in range(S):
+        parts = [fulls[i].ravel() for i in range(n) if home[i] == h]
+        homes.append(np.concatenate(parts) if parts else np.zeros(0, np.int64))
+    got = planner.route_offsets(shapes, split, home, S, shard_dim=dims)
+    assert got["shard_elems"] == [len(b) for b in shards]
+    assert got["home_elems"] == [len(b) for b in homes]
+    for i in range(n):
+        hb, ho, size = homes[home[i]], got["home_offset"][i], fulls[i].size
+        assert np.array_equal(hb[ho:ho + size], fulls[i].ravel())
+        lo = 0
+        for s in range(S):
+            blk = blocks[i][s].ravel()
+            so = got["shard_offset"][i][s]
+            assert np.array_equal(shards[s][so:so + blk.size], blk)
+            assert got["row_start"][i][s] == lo
+            lo += split[i][s]
+
+
+def test_route_offsets_axis_hand_case():
+    # a (2, 3, 4) tensor cut along dim 1 as [1, 2] and a (4, 2) tensor cut along
+    # dim 0 as [3, 1]: shard 0 holds 2*1*4 = 8 then 3*2 = 6 elements, shard 1
+    # holds 2*2*4 = 16 then 1*2 = 2; both tensors homed on 1 (24 then 8).
+    got = planner.route_offsets([(2, 3, 4), (4, 2)], [[1, 2], [3, 1]], [1, 1], 2, shard_dim=[1, 0])
+    assert got["shard_offset"] == [[0, 0], [8, 16]]
+    assert got["shard_elems"] == [14, 18]
+    assert got["home_offset"] == [0, 24]
+    assert got["home_elems"] == [0, 32]
+    assert got["row_start"] == [[0, 1], [0, 3]]
