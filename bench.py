@@ -3,27 +3,29 @@
 One step = the whole path over one batch: select / cost / LPT homes (ns_plan,
 host), pack the row shards into their homes (one HIP launch; the route plan is
 built once and reused, as the pages' cached `plan` dict is), batched 5-step
-quintic Newton-Schulz on the home buffers (norm + 15 product launches), and
-unpack the results into result shards (one HIP launch). Inputs are resident in
-HBM before the timed region. With --routing fused the step is one
-ns_orthogonalize_routed call instead, which reads the shard buffers and writes
-the result shards itself (no home buffers, no pack / unpack launches); the mode
-not selected is timed as well and reported under `other_routing`.
+quintic Newton-Schulz on the home buffers (input staging + 15 product
+launches), and unpack the results into result shards (one HIP launch). Inputs
+are resident in HBM before the timed region. With --routing fused the step is
+one ns_orthogonalize_routed call instead, which reads the shard buffers and
+writes the result shards itself (no home buffers, no pack / unpack launches);
+the mode not selected is timed as well and reported under `other_routing`.
 
-Default workload: 16 bf16 1024x1024 matrices, N(0, 0.02), stored as 4 uneven
-row shards (one home empty). Other workloads: --workload dense-transformer
-(224 matrices, 32 layers, hidden 4096, ffn 14336) or many-small (3000 random +
-192 MoE matrices).
+Default workload: the dense-transformer set (32 layers x q, k, v, o 4096-wide
+projections, gate, up and down 14336 x 4096 FFN weights: 224 bf16 matrices,
+N(0, 0.02)), stored as 4 even row shards. Other workloads: --workload
+routed-square (16 bf16 1024x1024 in 4 uneven row shards, one home empty) or
+many-small (3000 random + 192 MoE matrices).
 
 Prints ONE JSON line. `value` is matrices per second for the whole step.
-`roofline` covers the dominant kernel (the MFMA product kernel): algorithmic
-flops per launch over its average launch time, from HIP event pairs that its
-dispatches record (hipExtLaunchKernelGGL: kernel execution only, as rocprofv3
-reports it) in a pass of the same steps right after the timed region, with
-every launch timed as rocprofv3 times every dispatch; the timed region itself
-carries no events.
-`cpu_baseline` times the CPU oracle (plan, pack, fp64 Newton-Schulz, unpack) on
-a bounded sample of the same workload.
+`roofline` covers the dominant kernel, the one with the largest share of the
+step's kernel time: its algorithmic flops (or bytes) per launch over its
+average launch time, from HIP event pairs that the dispatches record
+(hipExtLaunchKernelGGL: kernel execution only, as rocprofv3 reports it) in a
+pass of the same steps right after the timed region, with every launch timed
+as rocprofv3 times every dispatch; the timed region itself carries no events.
+`cpu_baseline` times the CPU oracle (plan, pack, fp64 Newton-Schulz, unpack)
+on a bounded sample of the same workload: one matrix per frequent shape plus a
+seeded sample of the rest, extrapolated to the whole set by count.
 """
 
 from __future__ import annotations
@@ -40,14 +42,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "NS matrices/sec + achieved TFLOP/s (% bf16 MFMA peak), 5-step quintic NS"
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "ns_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ns_product_bx_routed16x1024.json")
-# rocprof symbol of the dominant kernel on the default workload (bf16, 256x256 tile, B X step)
-DOMINANT_SYMBOL = "ns_product_kernelIDF16bNS0_7TileCfgILi256ELi2ELi4ELi128ELi2EEELi2ELb0E"
-DOMINANT_NAME = "ns_product_kernel<bf16, 256x256 tile / 8 waves, B X step>"
+ROUTE_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "route.hip")
+PROFILES = os.path.join(ROOT, "profiles")
 TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a"}
+# What each timing kind is, and the part of its rocprofv3 kernel name that picks it.
+PHASES = {
+    "syrk_x": ("ns_product_kernel<bf16, A = X X^T, upper tiles>", "ELi0ELb0E", "mfma"),
+    "syrk_a": ("ns_product_kernel<bf16, B' = a I + b A + c A A, upper tiles>", "ELi1ELb0E", "mfma"),
+    "bx": ("ns_product_kernel<bf16, X' = B' X>", "ELi2ELb0E", "mfma"),
+    "bx_final": ("ns_product_kernel<bf16, X' = B' X, last step writes the output>", "ELi2ELb1E", "mfma"),
+    "norm": ("ns_prepare_kernel (input staging + norm partials)", "ns_prepare_kernel", "hbm"),
+    "route": ("route_copy_kernel (pack / unpack)", "route_copy_kernel", "hbm"),
+}
+WORKLOADS = ["dense-transformer", "routed-square", "many-small"]
 
 
 def _code_sha256(path: str) -> str:
@@ -63,50 +73,142 @@ def _code_sha256(path: str) -> str:
     return hashlib.sha256("".join(code.split()).encode()).hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if it is missing or the kernel source changed since."""
+def counters_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"counters_{workload}.json")
+
+
+def stored_traffic(workload: str, phase: str):
+    """HBM bytes per launch of `phase` on `workload` from the committed counter
+    summary, or None if it is missing or the kernel's source changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(counters_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_code_sha256") != _code_sha256(KERNEL_SRC):
+    src = ROUTE_SRC if phase == "route" else KERNEL_SRC
+    if t.get("source_code_sha256", {}).get(os.path.basename(src)) != _code_sha256(src):
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t.get("phases", {}).get(phase, {}).get("traffic_bytes_per_launch")
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
-    """Per-launch FETCH_SIZE / WRITE_SIZE of the dominant kernel from two
-    rocprofv3 --pmc runs, scaled by what the same counters read for the pack
-    copy kernel, which reads and writes `copy_bytes` per launch."""
+def _phase_of(kernel_name: str):
+    for phase, (_, key, _) in PHASES.items():
+        if key in kernel_name:
+            return phase
+    return None
+
+
+def summarize_counters(dirs, workload: str) -> dict:
+    """Per-phase counters from rocprofv3 --pmc runs (one directory per pass) of
+    one bench step of `workload`: per-dispatch averages of every counter, and
+
+      * mfma_busy = rocprofv3's MfmaUtil (the MFMA busy cycles of every SIMD
+        over the GPU's active cycles times the SIMD count): the fraction of
+        SIMD cycles the matrix cores were busy (clock independent);
+      * mfma_flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (rocprof's convention),
+        beside the algorithmic flops of the same launch (the ratio is the
+        padding and diagonal-tile work the algorithmic count leaves out);
+      * traffic = FETCH_SIZE and WRITE_SIZE (KiB), each scaled by what the same
+        counter reads for the pack copy kernel of the run, which reads and
+        writes a known number of bytes per launch.
+    """
     import csv
+    import glob
     import statistics
+    ms = build_workload(workload)
+    vals = {}          # phase -> counter -> dispatch -> value
+    names = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    phase = _phase_of(r["Kernel_Name"])
+                    if phase is None:
+                        continue
+                    names.setdefault(phase, r["Kernel_Name"].split("(")[0][:160])
+                    c = vals.setdefault(phase, {}).setdefault(r["Counter_Name"], {})
+                    c[r["Dispatch_Id"]] = c.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    avg = {p: {k: statistics.mean(v.values()) for k, v in cs.items()} for p, cs in vals.items()}
+    copy_bytes = sum(_numel(s) for s in ms.shapes) * 2
+    route = avg.get("route", {})
+    ff = copy_bytes / 1024.0 / route["FETCH_SIZE"] if route.get("FETCH_SIZE") else None
+    fw = copy_bytes / 1024.0 / route["WRITE_SIZE"] if route.get("WRITE_SIZE") else None
+    flops = alg_phase_flops(ms)
+    num_xcd, cus = 8, 256
+    out = {"workload": ms.name, "source_code_sha256": {os.path.basename(KERNEL_SRC): _code_sha256(KERNEL_SRC),
+                                                       os.path.basename(ROUTE_SRC): _code_sha256(ROUTE_SRC)},
+           "copy_kernel_bytes_each_way": copy_bytes, "factor_fetch": ff, "factor_write": fw, "phases": {}}
+    for phase, c in sorted(avg.items()):
+        e = {"kernel": PHASES[phase][0], "symbol": names.get(phase), "dispatches": len(next(iter(vals[phase].values()))),
+             "counters_per_dispatch": {k: round(v, 1) for k, v in sorted(c.items())}}
+        if "MfmaUtil" in c:      # rocprofv3's own: sum of MFMA busy cycles / (max GRBM_GUI_ACTIVE x SIMDs)
+            e["mfma_busy"] = round(c["MfmaUtil"] / 100.0, 4)
+        elif "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            e["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cus * c["GRBM_GUI_ACTIVE"] / num_xcd), 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            e["mfma_flops"] = 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+            if flops.get(phase):
+                e["alg_flops"] = flops[phase]
+                e["mfma_over_alg"] = round(e["mfma_flops"] / flops[phase], 4)
+        if ff and fw and "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            e["traffic_bytes_per_launch"] = (c["FETCH_SIZE"] * ff + c["WRITE_SIZE"] * fw) * 1024.0
+        out["phases"][phase] = e
+    return out
 
-    def per_kernel(d, counter):
-        vals = {}
-        with open(os.path.join(d, "run_counter_collection.csv")) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                key = "bx" if DOMINANT_SYMBOL in r["Kernel_Name"] else (
-                    "copy" if "route_copy_kernel" in r["Kernel_Name"] else None)
-                if key:
-                    vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
-                    vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: statistics.median(v.values()) for k, v in vals.items()}
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
-    ff = copy_bytes / 1024.0 / fetch["copy"]
-    fw = copy_bytes / 1024.0 / write["copy"]
-    traffic = (fetch["bx"] * ff + write["bx"] * fw) * 1024.0
-    return {"kernel": DOMINANT_NAME, "kernel_symbol_contains": DOMINANT_SYMBOL,
-            "source": "newton_schulz_quintic_amd/csrc/ns_kernels.hip", "source_code_sha256": _code_sha256(KERNEL_SRC),
-            "fetch_kib_per_launch_raw": fetch["bx"], "write_kib_per_launch_raw": write["bx"],
-            "copy_kernel_fetch_kib_raw": fetch["copy"], "copy_kernel_write_kib_raw": write["copy"],
-            "copy_kernel_bytes_each_way": copy_bytes, "factor_fetch": ff, "factor_write": fw,
-            "traffic_bytes_per_launch": traffic}
+def summarize_trace(trace_dir: str, workload: str, steps: int) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run of bench.py:
+    per phase the launches, average / min / max duration and time share, and
+    for the product phases the algorithmic TFLOP/s of an average launch."""
+    import csv
+    import glob
+    ms = build_workload(workload)
+    flops = alg_phase_flops(ms)
+    rows = {}
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            phase = _phase_of(r["Name"]) or r["Name"].split("(")[0][:60]
+            e = rows.setdefault(phase, [0, 0.0, float("inf"), 0.0])
+            n = int(r["Calls"])
+            e[0] += n
+            e[1] += float(r["TotalDurationNs"])
+            e[2] = min(e[2], float(r["MinNs"]))
+            e[3] = max(e[3], float(r["MaxNs"]))
+    total = sum(e[1] for e in rows.values())
+    lines = ["| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share | Algorithmic TFLOP/s (% of 2516.6) |",
+             "|---|---|---|---|---|---|---|"]
+    for phase, (n, tot, lo, hi) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        avg_ns = tot / n
+        rate = ""
+        if phase in flops and PHASES[phase][2] == "mfma":
+            tf = flops[phase] / (avg_ns * 1e-9) / 1e12
+            rate = f"{tf:.1f} ({100 * tf / PEAK_BF16_TFLOPS:.1f} %)"
+        name = PHASES[phase][0] if phase in PHASES else phase
+        lines.append(f"| {name} | {n} | {avg_ns / 1e3:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} | "
+                     f"{100 * tot / total:.1f} % | {rate} |")
+    return "\n".join(lines)
+
+
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def alg_phase_flops(ms) -> dict:
+    """Algorithmic flops of one launch of each product phase over the whole set."""
+    c_nonzero = ms.coeffs[2] != 0.0
+    fx = fa = fb = 0.0
+    for s in ms.shapes:
+        m, n = oriented(s)
+        if m == 0:
+            continue
+        fx += m * (m + 1) * n
+        fa += m * m * (m + 1) if c_nonzero else 0
+        fb += 2 * m * m * n
+    return {"syrk_x": fx, "syrk_a": fa, "bx": fb, "bx_final": fb}
 
 
 def alg_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
@@ -168,45 +270,75 @@ def make_shards(ms, device_gen: bool, shard_dim: int = 0):
 
 
 def cpu_baseline(ms, budget_s: float):
-    """The oracle on a bounded sample: plan, pack, fp64 NS and unpack of the
-    first k matrices (k grows until about budget_s of work)."""
+    """The oracle on a bounded sample of the workload, extrapolated to the set.
+
+    The sample: one matrix of every shape that makes up at least 1 % of the
+    set (every shape of a set with at most 8 distinct ones), plus a seeded
+    sample of up to 64 of the remaining matrices. Each sampled matrix goes
+    through the oracle's plan, pack, fp64 Newton-Schulz and unpack on its own,
+    repeated until about budget_s / (number of samples) of work (at least
+    once); its mean time stands for every matrix it represents. The set's
+    time is the sum over the sample of (time x matrices represented) plus the
+    oracle planner run once on the whole set."""
+    import collections
+    import random
+
     import numpy as np
+    import threadpoolctl
+
     from oracle import ns as ons
     from oracle import planner, route
     from workloads import host_matrix
-    import threadpoolctl
 
     a, b, c = (float(np.float32(x)) for x in ms.coeffs)
-    # warm the BLAS so threadpoolctl sees it
-    np.ones((64, 64)) @ np.ones((64, 64))
+    np.ones((64, 64)) @ np.ones((64, 64))      # load the BLAS so threadpoolctl sees it
     threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()
                   if p.get("user_api") == "blas") or 1
     S = ms.num_shards
-    done, t0 = 0, time.perf_counter()
-    elapsed = 0.0
-    while elapsed < budget_s or done == 0:
-        i = done % ms.n
-        shape = ms.shapes[i]
-        split = [ms.split_rows[i]]
+    counts = collections.Counter(tuple(s) for s in ms.shapes)
+    first = {}
+    for i, s in enumerate(ms.shapes):
+        first.setdefault(tuple(s), i)
+    frequent = {s for s, k in counts.items() if len(counts) <= 8 or k >= max(2, 0.01 * ms.n)}
+    sample = [(first[s], counts[s]) for s in sorted(frequent, key=lambda s: first[s])]
+    rest = [i for i, s in enumerate(ms.shapes) if tuple(s) not in frequent]
+    if rest:
+        picked = sorted(random.Random(0).sample(rest, min(64, len(rest))))
+        sample += [(i, len(rest) / len(picked)) for i in picked]
+    per_sample = budget_s / len(sample)
+    t_wall = time.perf_counter()
+    set_seconds, work, reps_total = 0.0, 0.0, 0
+    for i, weight in sample:
+        shape, split = ms.shapes[i], ms.split_rows[i]
         full = host_matrix(ms.seed, i, shape, std=ms.std)
-        shards = np.split(full, np.cumsum(split[0])[:-1], axis=0)
-        shards = [x.ravel() for x in shards]
-        t_start = time.perf_counter()
-        p = planner.plan([shape], ms.steps, S, split)
-        homes = route.pack(shards, [shape], split, p["home"], S)
-        x = ons.bf16_bits_to_f64(homes[p["home"][0]]).reshape(shape)
-        y = ons.newton_schulz(x, ms.steps, a, b, c, 1e-7)
-        res = [np.zeros(0)] * S
-        res[p["home"][0]] = y.ravel()
-        route.unpack(res, [shape], split, p["home"], S)
-        elapsed += time.perf_counter() - t_start
-        done += 1
-    total = time.perf_counter() - t0
-    what = (f"{done} matrices ({done / ms.n:.2f} passes over the {ms.n}-matrix set)" if done >= ms.n
-            else f"the first {done} of the {ms.n} matrices")
-    return {"value": done / elapsed, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what} through oracle plan + pack + fp64 NS ({ms.steps} steps) + unpack, "
-                      f"{elapsed:.1f} s of work ({total:.1f} s wall)"}
+        shards = [x.ravel() for x in np.split(full, np.cumsum(split)[:-1], axis=0)]
+        spent, reps = 0.0, 0
+        while reps == 0 or spent < per_sample:
+            t0 = time.perf_counter()
+            p = planner.plan([shape], ms.steps, S, [split])
+            homes = route.pack(shards, [shape], [split], p["home"], S)
+            x = ons.bf16_bits_to_f64(homes[p["home"][0]]).reshape(shape)
+            y = ons.newton_schulz(x, ms.steps, a, b, c, 1e-7)
+            res = [np.zeros(0)] * S
+            res[p["home"][0]] = y.ravel()
+            route.unpack(res, [shape], [split], p["home"], S)
+            spent += time.perf_counter() - t0
+            reps += 1
+        set_seconds += weight * spent / reps
+        work += spent
+        reps_total += reps
+    t0 = time.perf_counter()
+    planner.plan(ms.shapes, ms.steps, S, ms.split_rows)
+    t_plan = time.perf_counter() - t0
+    set_seconds += t_plan
+    kind = "the whole set" if len(sample) == ms.n and all(w == 1 for _, w in sample) else "extrapolated"
+    return {"value": ms.n / set_seconds, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": kind == "extrapolated", "set_seconds": round(set_seconds, 3),
+            "sample": (f"{len(sample)} matrices ({len(frequent)} frequent shapes, one each"
+                       + (f", + {len(sample) - len(frequent)} seeded picks from the other {len(rest)}" if rest else "")
+                       + f"), {reps_total} oracle runs of plan + pack + fp64 NS ({ms.steps} steps) + unpack, "
+                       f"{work:.1f} s of work ({time.perf_counter() - t_wall:.1f} s wall), {kind} to the "
+                       f"{ms.n}-matrix set by count, + the oracle planner on the whole set ({t_plan * 1e3:.1f} ms)")}
 
 
 def wave_bench(ms, slots: int, tokens: int, reps: int) -> dict:
@@ -355,8 +487,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="routed-square",
-                    choices=["routed-square", "dense-transformer", "many-small"])
+    ap.add_argument("--workload", default="dense-transformer", choices=WORKLOADS)
     ap.add_argument("--routing", default="pack", choices=["pack", "fused"],
                     help="pack: pack -> batched NS on the home buffers -> unpack (three calls); fused: "
                          "ns_orthogonalize_routed reads and writes the shard buffers directly. The other "
@@ -371,19 +502,23 @@ def main():
     ap.add_argument("--shard-dim", type=int, default=0,
                     help="cut every tensor's shards along this dimension (0 = rows; 1 = the TP stage's "
                          "column shards, evenly over the workload's shard count); pack / unpack routing only")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (at least one run "
+                    "of each sampled matrix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="skip the HIP-event timing of the product kernel")
-    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of the default "
-                         "workload into the traffic JSON (printed) and exit")
+                    help="skip the HIP-event timing of every launch")
+    ap.add_argument("--no-other-routing", action="store_true", help="do not time the other routing mode")
+    ap.add_argument("--counters", nargs="+", metavar="PMC_DIR",
+                    help="summarise rocprofv3 --pmc runs (one directory per pass) of one step of --workload "
+                         "into the per-phase counter JSON (printed) and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print the per-phase table of a rocprofv3 --kernel-trace --stats run of --workload and exit")
     args = ap.parse_args()
     if args.counters:
-        from workloads import routed_square_batch
-        ms = routed_square_batch(uneven=True)
-        copy_bytes = sum(r * c for r, c in ms.shapes) * 2
-        print(json.dumps(summarize_counters(args.counters[0], args.counters[1], copy_bytes), indent=1))
+        print(json.dumps(summarize_counters(args.counters, args.workload), indent=1))
+        return
+    if args.trace_summary:
+        print(summarize_trace(args.trace_summary, args.workload, args.steps))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no cross-GPU "
@@ -484,10 +619,9 @@ def main():
         torch.cuda.synchronize()
         nsq.ns_timing_enable(False)
         breakdown = {name: nsq.ns_timing_read(k) for k, name in TIMING_KINDS.items()}
-    dominant = breakdown.get("bx", (0.0, 0, 0.0))
     # The other routing mode, same inputs and step count, no instrumentation.
     ms_other = None
-    if not args.shard_dim:
+    if not args.shard_dim and not args.no_other_routing:
         for _ in range(args.warmup):
             other()
         torch.cuda.synchronize()
@@ -528,22 +662,34 @@ def main():
     }
     if not args.no_kernel_timing:
         t = breakdown
-        kms, kn, kwork = dominant
-        if kn:
-            achieved = (kwork / kn) / (kms / kn * 1e-3) / 1e12
-            traffic = stored_traffic() if args.workload == "routed-square" else None
-            out["roofline"] = {"kernel": DOMINANT_NAME, "bound": "mfma", "achieved": round(achieved, 2),
-                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                               "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                               "avg_launch_us": round(kms / kn * 1e3, 2),
-                               "alg_flops_per_launch": kwork / kn, "launches": kn}
+        total_ms = sum(v[0] for v in t.values())
+        # the dominant kernel: the largest share of the step's kernel time
+        dom = max((k for k in t if t[k][1]), key=lambda k: t[k][0])
+        kms, kn, kwork = t[dom]
+        name, _, bound = PHASES[dom]
+        avg_s = kms / kn * 1e-3
+        if bound == "mfma":
+            achieved, peak, unit = (kwork / kn) / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, unit = (kwork / kn) / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+        out["roofline"] = {"kernel": name, "phase": dom, "bound": bound, "achieved": round(achieved, 2),
+                           "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                           "traffic": stored_traffic(args.workload, dom) if not args.shard_dim else None,
+                           "time_share": round(kms / total_ms, 4), "avg_launch_us": round(kms / kn * 1e3, 2),
+                           ("alg_flops_per_launch" if bound == "mfma" else "alg_bytes_per_launch"): kwork / kn,
+                           "launches": kn}
         phases = {}
         for name in ("syrk_x", "syrk_a", "bx", "bx_final"):
             pms, pn, pwork = t[name]
             if pn:
-                phases[name] = {"avg_us": round(pms / pn * 1e3, 2),
-                                "tflops": round((pwork / pn) / (pms / pn * 1e-3) / 1e12, 1), "launches": pn}
+                tf = (pwork / pn) / (pms / pn * 1e-3) / 1e12
+                phases[name] = {"avg_us": round(pms / pn * 1e3, 2), "tflops": round(tf, 1),
+                                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "time_share": round(pms / total_ms, 4),
+                                "launches": pn}
         out["product_phases"] = phases
+        if phases:
+            low = min(phases, key=lambda k: phases[k]["tflops"])
+            out["lowest_utilisation_phase"] = low
         out["breakdown_note"] = ("roofline, product_phases, route_kernel and norm_kernels come from a second "
                                  "pass of the same steps with HIP events on every launch (kernel execution "
                                  "only); the timed region itself carries no events")

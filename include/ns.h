@@ -2,9 +2,12 @@
  * ns.h -- C ABI of the MI355X (gfx950) Newton-Schulz library.
  *
  * One GPU. Plain pointers and sizes; no C++ or torch types. Every call returns
- * an ns_status (0 = NS_OK, negative = error). On error nothing has been
- * enqueued on the stream and no output has been written; ns_last_error()
- * returns a message for the calling thread's last failure.
+ * an ns_status (0 = NS_OK, negative = error). Every argument is checked, and
+ * every group and wave of a call is planned, before anything is enqueued: on
+ * any error other than NS_ERR_HIP nothing has been enqueued on the stream and
+ * no output has been written. NS_ERR_HIP reports a failing HIP runtime call;
+ * work enqueued before it (earlier launches of the same call) may still run.
+ * ns_last_error() returns a message for the calling thread's last failure.
  *
  * Memory: the library never allocates device memory. Every device buffer (shard
  * buffers, home buffers, the route plan's device table, the Newton-Schulz
@@ -344,6 +347,9 @@ ns_status ns_wave_plan(int32_t n, const ns_shape *shapes, const int32_t *ready_o
  * are bit-identical to ns_orthogonalize_batched on the same tensors (no
  * result depends on which tensors share a call). The workspace minimum is that
  * of ns_workspace_bytes on all n shapes; the waves reuse it in stream order.
+ * Every wave is planned before the first event wait is enqueued, so an
+ * argument error enqueues nothing; an invalid event handle fails in
+ * hipStreamWaitEvent (NS_ERR_HIP) after the earlier waves were enqueued.
  * Other arguments and errors as for ns_orthogonalize_batched. */
 ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *const *in,
                                  void *const *out, ns_dtype dtype, int32_t steps, float a, float b,

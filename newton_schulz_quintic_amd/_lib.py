@@ -137,6 +137,26 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _new_workspace(nbytes: int, device, stream):
+    """A torch uint8 workspace for a call enqueued on ``stream``.
+
+    torch's caching allocator ties a block to the stream that allocated it
+    (the current stream). When the library's kernels run on another stream,
+    the block is also recorded on that stream, so that dropping the returned
+    workspace cannot hand its memory to new work before those kernels end.
+    """
+    import torch
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if stream is not None:
+        if isinstance(stream, torch.cuda.Stream):
+            s = stream
+        else:
+            s = torch.cuda.ExternalStream(int(stream), device=ws.device)
+        if s.cuda_stream != torch.cuda.current_stream(ws.device).cuda_stream:
+            ws.record_stream(s)
+    return ws
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
@@ -225,9 +245,8 @@ def ns_route_plan_query(plan: RoutePlan) -> dict:
 def ns_route_plan_upload(plan: RoutePlan, device_table=None, stream=None):
     """Upload the plan's table. Allocates a torch uint8 device tensor if none is given."""
     if device_table is None:
-        import torch
         nbytes = ns_route_plan_query(plan)["device_table_bytes"]
-        device_table = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        device_table = _new_workspace(nbytes, "cuda", stream)
     _check(lib().ns_route_plan_upload(plan.handle, device_table.data_ptr(), _stream(stream)))
     plan.device_table = device_table     # keep the memory alive with the plan
     return device_table
@@ -293,9 +312,8 @@ def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
             raise ValueError("tensors must be contiguous and outputs shaped like inputs")
     shapes = [tuple(x.shape) for x in inputs]
     if workspace is None:
-        import torch
         need, _ = ns_workspace_bytes(shapes, dtype)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+        workspace = _new_workspace(need, inputs[0].device, stream)
     a, b, c = coeffs
     sh = _shapes(shapes)
     ins = _arr(_P, [x.data_ptr() for x in inputs])
@@ -335,9 +353,8 @@ def ns_orthogonalize_strided(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
             raise ValueError("tensors must share one dtype and outputs be shaped like inputs")
     shapes = [tuple(x.shape) for x in inputs]
     if workspace is None:
-        import torch
         need, _ = ns_workspace_bytes(shapes, dtype)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+        workspace = _new_workspace(need, inputs[0].device, stream)
     a, b, c = coeffs
     sh = _shapes(shapes)
     ins = _arr(_P, [x.data_ptr() for x in inputs])
@@ -370,10 +387,9 @@ def ns_orthogonalize_routed(plan: RoutePlan, shard_in, shard_out, dtype: int, st
         raise TypeError(f"unsupported dtype code {dtype}")
     src, dst = _ptr_array(shard_in, plan.num_shards), _ptr_array(shard_out, plan.num_shards)
     if workspace is None:
-        import torch
         need, _ = ns_routed_workspace_bytes(plan, dtype)
         dev = next((t.device for t in list(shard_in) + list(shard_out) if t is not None), "cuda")
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = _new_workspace(need, dev, stream)
     a, b, c = coeffs
     ord_arr = None if order is None else _arr(_I32, order)
     _check(lib().ns_orthogonalize_routed(plan.handle, _addr(src), _addr(dst), dtype, steps, float(a),
@@ -406,9 +422,8 @@ def ns_orthogonalize_gram(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4.77
             raise ValueError("tensors must be contiguous and outputs shaped like inputs")
     shapes = [tuple(x.shape) for x in inputs]
     if workspace is None:
-        import torch
         need, _ = ns_gram_workspace_bytes(shapes, dtype)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+        workspace = _new_workspace(need, inputs[0].device, stream)
     a, b, c = coeffs
     sh = _shapes(shapes)
     ins = _arr(_P, [x.data_ptr() for x in inputs])
@@ -449,9 +464,8 @@ def ns_orthogonalize_waves(inputs, outputs, wave_of, num_waves: int, ready_event
             raise ValueError("tensors must be contiguous and outputs shaped like inputs")
     shapes = [tuple(x.shape) for x in inputs]
     if workspace is None:
-        import torch
         need, _ = ns_workspace_bytes(shapes, dtype)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=inputs[0].device)
+        workspace = _new_workspace(need, inputs[0].device, stream)
     evs = None
     if ready_events is not None:
         if len(ready_events) != num_waves:

@@ -750,12 +750,19 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         }
     }
 
+    // K stages of the NS products: the K extent (n for X X^T, m for A A and
+    // B' X) rounded up to a whole stage; the zero padding past it adds nothing.
+    // The Gram-space products run over the padded extents.
+    constexpr int KW = C::ROWB / ES;
+    constexpr bool kTrim = MODE == kSyrkX || MODE == kSyrkA || MODE == kGemmBX;
+    const int nk_n = kTrim ? (pr.n + KW - 1) / KW : np / KW;
+    const int nk_m = kTrim ? (pr.m + KW - 1) / KW : mp / KW;
     f32x16 acc[C::NBM][C::NBN];
     if constexpr (MODE == kSyrkX || MODE == kGramG) {
         zero_acc<C>(acc);
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
-                           np * ES / C::ROWB, lds, acc);
+                           nk_n, lds, acc);
     } else if constexpr (MODE == kSyrkA || MODE == kGramB0 || MODE == kGramAA) {
         // S S with S symmetric (A, G): the Q operand is S's rows; the general
         // A A of the Gram space reads A^T's rows instead
@@ -767,7 +774,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
             // columns col0 .. col0 + BM: seed s_init S from there
             zero_acc<C>(acc);
             tile_product<T, C, true>(S + (int64_t)row0 * ld, SQ + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
-                                     mp * ES / C::ROWB, lds, acc, col0 * ES / C::ROWB, s_init);
+                                     nk_m, lds, acc, col0 / KW, s_init);
         } else {
             init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
         }
@@ -781,11 +788,11 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
             char *X = MODE == kGemmBX ? xc : pr.x0;
             const int ldq = ldx * ES;
             tile_product<T, C, false, true>(P + (int64_t)row0 * ldp, X + (int64_t)col0 * ES, ldp, ldq, BM * ldp,
-                                            mp * ldq - col0 * ES, mp * ES / C::ROWB, lds, acc);
+                                            mp * ldq - col0 * ES, nk_m, lds, acc);
         } else {
             const int ldq = ldxt * ES;
             tile_product<T, C>(P + (int64_t)row0 * ldp, xtc + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
-                               mp * ES / C::ROWB, lds, acc);
+                               nk_m, lds, acc);
         }
     } else {   // the other Gram-space products, all with K = mp
         char *qtc = cur ? pr.qt1 : pr.qt0;
@@ -794,7 +801,7 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
         const int ldp = ldt * ES, ldq = ldt * ES;
         zero_acc<C>(acc);
         tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
-                           mp * ES / C::ROWB, lds, acc);
+                           nk_m, lds, acc);
     }
 
     // Epilogue, part 1: scaling, rounding, staging. Accumulator element
@@ -1281,23 +1288,37 @@ void launch_mode(TimedScope &ts, int32_t nt, hipStream_t st, const NsProb *probs
               cur, s_init, s_final, s_diag, do_product, first, eps, pieces);
 }
 
-// One group of matrices: tables, input staging, then the product launches.
-// TI is the input's type, T the workspace's. gram: the Gram-space iteration
-// in fp32 (T = float) with the trace ridge `ridge`; else NS in TI.
-template <typename TI, typename T>
-ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo> &info,
-                    const PieceLists &pieces, int32_t steps, float a, float b,
-                    float c, float eps, bool gram, float ridge, char *ws, const TableSizes &tsz, hipStream_t st) {
-    static_assert(sizeof(T) >= sizeof(TI), "workspace type");
-    const int64_t es = sizeof(T), esi = sizeof(TI);
-    const int bm = gram ? 128 : pick_tile(group, info, es);
+// The device tables of one group of matrices, built on the host, and what its
+// launches need. Each group has its own table layout (`tsz`, over its members
+// only) at the head of the workspace; the matrices' buffers start after the
+// head sized for the whole call.
+struct GroupPlan {
+    int bm = 256;                 // product tile edge
+    TableSizes tsz{};             // this group's table layout
+    std::vector<char> tables;     // tsz.o_partials() bytes, as they go to the device
+    int32_t nsyrk = 0, ngemm = 0, nsq = 0, nptiles = 0;
+    double f_syrk_x = 0, f_syrk_a = 0, f_gemm = 0, f_sq = 0, norm_bytes = 0;
+    size_t staging_off = 0;       // where its tables sit in the call's staging buffer
+};
+
+// Builds the tables of one group. TI's size is esi, the workspace type's es.
+// gram: the Gram-space workspace layout.
+GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatInfo> &info,
+                      const PieceLists &pieces, float b, float c, bool gram, int64_t es, int64_t esi,
+                      char *ws, size_t head_bytes) {
+    GroupPlan g;
+    g.bm = gram ? 128 : pick_tile(group, info, es);
+    const int bm = g.bm;
+    std::vector<MatInfo> members;
+    members.reserve(group.size());
+    for (int32_t idx : group) members.push_back(info[idx]);
+    g.tsz = table_sizes(members);
     std::vector<NsProb> probs;
     std::vector<TileRef> syrk, gemm, sq, ptiles;
     std::vector<RowPiece> gpieces;
-    char *base = ws + tsz.total;
-    float *partials = reinterpret_cast<float *>(ws + tsz.o_partials());
+    char *base = ws + head_bytes;
+    float *partials = reinterpret_cast<float *>(ws + g.tsz.o_partials());
     int64_t part_off = 0;
-    double f_syrk_x = 0, f_syrk_a = 0, f_gemm = 0, norm_bytes = 0;
     for (int32_t idx : group) {
         const MatInfo &mi = info[idx];
         NsProb p{};
@@ -1374,57 +1395,62 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                 set_band(ptiles.back(), kPrepTile);
             }
         const double m = (double)mi.m, n = (double)mi.n;
-        f_syrk_x += m * (m + 1) * n;                                            // X X^T, or G
-        f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
-        f_gemm += 2 * m * m * n;                                                // B X, or Q X0
+        g.f_syrk_x += m * (m + 1) * n;                                            // X X^T, or G
+        g.f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
+        g.f_gemm += 2 * m * m * n;                                                // B X, or Q X0
+        g.f_sq += 2.0 * m * m * m;                                                // a full m x m product
         // input read, X0 written (padded), and X0^T when it is kept
-        norm_bytes += m * n * esi + (mi.kmajor ? 1.0 : 2.0) * (double)mi.mp * (double)mi.np * es;
+        g.norm_bytes += m * n * esi + (mi.kmajor ? 1.0 : 2.0) * (double)mi.mp * (double)mi.np * es;
     }
-    if (probs.empty()) return NS_OK;
     deal_to_xcds(syrk);
     deal_to_xcds(gemm);
     deal_to_xcds(sq);
-
-    // The tables go to pinned host memory; the first kernel reads its own from
-    // there and copies all of them into the workspace head.
-    const size_t table_bytes = tsz.o_partials();   // a multiple of 256
-    int slot;
-    void *staging, *staging_dev;
-    ns_status sst = staging_acquire(table_bytes, &slot, &staging, &staging_dev);
-    if (sst) return sst;
-    char *host = static_cast<char *>(staging);
+    g.nsyrk = (int32_t)syrk.size();
+    g.ngemm = (int32_t)gemm.size();
+    g.nsq = (int32_t)sq.size();
+    g.nptiles = (int32_t)ptiles.size();
+    g.tables.assign(g.tsz.o_partials(), 0);   // a multiple of 256
     auto put = [&](size_t off, const void *src, size_t bytes) {
-        if (bytes) std::memcpy(host + off, src, bytes);
+        if (bytes) std::memcpy(g.tables.data() + off, src, bytes);
     };
     put(0, probs.data(), probs.size() * sizeof(NsProb));
-    put(tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
-    put(tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
-    put(tsz.o_sq(), sq.data(), sq.size() * sizeof(TileRef));
-    put(tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
-    put(tsz.o_pieces(), gpieces.data(), gpieces.size() * sizeof(RowPiece));
-    const char *hdev = static_cast<const char *>(staging_dev);
+    put(g.tsz.o_syrk(), syrk.data(), syrk.size() * sizeof(TileRef));
+    put(g.tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
+    put(g.tsz.o_sq(), sq.data(), sq.size() * sizeof(TileRef));
+    put(g.tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
+    put(g.tsz.o_pieces(), gpieces.data(), gpieces.size() * sizeof(RowPiece));
+    return g;
+}
 
+// Enqueues one group: input staging (which reads the group's tables from
+// `hdev`, the device's view of its part of the staging buffer, and copies them
+// into the workspace head), then the product launches. TI is the input's
+// type, T the workspace's. gram: the Gram-space iteration in fp32 (T = float)
+// with the trace ridge `ridge`; else NS in TI. Returns NS_ERR_HIP if a launch
+// fails.
+template <typename TI, typename T>
+ns_status launch_group(const GroupPlan &g, int32_t steps, float a, float b, float c, float eps, bool gram,
+                       float ridge, char *ws, const char *hdev, hipStream_t st) {
+    static_assert(sizeof(T) >= sizeof(TI), "workspace type");
+    const TableSizes &tsz = g.tsz;
+    const int bm = g.bm;
     const NsProb *d_probs = reinterpret_cast<const NsProb *>(ws);
     const TileRef *d_syrk = reinterpret_cast<const TileRef *>(ws + tsz.o_syrk());
     const TileRef *d_gemm = reinterpret_cast<const TileRef *>(ws + tsz.o_gemm());
     const TileRef *d_sq = reinterpret_cast<const TileRef *>(ws + tsz.o_sq());
     const TileRef *d_ptiles = reinterpret_cast<const TileRef *>(ws + tsz.o_ptiles());
     const RowPiece *d_pieces = reinterpret_cast<const RowPiece *>(ws + tsz.o_pieces());
-    const int32_t npt = (int32_t)ptiles.size();
-
+    const int32_t npt = g.nptiles;
     {
-        TimedScope ts(kTimeNorm, norm_bytes);
+        TimedScope ts(kTimeNorm, g.norm_bytes);
         ts.launch(ns_prepare_kernel<TI, T>, dim3((unsigned)npt), dim3(kPrepThreads), st,
-                           reinterpret_cast<const NsProb *>(hdev),
-                           reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
-                           reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
-                           (int32_t)(table_bytes / 16), reinterpret_cast<const RowPiece *>(hdev + tsz.o_pieces()));
-        const hipError_t le = hipGetLastError();
-        if ((sst = staging_release(slot, st, le == hipSuccess))) return sst;
-        if (le != hipSuccess) return fail(NS_ERR_HIP, "launch failed: %s", hipGetErrorString(le));
+                  reinterpret_cast<const NsProb *>(hdev), reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()),
+                  npt, reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
+                  (int32_t)(g.tables.size() / 16), reinterpret_cast<const RowPiece *>(hdev + tsz.o_pieces()));
+        NSQ_HIP(hipGetLastError());
         if (steps == 0)
-            ts.launch(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), st, d_probs,
-                               d_ptiles, npt, eps, d_pieces);
+            ts.launch(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), st, d_probs, d_ptiles, npt,
+                      eps, d_pieces);
     }
     NSQ_HIP(hipGetLastError());
     if (gram) {
@@ -1434,11 +1460,10 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                 const bool fused = c != 0.f && std::isfinite(ratio);
                 const float si = fused ? ratio : b, sf = fused ? c : 1.f;
                 const int32_t prod = fused ? 1 : 0;
-                const int32_t nsy = (int32_t)syrk.size(), nge = (int32_t)gemm.size(), nsq = (int32_t)sq.size();
-                double f_sq = 0;   // one full m x m product per matrix: 2 m^3
-                for (int32_t idx : group) f_sq += 2.0 * (double)info[idx].m * info[idx].m * info[idx].m;
+                const int32_t nsy = g.nsyrk, nge = g.ngemm, nsq = g.nsq;
+                const double f_sq = g.f_sq;   // one full m x m product per matrix: 2 m^3
                 {
-                    TimedScope ts(kTimeSyrkX, f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
+                    TimedScope ts(kTimeSyrkX, g.f_syrk_x);   // G = s^2 X0 X0^T + ridge tr(G)/m I
                     launch_mode<T, Small, kGramG>(ts, nsy, st, d_probs, d_syrk, 0, 1.f, 1.f, ridge, 1, 1, eps, d_pieces);
                 }
                 {
@@ -1465,7 +1490,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
                     qcur ^= 1;
                 }
                 {
-                    TimedScope ts(kTimeFinal, f_gemm);   // out = s Q X0
+                    TimedScope ts(kTimeFinal, g.f_gemm);   // out = s Q X0
                     launch_mode<T, Small, kGramOut, true, TI>(ts, nge, st, d_probs, d_gemm, qcur, 1.f, 1.f, 0.f, 1, 1,
                                                               eps, d_pieces);
                 }
@@ -1475,7 +1500,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
         return NS_OK;
     }
     int cur = 0;
-    const double work[3] = {f_syrk_x, f_syrk_a, f_gemm};
+    const double work[3] = {g.f_syrk_x, g.f_syrk_a, g.f_gemm};
     // B' = a I + b A + c A A as c (b / c A + A A) + a I: the accumulators of the
     // A A product start at (b / c) A. With c == 0, or b / c out of fp32 range
     // (c A A is then below fp32 resolution of b A), B' = b A + a I and the
@@ -1487,7 +1512,7 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     for (int32_t s = 0; s < steps; ++s) {
         for (int mode = kSyrkX; mode <= kGemmBX; ++mode) {
             const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;
-            const int32_t nt = (int32_t)(mode == kGemmBX ? gemm.size() : syrk.size());
+            const int32_t nt = mode == kGemmBX ? g.ngemm : g.nsyrk;
             const bool last = mode == kGemmBX && s == steps - 1;
             const int kind = last ? kTimeFinal : mode == kSyrkX ? kTimeSyrkX : mode == kSyrkA ? kTimeSyrkA
                                                                                   : kTimeProduct;
@@ -1512,13 +1537,19 @@ ns_status run_group(const std::vector<int32_t> &group, const std::vector<MatInfo
     return NS_OK;
 }
 
-// The common path of the entry points: every active tensor's input and output
-// rows are given as row pieces. gram: Gram-space iteration (info described
-// with the Gram workspace).
-ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype,
-                        int32_t steps, float a, float b, float c, float eps, const int32_t *order,
-                        void *workspace, size_t workspace_bytes, hipStream_t hs, bool gram = false,
-                        float ridge = 0.f) {
+// A call split into groups: groups[wave_start[w] .. wave_start[w + 1]) make
+// wave w (a plain call is one wave).
+struct CallPlan {
+    std::vector<GroupPlan> groups;
+    std::vector<size_t> wave_start{0};
+};
+
+// Validates a call and appends its groups (consecutive matrices in dispatch
+// order whose buffers fit the workspace together) to `plan` as one wave.
+// Nothing is enqueued. gram: Gram-space workspace layout.
+ns_status plan_call(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype, int32_t steps,
+                    float b, float c, const int32_t *order, void *workspace, size_t workspace_bytes, bool gram,
+                    CallPlan &plan) {
     const int32_t n = (int32_t)info.size();
     // Dispatch order: caller's permutation, else descending cost (ties by index).
     std::vector<int32_t> ord(n);
@@ -1547,36 +1578,89 @@ ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &piec
         return fail(NS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(NS_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, need);
-    // Groups of consecutive matrices (in dispatch order) whose buffers fit.
+    const int64_t es = gram ? 4 : dtype == NS_BF16 ? 2 : 4, esi = dtype == NS_BF16 ? 2 : 4;
     const size_t room = workspace_bytes - tsz.total;
     std::vector<int32_t> group;
     size_t used = 0;
-    auto flush = [&]() -> ns_status {
-        if (group.empty()) return NS_OK;
-        char *ws = static_cast<char *>(workspace);
-        ns_status r;
-        if (gram)
-            r = dtype == NS_BF16 ? run_group<__bf16, float>(group, info, pieces, steps, a, b, c, eps, true, ridge, ws,
-                                                            tsz, hs)
-                                 : run_group<float, float>(group, info, pieces, steps, a, b, c, eps, true, ridge, ws,
-                                                           tsz, hs);
-        else
-            r = dtype == NS_BF16 ? run_group<__bf16, __bf16>(group, info, pieces, steps, a, b, c, eps, false, 0.f,
-                                                             ws, tsz, hs)
-                                 : run_group<float, float>(group, info, pieces, steps, a, b, c, eps, false, 0.f, ws,
-                                                           tsz, hs);
+    auto flush = [&]() {
+        if (group.empty()) return;
+        plan.groups.push_back(build_group(group, info, pieces, b, c, gram, es, esi, static_cast<char *>(workspace),
+                                          tsz.total));
         group.clear();
         used = 0;
-        return r;
     };
-    ns_status st;
     for (int32_t i : ord) {
         if (!info[i].active) continue;
-        if (used + info[i].buf_bytes > room && (st = flush())) return st;
+        if (used + info[i].buf_bytes > room) flush();
         group.push_back(i);
         used += info[i].buf_bytes;
     }
-    return flush();
+    flush();
+    plan.wave_start.push_back(plan.groups.size());
+    return NS_OK;
+}
+
+// Enqueues a planned call: every group's tables go into one pinned staging
+// buffer, then wave by wave (after its ready event, if any) the groups' launches.
+// Only a HIP runtime failure can stop it after the first enqueue.
+ns_status launch_call(CallPlan &plan, ns_dtype dtype, int32_t steps, float a, float b, float c, float eps,
+                      bool gram, float ridge, void *workspace, void *const *ready_events, hipStream_t hs) {
+    if (plan.groups.empty() && !ready_events) return NS_OK;
+    size_t total = 0;
+    for (GroupPlan &g : plan.groups) {
+        g.staging_off = total;
+        total += g.tables.size();   // multiples of 256
+    }
+    int slot = -1;
+    void *staging = nullptr, *staging_dev = nullptr;
+    if (total) {
+        ns_status sst = staging_acquire(total, &slot, &staging, &staging_dev);
+        if (sst) return sst;
+        for (const GroupPlan &g : plan.groups)
+            std::memcpy(static_cast<char *>(staging) + g.staging_off, g.tables.data(), g.tables.size());
+    }
+    char *ws = static_cast<char *>(workspace);
+    ns_status st = NS_OK;
+    bool launched = false;
+    const size_t waves = plan.wave_start.size() - 1;
+    for (size_t w = 0; w < waves && st == NS_OK; ++w) {
+        if (ready_events && ready_events[w]) {
+            const hipError_t e = hipStreamWaitEvent(hs, reinterpret_cast<hipEvent_t>(ready_events[w]), 0);
+            if (e != hipSuccess) {
+                st = fail(NS_ERR_HIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
+                break;
+            }
+        }
+        for (size_t k = plan.wave_start[w]; k < plan.wave_start[w + 1] && st == NS_OK; ++k) {
+            const GroupPlan &g = plan.groups[k];
+            const char *hdev = static_cast<const char *>(staging_dev) + g.staging_off;
+            launched = true;
+            if (gram)
+                st = dtype == NS_BF16 ? launch_group<__bf16, float>(g, steps, a, b, c, eps, true, ridge, ws, hdev, hs)
+                                      : launch_group<float, float>(g, steps, a, b, c, eps, true, ridge, ws, hdev, hs);
+            else
+                st = dtype == NS_BF16 ? launch_group<__bf16, __bf16>(g, steps, a, b, c, eps, false, 0.f, ws, hdev, hs)
+                                      : launch_group<float, float>(g, steps, a, b, c, eps, false, 0.f, ws, hdev, hs);
+        }
+    }
+    if (slot >= 0) {
+        const ns_status rs = staging_release(slot, hs, launched);
+        if (st == NS_OK) st = rs;
+    }
+    return st;
+}
+
+// The common path of the entry points: every active tensor's input and output
+// rows are given as row pieces. gram: Gram-space iteration (info described
+// with the Gram workspace).
+ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype,
+                        int32_t steps, float a, float b, float c, float eps, const int32_t *order,
+                        void *workspace, size_t workspace_bytes, hipStream_t hs, bool gram = false,
+                        float ridge = 0.f) {
+    CallPlan plan;
+    ns_status st = plan_call(info, pieces, dtype, steps, b, c, order, workspace, workspace_bytes, gram, plan);
+    if (st) return st;
+    return launch_call(plan, dtype, steps, a, b, c, eps, gram, ridge, workspace, nullptr, hs);
 }
 
 ns_status check_coefficients(int32_t steps, float a, float b, float c, float eps) {
@@ -1752,21 +1836,18 @@ extern "C" ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, c
     workspace_need(info, &all, &need);
     if (!workspace || workspace_bytes < need)
         return fail(NS_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, need);
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(NS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    // Every wave is planned (and every argument checked) before anything is
+    // enqueued; then the waves go out in order, each after its event.
+    CallPlan plan;
     for (int32_t w = 0; w < num_waves; ++w) {
         std::vector<MatInfo> wi = info;
-        bool any = false;
-        for (int32_t i = 0; i < n; ++i) {
-            wi[i].active = info[i].active && wave_of[i] == w;
-            any = any || wi[i].active;
-        }
-        if (ready_events && ready_events[w])
-            NSQ_HIP(hipStreamWaitEvent(hs, reinterpret_cast<hipEvent_t>(ready_events[w]), 0));
-        if (!any) continue;
-        if ((st = orthogonalize(wi, pieces, dtype, steps, a, b, c, eps, nullptr, workspace, workspace_bytes, hs)))
+        for (int32_t i = 0; i < n; ++i) wi[i].active = info[i].active && wave_of[i] == w;
+        if ((st = plan_call(wi, pieces, dtype, steps, b, c, nullptr, workspace, workspace_bytes, false, plan)))
             return st;
     }
-    return NS_OK;
+    return launch_call(plan, dtype, steps, a, b, c, eps, false, 0.f, workspace, ready_events,
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" ns_status ns_gram_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype, size_t *bytes,

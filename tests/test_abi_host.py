@@ -361,3 +361,35 @@ def test_route_plan_bands_strided_pieces():
     assert rag["device_table_bytes"] == 33 * 3 * entry
     small = nsq.ns_route_plan_query(nsq.ns_route_plan_create_axis([(30, 64)], 2, [[32, 32]], [1], [0], 2))
     assert small["device_table_bytes"] == max(16, 2 * entry)
+
+
+def test_errors_come_before_any_enqueue():
+    # Every argument error is found before the first HIP call: without a GPU
+    # any HIP call fails with NS_ERR_HIP (-9), so each of these returning its
+    # own code shows that nothing was enqueued first. The event handle is a
+    # stand-in that must never be touched.
+    lib = nsq.lib()
+    shapes = [(300, 200), (64, 1000), (5, 7)]
+    sh = _lib._shapes(shapes)
+    need, minimum = nsq.ns_workspace_bytes(shapes, nsq.NS_BF16)
+    assert minimum < need
+    ptrs = _lib._arr(ctypes.c_void_p, [4096, 8192, 16384])
+    wave = _lib._arr(ctypes.c_int32, [0, 1, 1])
+    events = _lib._arr(ctypes.c_void_p, [0x1000, 0x2000])
+
+    def waves(ws, nbytes):
+        return lib.ns_orthogonalize_waves(3, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                          0, 5, 3.4, -4.7, 2.0, 1e-7, ctypes.addressof(wave), 2,
+                                          ctypes.addressof(events), ws, nbytes, None)
+    assert waves((1 << 20) + 128, need) == -7       # misaligned workspace: no event wait enqueued
+    assert waves(1 << 20, minimum - 1) == -7        # below the minimum
+    assert waves(None, need) == -7
+
+    def batched(ws, nbytes, order=None):
+        return lib.ns_orthogonalize_batched(3, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                            0, 5, 3.4, -4.7, 2.0, 1e-7, order, ws, nbytes, None)
+    # a minimum workspace makes several groups; every one is planned first
+    bad = _lib._arr(ctypes.c_int32, [0, 0, 1])
+    assert batched(1 << 20, minimum, ctypes.addressof(bad)) == -1
+    assert batched((1 << 20) + 128, minimum) == -7
+    assert batched(1 << 20, minimum - 1) == -7

@@ -1,17 +1,29 @@
 """GPU checks of wave dispatch (ns_orthogonalize_waves).
 
-Bar: bit-identical to ns_orthogonalize_batched on the same tensors; each
-wave waits for its ready event: inputs written on another stream after a
-long run of unrelated work, with an event per wave, come out exactly as
-when they were ready from the start.
+Bar: every wave output within the bf16 tolerance of the fp64 oracle,
+element by element, and bit-identical to ns_orthogonalize_batched on the same
+tensors; each wave waits for its ready event: inputs written on another
+stream after a long run of unrelated work, with an event per wave, come out
+exactly as when they were ready from the start (and within the oracle's
+tolerance).
 """
 
 import numpy as np
 import pytest
 
 import newton_schulz_quintic_amd as nsq
-from tests.helpers import log, to_device, to_host
+from tests.helpers import TOL, host_to_f64, log, oracle_ns, to_device, to_host
 from workloads import host_matrix
+
+COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def _check_oracle(hosts, outs):
+    for i, (h, o) in enumerate(zip(hosts, outs)):
+        want = oracle_ns(h, "bf16", 5, COEFFS, 1e-7)
+        got = host_to_f64(to_host(o, "bf16"), "bf16").reshape(want.shape)
+        err = float(np.max(np.abs(got - want))) if want.size else 0.0
+        assert err <= TOL["bf16"], (i, SHAPES[i], err)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +51,7 @@ def test_waves_bit_identical_to_batched():
     log("waves: 3 waves, no events")
     nsq.ns_orthogonalize_waves(ins, outs, wave_of, num)
     torch.cuda.synchronize()
+    _check_oracle(hosts, outs)
     for w, o in zip(want, outs):
         assert np.array_equal(w, to_host(o, "bf16"))
     # a tensor left out of every wave is untouched
@@ -77,5 +90,6 @@ def test_waves_wait_for_their_events():
     nsq.ns_orthogonalize_waves(ins, outs, wave_of, num, ready_events=events, workspace=ws,
                                stream=consumer)
     torch.cuda.synchronize()
+    _check_oracle(hosts, outs)
     for w, o in zip(want, outs):
         assert np.array_equal(w, to_host(o, "bf16"))
