@@ -47,13 +47,14 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "ns_kernels.hip")
 ROUTE_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "route.hip")
 PROFILES = os.path.join(ROOT, "profiles")
-TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a"}
+TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a", 6: "small"}
 # What each timing kind is, and the part of its rocprofv3 kernel name that picks it.
 PHASES = {
     "syrk_x": ("ns_product_kernel<bf16, A = X X^T, upper tiles>", "ELi0ELb0E", "mfma"),
     "syrk_a": ("ns_product_kernel<bf16, B' = a I + b A + c A A, upper tiles>", "ELi1ELb0E", "mfma"),
     "bx": ("ns_product_kernel<bf16, X' = B' X>", "ELi2ELb0E", "mfma"),
     "bx_final": ("ns_product_kernel<bf16, X' = B' X, last step writes the output>", "ELi2ELb1E", "mfma"),
+    "small": ("ns_small_kernel (every step of the matrices with m <= 128)", "ns_small_kernel", "mfma"),
     "norm": ("ns_prepare_kernel (input staging + norm partials)", "ns_prepare_kernel", "hbm"),
     "route": ("route_copy_kernel (pack / unpack)", "route_copy_kernel", "hbm"),
 }
@@ -679,7 +680,7 @@ def main():
                            ("alg_flops_per_launch" if bound == "mfma" else "alg_bytes_per_launch"): kwork / kn,
                            "launches": kn}
         phases = {}
-        for name in ("syrk_x", "syrk_a", "bx", "bx_final"):
+        for name in ("syrk_x", "syrk_a", "bx", "bx_final", "small"):
             pms, pn, pwork = t[name]
             if pn:
                 tf = (pwork / pn) / (pms / pn * 1e-3) / 1e12

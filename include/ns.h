@@ -24,6 +24,8 @@
  *                        the group has enough 256-tiles to fill the GPU)
  *   NS_KMAJOR_MAX=K      largest padded m for which B.X reads X in place
  *                        (default 1024; larger m keep a transposed copy)
+ *   NS_SMALL_MAX=M       largest m of the small size class (default 128, at
+ *                        most 128; 0 sends every matrix down the tiled path)
  *   NS_ROUTE_MAX_GRID=W  cap on pack/unpack workgroups (default 2^23, one
  *                        16 KiB chunk each; a lower cap gives each several)
  *
@@ -374,10 +376,11 @@ ns_status ns_orthogonalize_waves(int32_t n, const ns_shape *shapes, const void *
  *       1 = pack/unpack kernel, 2 = input staging (with steps = 0, also the
  *       scaling kernel after it),
  *       3 = the final B X launch of each call (it writes the caller's output),
- *       4 = the A = X X^T product kernel, 5 = the B = b A + c A A product kernel.
+ *       4 = the A = X X^T product kernel, 5 = the B = b A + c A A product kernel,
+ *       6 = the small-class kernel (every step of the matrices with m <= 128).
  * total_ms: summed durations; launches: number of launches; work: summed
- * algorithmic work of those launches (flops for kinds 0, 3, 4, 5; bytes moved
- * for kind 1; bytes read + written for kind 2). */
+ * algorithmic work of those launches (flops for kinds 0, 3, 4, 5, 6; bytes
+ * moved for kind 1; bytes read + written for kind 2). */
 ns_status ns_timing_enable(int32_t kinds);
 ns_status ns_timing_read(int32_t kind, double *total_ms, int64_t *launches, double *work);
 

@@ -499,7 +499,8 @@ def ns_timing_enable(kinds) -> None:
 
 def ns_timing_read(kind: int) -> tuple[float, int, float]:
     """(total_ms, launches, work) for kind 0 = B X product kernel, 1 = pack/unpack,
-    2 = norm, 3 = final B X launch, 4 = A = X X^T kernel, 5 = A A kernel."""
+    2 = norm, 3 = final B X launch, 4 = A = X X^T kernel, 5 = A A kernel,
+    6 = small-class kernel."""
     ms, cnt, work = ctypes.c_double(0), _I64(0), ctypes.c_double(0)
     _check(lib().ns_timing_read(kind, ctypes.addressof(ms), ctypes.addressof(cnt),
                                 ctypes.addressof(work)))

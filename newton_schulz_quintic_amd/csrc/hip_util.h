@@ -20,7 +20,8 @@ namespace nsq {
 // records, so a pair spans the kernel's execution only (the figure rocprofv3
 // reports), not the launch's dispatch. kTimeProduct covers the B X product
 // kernel (all but the final step); kTimeSyrkX / kTimeSyrkA the two symmetric
-// products; kTimeFinal the last B X.
+// products; kTimeFinal the last B X; kTimeSmall the small-class kernel (every
+// step of every small matrix in one launch).
 enum TimingKind {
     kTimeProduct = 0,
     kTimeRoute = 1,
@@ -28,7 +29,8 @@ enum TimingKind {
     kTimeFinal = 3,
     kTimeSyrkX = 4,
     kTimeSyrkA = 5,
-    kTimeKinds = 6
+    kTimeSmall = 6,
+    kTimeKinds = 7
 };
 
 // Whether launches of `kind` are timed now.

@@ -61,7 +61,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPad = 256;           // every matrix is padded to a multiple of this (zero padding)
+constexpr int kPad = 256;           // tiled matrices are padded to a multiple of this (zero padding)
+constexpr int kSmallPad = 128;      // ... matrices of the small size class to a multiple of this
+constexpr int kSmallM = 128;        // largest m of the small size class
 constexpr int kPrepTile = 128;      // tile edge of the input-staging pass
 constexpr int kPrepThreads = 256;   // its threads
 constexpr int kScaleSlots = 256;    // width of the fixed-order reduction of the norm partials
@@ -82,7 +84,7 @@ struct NsProb {
     char *qt0, *qt1, *at;    // Gram-space only: Q^T ping/pong, A^T
     float *partials;   // nparts fp32 sums of squares, one per staging tile
     int32_t m, n;      // oriented sizes (m <= n)
-    int32_t mp, np;    // padded to kPad
+    int32_t mp, np;    // padded to kPad (kSmallPad for the small size class)
     int32_t ldx;       // row stride of X (elements, > np)
     int32_t ldxt;      // row stride of X^T (elements, > mp)
     int32_t ldt;       // row stride of A and B (elements, > mp)
@@ -711,20 +713,21 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
 // A0 = s^2 (G G^T), and B0' is stored scaled by s, so X1 = (s B0') G.
 // LAST (kGemmBX only): the final step writes B' X straight to the caller's
 // output in the input's orientation instead of into the workspace.
+// LDS bytes of one product tile: the operand ring, or the staged output tile.
+template <typename T, class C> constexpr int tile_lds_bytes() {
+    return C::RING > C::BM * C::BM * (int)sizeof(T) ? C::RING : C::BM * C::BM * (int)sizeof(T);
+}
+
+// One BM x BM tile `tr` of matrix `pr` for the product MODE (see Mode). The
+// caller's workgroup runs it whole; `lds` is tile_lds_bytes() of LDS, free on
+// entry and free again on return.
 template <typename T, class C, int MODE, bool LAST, typename TO = T>
-__global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
-    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
-    float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
-    const RowPiece *__restrict__ pieces) {
+__device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int32_t cur, float s_init,
+                                         float s_final, float s_diag, int32_t do_product, int32_t first,
+                                         float eps, const RowPiece *__restrict__ pieces, char *lds) {
     static_assert(!LAST || MODE == kGemmBX || MODE == kGramOut, "only B X or the Gram-space output writes out");
     static_assert(MODE != kGramOut || LAST, "the Gram-space output launch is a last launch");
     constexpr int BM = C::BM, ES = sizeof(T);
-    constexpr int LDS_BYTES = C::RING > BM * BM * ES ? C::RING : BM * BM * ES;   // ring, or a staged tile
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-    const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
-    if (tile_id >= ntiles) return;
-    const TileRef tr = tiles[tile_id];
-    const NsProb &pr = probs[tr.prob];
     const int mp = pr.mp, np = pr.np;
     const int row0 = tr.ti * BM, col0 = tr.tj * BM;
     const int ldx = pr.ldx, ldxt = pr.ldxt, ldt = pr.ldt;
@@ -895,6 +898,74 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
                 store_chunk_checked<TS>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
             }
         }
+    }
+}
+
+// One product launch: every tile of `tiles` (hardware workgroup ids remapped
+// so each XCD takes a contiguous range of the list).
+template <typename T, class C, int MODE, bool LAST, typename TO = T>
+__global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_kernel(
+    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
+    float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
+    const RowPiece *__restrict__ pieces) {
+    __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<T, C>()];
+    const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
+    if (tile_id >= ntiles) return;
+    const TileRef tr = tiles[tile_id];
+    run_tile<T, C, MODE, LAST, TO>(probs[tr.prob], tr, cur, s_init, s_final, s_diag, do_product, first, eps,
+                                   pieces, lds);
+}
+
+
+// Ends a phase of the small-matrix kernel: every thread's global stores of
+// this phase are complete (release at workgroup scope), the workgroup meets,
+// and its later loads see them (acquire at workgroup scope). Only this
+// workgroup reads what it wrote, and it runs on one CU, so workgroup scope is
+// enough; agent scope would write back and invalidate the XCD's whole L2 at
+// every phase.
+// The explicit vmcnt(0) makes every store of this thread complete at the L2
+// before the barrier, whatever path the next phase's direct-to-LDS loads take.
+__device__ __forceinline__ void phase_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmcnt<0>();
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// The small size class ("[GTP][Muon] Optimize Muon step performance", Current
+// Progress: shape-batched NS over many small tensors): one workgroup runs
+// every step of one matrix with m <= kSmallM (padded to 128 x np), phase after
+// phase: the X X^T tile, the A A tile, then the np / 128 tiles of B' X
+// (bx_tiles[mats[i].piece ..] with their output pieces), each phase finished
+// by the whole workgroup before the next starts. The tiles are the product
+// kernel's 128-tiles, so the bits equal the tiled path's.
+template <typename T>
+__global__ __launch_bounds__(Small::THREADS, 2) void ns_small_kernel(
+    const NsProb *__restrict__ probs, const TileRef *__restrict__ mats, const TileRef *__restrict__ bx_tiles,
+    int32_t steps, float sa_init, float sa_final, float s_diag, int32_t sa_product, float eps,
+    const RowPiece *__restrict__ pieces) {
+    __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<T, Small>()];
+    const TileRef m = mats[blockIdx.x];
+    const NsProb &pr = probs[m.prob];
+    const TileRef diag{m.prob, 0, 0, 0, 1};
+    int32_t cur = 0;
+    for (int32_t s = 0; s < steps; ++s) {
+        const int32_t first = s == 0;
+        run_tile<T, Small, kSyrkX, false>(pr, diag, cur, 1.f, 1.f, 0.f, 1, first, eps, pieces, lds);
+        phase_fence();
+        run_tile<T, Small, kSyrkA, false>(pr, diag, cur, sa_init, sa_final, s_diag, sa_product, first, eps, pieces,
+                                          lds);
+        phase_fence();
+        for (int32_t k = 0; k < m.npiece; ++k) {
+            const TileRef tr = bx_tiles[m.piece + k];
+            if (k > 0) __syncthreads();   // the previous tile's epilogue is done with the LDS
+            if (s + 1 < steps)
+                run_tile<T, Small, kGemmBX, false>(pr, tr, cur, 1.f, 1.f, 0.f, 1, first, eps, pieces, lds);
+            else
+                run_tile<T, Small, kGemmBX, true>(pr, tr, cur, 1.f, 1.f, 0.f, 1, first, eps, pieces, lds);
+        }
+        phase_fence();
+        cur ^= 1;
     }
 }
 
@@ -1076,6 +1147,7 @@ struct MatInfo {
     int64_t rows, cols, m, n, mp, np;
     bool tall, active;
     bool kmajor;       // B X reads X K-major; no X^T arrays
+    bool small;        // small size class: one workgroup per matrix (ns_small_kernel)
     int64_t nparts, syrk_tiles, gemm_tiles;
     int64_t sq_tiles;  // full m x m grid (Gram-space products only)
     int64_t npieces;   // row pieces its input / output is split into
@@ -1099,6 +1171,13 @@ inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(
 int64_t kmajor_max_k() {
     if (const char *env = getenv("NS_KMAJOR_MAX")) return atoll(env);
     return 1024;
+}
+
+// Largest m of the small size class; NS_SMALL_MAX=0 sends every matrix down
+// the tiled path (tests compare the two, which give the same bits).
+int64_t small_max_m() {
+    if (const char *env = getenv("NS_SMALL_MAX")) return std::min<int64_t>(atoll(env), kSmallM);
+    return kSmallM;
 }
 
 // gram: the Gram-space workspace (fp32 X0, G, Q and Q^T ping/pong, Q G, A,
@@ -1126,12 +1205,14 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
             round_up(mi.n, kPad) * (round_up(mi.m, kPad) + kRowPadBytes / es) * es >= (1ll << 31))
             return fail(NS_ERR_OVERFLOW, "tensor %d: %lld x %lld is too large", i,
                         (long long)mi.rows, (long long)mi.cols);
-        mi.mp = round_up(mi.m, kPad);
-        mi.np = round_up(mi.n, kPad);
+        mi.small = !gram && mi.m <= small_max_m();
+        const int64_t pad = mi.small ? kSmallPad : kPad;
+        mi.mp = round_up(mi.m, pad);
+        mi.np = round_up(mi.n, pad);
         // table sizing uses the smaller product tile (more tiles)
         const int64_t tm = mi.mp / 128, tn = mi.np / 128;
-        mi.syrk_tiles = tm * (tm + 1) / 2;
-        mi.gemm_tiles = tm * tn;
+        mi.syrk_tiles = mi.small ? 0 : tm * (tm + 1) / 2;
+        mi.gemm_tiles = tm * tn;   // the small class keeps its B X tiles in a list of their own
         mi.sq_tiles = gram ? tm * tm : 0;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.npieces = 1;
@@ -1144,20 +1225,22 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
 
 // Workspace head: device tables for one group, then fp32 norm partials.
 struct TableSizes {
-    size_t probs, syrk, gemm, sq, ptiles, pieces, partials, total;
+    size_t probs, syrk, gemm, sq, ptiles, smalls, pieces, partials, total;
     size_t o_syrk() const { return probs; }
-    size_t o_gemm() const { return o_syrk() + syrk; }
+    size_t o_gemm() const { return o_syrk() + syrk; }   // tiled B X tiles, then the small class's
     size_t o_sq() const { return o_gemm() + gemm; }
     size_t o_ptiles() const { return o_sq() + sq; }
-    size_t o_pieces() const { return o_ptiles() + ptiles; }
+    size_t o_smalls() const { return o_ptiles() + ptiles; }
+    size_t o_pieces() const { return o_smalls() + smalls; }
     size_t o_partials() const { return o_pieces() + pieces; }
 };
 
 TableSizes table_sizes(const std::vector<MatInfo> &info) {
-    int64_t np = 0, sy = 0, ge = 0, sq = 0, pa = 0, pc = 0;
+    int64_t np = 0, sy = 0, ge = 0, sq = 0, pa = 0, pc = 0, sm = 0;
     for (const MatInfo &mi : info) {
         if (!mi.active) continue;
         ++np;
+        sm += mi.small;
         sy += mi.syrk_tiles;
         ge += mi.gemm_tiles;
         sq += mi.sq_tiles;
@@ -1170,6 +1253,7 @@ TableSizes table_sizes(const std::vector<MatInfo> &info) {
     t.gemm = align256(ge * sizeof(TileRef));
     t.sq = align256(sq * sizeof(TileRef));
     t.ptiles = align256(pa * sizeof(TileRef));
+    t.smalls = align256(sm * sizeof(TileRef));
     t.pieces = align256(pc * sizeof(RowPiece));
     t.partials = align256(pa * sizeof(float));
     t.total = t.o_partials() + t.partials;
@@ -1213,6 +1297,7 @@ int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &inf
     }
     int64_t big_syrk = 0;
     for (int32_t idx : group) {
+        if (info[idx].small) continue;
         const int64_t t = info[idx].mp / 256;
         big_syrk += t * (t + 1) / 2;
     }
@@ -1296,8 +1381,9 @@ struct GroupPlan {
     int bm = 256;                 // product tile edge
     TableSizes tsz{};             // this group's table layout
     std::vector<char> tables;     // tsz.o_partials() bytes, as they go to the device
-    int32_t nsyrk = 0, ngemm = 0, nsq = 0, nptiles = 0;
+    int32_t nsyrk = 0, ngemm = 0, nsq = 0, nptiles = 0, nsmall = 0;
     double f_syrk_x = 0, f_syrk_a = 0, f_gemm = 0, f_sq = 0, norm_bytes = 0;
+    double f_small = 0;           // algorithmic flops of one step of the small class
     size_t staging_off = 0;       // where its tables sit in the call's staging buffer
 };
 
@@ -1314,7 +1400,7 @@ GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatIn
     for (int32_t idx : group) members.push_back(info[idx]);
     g.tsz = table_sizes(members);
     std::vector<NsProb> probs;
-    std::vector<TileRef> syrk, gemm, sq, ptiles;
+    std::vector<TileRef> syrk, gemm, sq, ptiles, smalls, sgemm;
     std::vector<RowPiece> gpieces;
     char *base = ws + head_bytes;
     float *partials = reinterpret_cast<float *>(ws + g.tsz.o_partials());
@@ -1377,13 +1463,23 @@ GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatIn
             band_of(pc, lo, lo + edge, &t.piece, &t.npiece);
             t.piece += pbase;
         };
-        const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
-        const size_t s0 = syrk.size(), g0 = gemm.size();
-        grouped_tiles(pid, tm, tm, true, syrk);
-        for (size_t k = s0; k < syrk.size(); ++k) syrk[k].piece = pbase;   // unused by the SYRK steps
-        grouped_tiles(pid, tm, tn, false, gemm);
-        for (size_t k = g0; k < gemm.size(); ++k) set_band(gemm[k], bm);
+        if (mi.small) {   // one entry; its B X tiles (0, tj) with their output pieces in sgemm
+            const int tn = (int)(mi.np / kSmallPad);
+            smalls.push_back(TileRef{pid, 0, 0, (int32_t)sgemm.size(), tn});
+            for (int tj = 0; tj < tn; ++tj) {
+                sgemm.push_back(TileRef{pid, 0, (uint16_t)tj, 0, 1});
+                set_band(sgemm.back(), kSmallPad);
+            }
+        } else {
+            const int tm = (int)(mi.mp / bm), tn = (int)(mi.np / bm);
+            const size_t s0 = syrk.size(), g0 = gemm.size();
+            grouped_tiles(pid, tm, tm, true, syrk);
+            for (size_t k = s0; k < syrk.size(); ++k) syrk[k].piece = pbase;   // unused by the SYRK steps
+            grouped_tiles(pid, tm, tn, false, gemm);
+            for (size_t k = g0; k < gemm.size(); ++k) set_band(gemm[k], bm);
+        }
         if (gram) {
+            const int tm = (int)(mi.mp / bm);
             const size_t q0 = sq.size();
             grouped_tiles(pid, tm, tm, false, sq);
             for (size_t k = q0; k < sq.size(); ++k) sq[k].piece = pbase;   // no caller memory touched
@@ -1395,9 +1491,16 @@ GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatIn
                 set_band(ptiles.back(), kPrepTile);
             }
         const double m = (double)mi.m, n = (double)mi.n;
-        g.f_syrk_x += m * (m + 1) * n;                                            // X X^T, or G
-        g.f_syrk_a += (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
-        g.f_gemm += 2 * m * m * n;                                                // B X, or Q X0
+        const double fx = m * (m + 1) * n;                                              // X X^T, or G
+        const double fa = (c != 0.f && std::isfinite(b / c)) ? m * m * (m + 1) : 0.0;   // A A (per step)
+        const double fb = 2 * m * m * n;                                                // B X, or Q X0
+        if (mi.small) {
+            g.f_small += fx + fa + fb;
+        } else {
+            g.f_syrk_x += fx;
+            g.f_syrk_a += fa;
+            g.f_gemm += fb;
+        }
         g.f_sq += 2.0 * m * m * m;                                                // a full m x m product
         // input read, X0 written (padded), and X0^T when it is kept
         g.norm_bytes += m * n * esi + (mi.kmajor ? 1.0 : 2.0) * (double)mi.mp * (double)mi.np * es;
@@ -1407,6 +1510,9 @@ GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatIn
     deal_to_xcds(sq);
     g.nsyrk = (int32_t)syrk.size();
     g.ngemm = (int32_t)gemm.size();
+    g.nsmall = (int32_t)smalls.size();
+    for (TileRef &t : smalls) t.piece += g.ngemm;   // the small class's B X tiles follow the tiled ones
+    gemm.insert(gemm.end(), sgemm.begin(), sgemm.end());
     g.nsq = (int32_t)sq.size();
     g.nptiles = (int32_t)ptiles.size();
     g.tables.assign(g.tsz.o_partials(), 0);   // a multiple of 256
@@ -1418,6 +1524,7 @@ GroupPlan build_group(const std::vector<int32_t> &group, const std::vector<MatIn
     put(g.tsz.o_gemm(), gemm.data(), gemm.size() * sizeof(TileRef));
     put(g.tsz.o_sq(), sq.data(), sq.size() * sizeof(TileRef));
     put(g.tsz.o_ptiles(), ptiles.data(), ptiles.size() * sizeof(TileRef));
+    put(g.tsz.o_smalls(), smalls.data(), smalls.size() * sizeof(TileRef));
     put(g.tsz.o_pieces(), gpieces.data(), gpieces.size() * sizeof(RowPiece));
     return g;
 }
@@ -1453,6 +1560,21 @@ ns_status launch_group(const GroupPlan &g, int32_t steps, float a, float b, floa
                       eps, d_pieces);
     }
     NSQ_HIP(hipGetLastError());
+    // B' = a I + b A + c A A as c (b / c A + A A) + a I: the accumulators of the
+    // A A product start at (b / c) A. With c == 0, or b / c out of fp32 range
+    // (c A A is then below fp32 resolution of b A), B' = b A + a I and the
+    // product is skipped.
+    const float ratio = c != 0.f ? b / c : 0.f;
+    const bool sa_fused = c != 0.f && std::isfinite(ratio);
+    const float sa_init = sa_fused ? ratio : b, sa_final = sa_fused ? c : 1.f;
+    const int32_t sa_product = sa_fused ? 1 : 0;
+    if (!gram && g.nsmall > 0 && steps > 0) {
+        const TileRef *d_small = reinterpret_cast<const TileRef *>(ws + tsz.o_smalls());
+        TimedScope ts(kTimeSmall, g.f_small * steps);
+        ts.launch(ns_small_kernel<T>, dim3((unsigned)g.nsmall), dim3(Small::THREADS), st, d_probs, d_small, d_gemm,
+                  steps, sa_init, sa_final, a, sa_product, eps, d_pieces);
+        NSQ_HIP(hipGetLastError());
+    }
     if (gram) {
         if constexpr (sizeof(T) == 4) {
             if (steps > 0) {
@@ -1501,14 +1623,7 @@ ns_status launch_group(const GroupPlan &g, int32_t steps, float a, float b, floa
     }
     int cur = 0;
     const double work[3] = {g.f_syrk_x, g.f_syrk_a, g.f_gemm};
-    // B' = a I + b A + c A A as c (b / c A + A A) + a I: the accumulators of the
-    // A A product start at (b / c) A. With c == 0, or b / c out of fp32 range
-    // (c A A is then below fp32 resolution of b A), B' = b A + a I and the
-    // product is skipped.
-    const float ratio = c != 0.f ? b / c : 0.f;
-    const bool sa_fused = c != 0.f && std::isfinite(ratio);
-    const float sa_init = sa_fused ? ratio : b, sa_final = sa_fused ? c : 1.f;
-    const int32_t sa_product = sa_fused ? 1 : 0;
+    if (g.nsyrk == 0 && g.ngemm == 0) return NS_OK;   // only small matrices
     for (int32_t s = 0; s < steps; ++s) {
         for (int mode = kSyrkX; mode <= kGemmBX; ++mode) {
             const TileRef *d_t = mode == kGemmBX ? d_gemm : d_syrk;

@@ -227,3 +227,45 @@ def test_tile_size_does_not_change_bits(monkeypatch):
     small = _run_gpu(hosts, "bf16")
     for x, y in zip(big, small):
         assert np.array_equal(x, y)
+
+
+SMALL_CLASS = [(1, 7), (7, 1), (5, 3, 4), (64, 64), (100, 1000), (1000, 100), (128, 129), (129, 128),
+               (128, 128), (96, 700), (33, 4097), (2, 2), (300, 700), (127, 1025)]
+
+
+@pytest.mark.parametrize("dtype,steps,coeffs", [("bf16", 5, QUINTIC), ("bf16", 1, QUINTIC), ("f32", 5, QUINTIC),
+                                                ("f32", 7, CUBIC), ("bf16", 3, (2.0, -1.5, 0.0))])
+def test_small_class_equals_tiled_path(dtype, steps, coeffs, monkeypatch):
+    """Matrices with m <= 128 run in the small size class (one workgroup per
+    matrix, every step in one kernel, padded to 128): the same 128-tile
+    products in the same order as the tiled path, so the same bits, and within
+    the oracle's tolerance. Mixed with tiled matrices in one call."""
+    std = 0.02 if dtype == "bf16" else 1.0
+    hosts = [host_matrix(23, i, s, std=std, dtype=dtype) for i, s in enumerate(SMALL_CLASS)]
+    log(f"ns: small class vs tiled path {dtype} steps={steps} coeffs={coeffs}")
+    monkeypatch.setenv("NS_SMALL_MAX", "0")
+    tiled = _run_gpu(hosts, dtype, steps=steps, coeffs=coeffs)
+    monkeypatch.delenv("NS_SMALL_MAX")
+    small = _run_gpu(hosts, dtype, steps=steps, coeffs=coeffs)
+    _check(hosts, dtype, small, steps=steps, coeffs=coeffs)
+    for s, x, y in zip(SMALL_CLASS, tiled, small):
+        assert np.array_equal(x, y), s
+
+
+def test_small_class_many_random_shapes():
+    """A many-small-style batch (rows and cols log-uniform in [8, 600], most with
+    m <= 128) against the oracle, and bit-identical to the tiled path."""
+    import os
+    rng = np.random.default_rng(29)
+    shapes = [tuple(int(round(np.exp(rng.uniform(np.log(8), np.log(600))))) for _ in range(2)) for _ in range(40)]
+    hosts = [host_matrix(29, i, s) for i, s in enumerate(shapes)]
+    log(f"ns: 40 random small shapes, {sum(min(s) <= 128 for s in shapes)} in the small class")
+    small = _run_gpu(hosts, "bf16")
+    _check(hosts, "bf16", small)
+    os.environ["NS_SMALL_MAX"] = "0"
+    try:
+        tiled = _run_gpu(hosts, "bf16")
+    finally:
+        del os.environ["NS_SMALL_MAX"]
+    for s, x, y in zip(shapes, tiled, small):
+        assert np.array_equal(x, y), s
