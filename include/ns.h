@@ -242,6 +242,34 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                    const int32_t *order, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ns_orthogonalize_batched with no workspace argument. Its scratch is a
+ * 64 MiB array in device memory that the library defines and that every GPU
+ * it runs on holds for the life of the process (one array per GPU, shared by
+ * every call on that GPU).
+ *
+ * ns_noalloc_init: call once per device, with that device current, before
+ * the first ns_orthogonalize_batched_noalloc on it and outside any region
+ * that may not allocate: it looks up the array's device address and reserves
+ * the pinned host staging (8 slots of 1 MiB) that the calls' tables go
+ * through. Calling it again is harmless. Errors: HIP, INVALID_ARG (device
+ * index >= 64, or the staging busy in another thread's call).
+ *
+ * ns_orthogonalize_batched_noalloc: arguments, results and errors as for
+ * ns_orthogonalize_batched (same bits), on the current device's array; it
+ * calls no allocating routine. NS_ERR_WORKSPACE if the largest tensor alone
+ * needs more than 64 MiB of scratch (ns_workspace_bytes' minimum), or if the
+ * call's tables exceed 1 MiB; NS_ERR_INVALID_ARG if ns_noalloc_init was not
+ * called on the device. Larger sets run in groups that fit, with the same
+ * bits. Nothing in the array needs clearing between calls: every byte a call
+ * reads, it writes first. Calls that overlap on one GPU (e.g. on two streams)
+ * share the array and race; keep them in one stream order. */
+ns_status ns_noalloc_init(void);
+ns_status ns_orthogonalize_batched_noalloc(int32_t n, const ns_shape *shapes, const void *const *in,
+                                           void *const *out, ns_dtype dtype, int32_t steps, float a, float b,
+                                           float c, float eps, const int32_t *order, void *stream);
+
 /* ns_orthogonalize_batched on strided views: tensor i's input row r starts
  * at in[i] + r * in_ld[i] elements and its output row at out[i] + r *
  * out_ld[i] (rows as given, i.e. dims[0]; a row holds dims[1] * ... *

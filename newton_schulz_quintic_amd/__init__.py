@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     lib,
     ns_last_error,
     ns_gram_workspace_bytes,
+    ns_noalloc_init,
     ns_orthogonalize_batched,
+    ns_orthogonalize_batched_noalloc,
     ns_orthogonalize_gram,
     ns_orthogonalize_routed,
     ns_orthogonalize_strided,

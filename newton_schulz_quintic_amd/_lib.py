@@ -26,7 +26,8 @@ EXPORTS = [
     "ns_last_error", "ns_version", "ns_plan", "ns_route_plan_create", "ns_route_plan_create_axis",
     "ns_route_plan_query",
     "ns_route_plan_upload", "ns_route_plan_destroy", "ns_pack_shards", "ns_unpack_shards",
-    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_orthogonalize_strided", "ns_routed_workspace_bytes",
+    "ns_workspace_bytes", "ns_orthogonalize_batched", "ns_noalloc_init", "ns_orthogonalize_batched_noalloc",
+    "ns_orthogonalize_strided", "ns_routed_workspace_bytes",
     "ns_orthogonalize_routed", "ns_gram_workspace_bytes", "ns_orthogonalize_gram", "ns_wave_plan", "ns_orthogonalize_waves", "ns_timing_enable",
     "ns_timing_read",
 ]
@@ -63,6 +64,8 @@ _SIGS = {
     "ns_workspace_bytes": (_I32, [_I32, _P, _I32, _P, _P]),
     "ns_orthogonalize_batched": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P,
                                         _SZ, _P]),
+    "ns_noalloc_init": (_I32, []),
+    "ns_orthogonalize_batched_noalloc": (_I32, [_I32, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P, _P]),
     "ns_orthogonalize_strided": (_I32, [_I32, _P, _P, _P, _P, _P, _I32, _I32, _F32, _F32, _F32, _F32, _P,
                                         _P, _SZ, _P]),
     "ns_routed_workspace_bytes": (_I32, [_P, _I32, _P, _P]),
@@ -324,6 +327,36 @@ def ns_orthogonalize_batched(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4
                                           None if ord_arr is None else _addr(ord_arr),
                                           workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return workspace
+
+
+def ns_noalloc_init() -> None:
+    """Set up the no-allocation entry point on the current device (see ns.h)."""
+    _check(lib().ns_noalloc_init())
+
+
+def ns_orthogonalize_batched_noalloc(inputs, outputs, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315),
+                                     eps: float = 1e-7, order=None, stream=None) -> None:
+    """ns_orthogonalize_batched on the library's own scratch array: no workspace,
+    nothing allocated (see ns.h). Tensors: contiguous, one dtype (bf16 or f32)."""
+    n = len(inputs)
+    if len(outputs) != n:
+        raise ValueError("inputs and outputs differ in length")
+    if n == 0:
+        return
+    dtype = _dtype_code(inputs[0])
+    for x, y in zip(inputs, outputs):
+        if _dtype_code(x) != dtype or _dtype_code(y) != dtype:
+            raise TypeError("all tensors must share one dtype")
+        if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+            raise ValueError("tensors must be contiguous and outputs shaped like inputs")
+    a, b, c = coeffs
+    sh = _shapes([tuple(x.shape) for x in inputs])
+    ins = _arr(_P, [x.data_ptr() for x in inputs])
+    outs = _arr(_P, [y.data_ptr() for y in outputs])
+    ord_arr = None if order is None else _arr(_I32, order)
+    _check(lib().ns_orthogonalize_batched_noalloc(n, _addr(sh), _addr(ins), _addr(outs), dtype, steps, float(a),
+                                                  float(b), float(c), float(eps),
+                                                  None if ord_arr is None else _addr(ord_arr), _stream(stream)))
 
 
 def _row_stride(t) -> int:

@@ -45,7 +45,10 @@ void timing_close(int slot, bool ok);
 // a buffer of at least `bytes` (host pointer and the device's pointer to the
 // same memory), fill it, enqueue the kernel that reads it, then release it
 // with that stream so it is reused only after the kernel ends.
-ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr);
+// Without may_grow the call uses only slots already large enough (see
+// staging_reserve) and allocates nothing.
+ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr, bool may_grow = true);
+ns_status staging_reserve(size_t bytes);
 ns_status staging_release(int slot, hipStream_t stream, bool used);
 
 // The launches of one timed step of a call: `work` is what they perform

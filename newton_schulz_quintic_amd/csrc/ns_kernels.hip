@@ -47,6 +47,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -73,6 +74,10 @@ constexpr int kNumXcd = 8;
 // 256 consecutive rows) then spreads over the L2 channels instead of landing
 // on a few of them, as a power-of-two stride makes it do.
 constexpr int kRowPadBytes = 256;
+// The no-allocation entry point: its scratch array (one per GPU) and the most
+// table bytes a call may stage (the pinned staging that ns_noalloc_init makes).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr size_t kNoAllocTableBytes = size_t(1) << 20;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
@@ -1719,7 +1724,8 @@ ns_status plan_call(const std::vector<MatInfo> &info, const PieceLists &pieces, 
 // buffer, then wave by wave (after its ready event, if any) the groups' launches.
 // Only a HIP runtime failure can stop it after the first enqueue.
 ns_status launch_call(CallPlan &plan, ns_dtype dtype, int32_t steps, float a, float b, float c, float eps,
-                      bool gram, float ridge, void *workspace, void *const *ready_events, hipStream_t hs) {
+                      bool gram, float ridge, void *workspace, void *const *ready_events, hipStream_t hs,
+                      bool may_grow = true) {
     if (plan.groups.empty() && !ready_events) return NS_OK;
     size_t total = 0;
     for (GroupPlan &g : plan.groups) {
@@ -1729,7 +1735,7 @@ ns_status launch_call(CallPlan &plan, ns_dtype dtype, int32_t steps, float a, fl
     int slot = -1;
     void *staging = nullptr, *staging_dev = nullptr;
     if (total) {
-        ns_status sst = staging_acquire(total, &slot, &staging, &staging_dev);
+        ns_status sst = staging_acquire(total, &slot, &staging, &staging_dev, may_grow);
         if (sst) return sst;
         for (const GroupPlan &g : plan.groups)
             std::memcpy(static_cast<char *>(staging) + g.staging_off, g.tables.data(), g.tables.size());
@@ -1768,14 +1774,16 @@ ns_status launch_call(CallPlan &plan, ns_dtype dtype, int32_t steps, float a, fl
 // The common path of the entry points: every active tensor's input and output
 // rows are given as row pieces. gram: Gram-space iteration (info described
 // with the Gram workspace).
+// may_grow = false: the table staging must already be large enough (nothing
+// is allocated).
 ns_status orthogonalize(const std::vector<MatInfo> &info, const PieceLists &pieces, ns_dtype dtype,
                         int32_t steps, float a, float b, float c, float eps, const int32_t *order,
                         void *workspace, size_t workspace_bytes, hipStream_t hs, bool gram = false,
-                        float ridge = 0.f) {
+                        float ridge = 0.f, bool may_grow = true) {
     CallPlan plan;
     ns_status st = plan_call(info, pieces, dtype, steps, b, c, order, workspace, workspace_bytes, gram, plan);
     if (st) return st;
-    return launch_call(plan, dtype, steps, a, b, c, eps, gram, ridge, workspace, nullptr, hs);
+    return launch_call(plan, dtype, steps, a, b, c, eps, gram, ridge, workspace, nullptr, hs, may_grow);
 }
 
 ns_status check_coefficients(int32_t steps, float a, float b, float c, float eps) {
@@ -1806,7 +1814,42 @@ ns_status describe_routed(const ns_route_plan *plan, ns_dtype dtype, std::vector
     return NS_OK;
 }
 
+// The checks and row pieces of a batched call (contiguous tensors, one piece
+// each). n == 0 leaves `pieces` empty.
+ns_status batched_args(int32_t n, const ns_shape *shapes, const void *const *in, void *const *out, ns_dtype dtype,
+                       int32_t steps, float a, float b, float c, float eps, std::vector<MatInfo> &info,
+                       PieceLists &pieces) {
+    ns_status st = describe(n, shapes, dtype, info);
+    if (st) return st;
+    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
+    if (n == 0) return NS_OK;
+    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
+    const size_t es = dtype == NS_BF16 ? 2 : 4;
+    pieces.assign(n, {});
+    for (int32_t i = 0; i < n; ++i) {
+        if (!info[i].active) continue;
+        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
+        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
+            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
+        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]),
+                                     info[i].cols, info[i].cols});
+    }
+    return NS_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];   // device address of `scratch`, per device, once set up
+
 }  // namespace
+
+// Scratch for ns_orthogonalize_batched_noalloc: the workspace of callers that
+// cannot allocate. Each GPU the library runs on holds its own copy of this
+// array for the life of the process. In host code its name is only a
+// stand-in: the device address comes from hipGetSymbolAddress, once per
+// device (ns_noalloc_init), and only that address is ever used.
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
 }  // namespace nsq
 
 using namespace nsq;
@@ -1821,6 +1864,49 @@ extern "C" ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dt
     return NS_OK;
 }
 
+extern "C" ns_status ns_noalloc_init(void) {
+    int dev = -1;
+    NSQ_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(NS_ERR_INVALID_ARG, "device %d out of range", dev);
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (!g_scratch_dev[dev]) {
+            void *p = nullptr;
+            NSQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+            if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+                return fail(NS_ERR_HIP, "scratch array address %p is unusable", p);
+            g_scratch_dev[dev] = p;
+        }
+    }
+    return staging_reserve(kNoAllocTableBytes);
+}
+
+extern "C" ns_status ns_orthogonalize_batched_noalloc(int32_t n, const ns_shape *shapes, const void *const *in,
+                                                      void *const *out, ns_dtype dtype, int32_t steps, float a,
+                                                      float b, float c, float eps, const int32_t *order,
+                                                      void *stream) {
+    std::vector<MatInfo> info;
+    PieceLists pieces;
+    ns_status st = batched_args(n, shapes, in, out, dtype, steps, a, b, c, eps, info, pieces);
+    if (st || n == 0) return st;
+    size_t all, need;
+    workspace_need(info, &all, &need);
+    if (need > kNoAllocScratchBytes)
+        return fail(NS_ERR_WORKSPACE,
+                    "the largest tensor needs %zu bytes of scratch; the no-allocation entry point has %zu", need,
+                    kNoAllocScratchBytes);
+    int dev = -1;
+    NSQ_HIP(hipGetDevice(&dev));
+    void *ws = nullptr;
+    if (dev >= 0 && dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        ws = g_scratch_dev[dev];
+    }
+    if (!ws) return fail(NS_ERR_INVALID_ARG, "ns_noalloc_init has not been called on device %d", dev);
+    return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, ws, kNoAllocScratchBytes,
+                         reinterpret_cast<hipStream_t>(stream), false, 0.f, false);
+}
+
 extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                               const void *const *in, void *const *out,
                                               ns_dtype dtype, int32_t steps, float a, float b,
@@ -1828,21 +1914,9 @@ extern "C" ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
                                               void *workspace, size_t workspace_bytes,
                                               void *stream) {
     std::vector<MatInfo> info;
-    ns_status st = describe(n, shapes, dtype, info);
-    if (st) return st;
-    if ((st = check_coefficients(steps, a, b, c, eps))) return st;
-    if (n == 0) return NS_OK;
-    if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out are required");
-    const size_t es = dtype == NS_BF16 ? 2 : 4;
-    PieceLists pieces(n);
-    for (int32_t i = 0; i < n; ++i) {
-        if (!info[i].active) continue;
-        if (!in[i] || !out[i]) return fail(NS_ERR_INVALID_ARG, "tensor %d: NULL in/out", i);
-        if ((reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i])) % es)
-            return fail(NS_ERR_INVALID_ARG, "tensor %d: in/out not %zu-byte aligned", i, es);
-        pieces[i].push_back(RowPiece{0, static_cast<const char *>(in[i]), static_cast<char *>(out[i]),
-                                     info[i].cols, info[i].cols});
-    }
+    PieceLists pieces;
+    ns_status st = batched_args(n, shapes, in, out, dtype, steps, a, b, c, eps, info, pieces);
+    if (st || n == 0) return st;
     return orthogonalize(info, pieces, dtype, steps, a, b, c, eps, order, workspace, workspace_bytes,
                          reinterpret_cast<hipStream_t>(stream));
 }

@@ -34,8 +34,54 @@ bool idle(Slot &s) {
 }
 }  // namespace
 
-ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr) {
+// Makes every slot hold at least `bytes` (allocating pinned memory now), so
+// that later calls whose tables fit never allocate.
+ns_status staging_reserve(size_t bytes) {
     std::lock_guard<std::mutex> lk(g_mu);
+    while (g_slots.size() < kMaxSlots) {
+        g_slots.emplace_back();
+        NSQ_HIP(hipEventCreateWithFlags(&g_slots.back().done, hipEventDisableTiming));
+    }
+    for (Slot &s : g_slots) {
+        if (s.cap >= bytes) continue;
+        if (s.in_use) return fail(NS_ERR_INVALID_ARG, "table staging is in use by another thread's call");
+        if (s.pending) {
+            NSQ_HIP(hipEventSynchronize(s.done));
+            s.pending = false;
+        }
+        if (s.ptr) NSQ_HIP(hipHostFree(s.ptr));
+        s.ptr = s.dev = nullptr;
+        s.cap = 0;
+        NSQ_HIP(hipHostMalloc(&s.ptr, bytes, hipHostMallocDefault));
+        NSQ_HIP(hipHostGetDevicePointer(&s.dev, s.ptr, 0));
+        s.cap = bytes;
+    }
+    return NS_OK;
+}
+
+// Without may_grow, only slots that already hold `bytes` are used (waiting for
+// one to become free if need be) and nothing is allocated.
+ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr, bool may_grow) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!may_grow) {
+        int pick = -1;
+        for (size_t i = 0; i < g_slots.size() && pick < 0; ++i)
+            if (g_slots[i].cap >= bytes && idle(g_slots[i])) pick = (int)i;
+        for (size_t i = 0; i < g_slots.size() && pick < 0; ++i)
+            if (g_slots[i].cap >= bytes && !g_slots[i].in_use) {
+                NSQ_HIP(hipEventSynchronize(g_slots[i].done));
+                g_slots[i].pending = false;
+                pick = (int)i;
+            }
+        if (pick < 0)
+            return fail(NS_ERR_WORKSPACE, "the call's tables take %zu bytes, more than the table staging reserved "
+                        "without allocating (ns_noalloc_init)", bytes);
+        g_slots[pick].in_use = true;
+        *slot = pick;
+        *ptr = g_slots[pick].ptr;
+        *dev_ptr = g_slots[pick].dev;
+        return NS_OK;
+    }
     while (g_slots.size() < kMaxSlots) {
         g_slots.emplace_back();
         Slot &s = g_slots.back();

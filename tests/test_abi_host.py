@@ -393,3 +393,18 @@ def test_errors_come_before_any_enqueue():
     assert batched(1 << 20, minimum, ctypes.addressof(bad)) == -1
     assert batched((1 << 20) + 128, minimum) == -7
     assert batched(1 << 20, minimum - 1) == -7
+
+
+def test_noalloc_errors_before_any_hip_call():
+    # Without a GPU every HIP call fails (NS_ERR_HIP); these return their own
+    # codes first: bad dtype, and a tensor larger than the 64 MiB scratch.
+    lib = nsq.lib()
+    sh = _lib._shapes([(4096, 4096)])
+    ptrs = _lib._arr(ctypes.c_void_p, [4096])
+    call = lambda dtype: lib.ns_orthogonalize_batched_noalloc(  # noqa: E731
+        1, ctypes.addressof(sh), ctypes.addressof(ptrs), ctypes.addressof(ptrs), dtype, 5, 3.4, -4.7, 2.0, 1e-7,
+        None, None)
+    assert call(7) == -8
+    assert call(0) == -7
+    assert "64 MiB" in nsq.ns_last_error() or "scratch" in nsq.ns_last_error()
+    assert lib.ns_orthogonalize_batched_noalloc(0, None, None, None, 0, 5, 3.4, -4.7, 2.0, 1e-7, None, None) == 0
