@@ -221,6 +221,15 @@ ns_status ns_workspace_bytes(int32_t n, const ns_shape *shapes, ns_dtype dtype,
  * by s), so X0 itself is never rounded. f32 tensors keep everything in fp32
  * (f32 MFMA).
  *
+ * Input range: ||G||_F^2, and the entries of G G^T, must be within fp32 range
+ * (||G||_F below about 1.8e19; gradients and momenta are far below it). A
+ * tensor past it, or one holding inf or NaN, comes out as all NaN (never as
+ * silent zeros).
+ *
+ * Size classes: tensors with m <= 128 are padded to 128 and run every step in
+ * one workgroup per tensor; the others are padded to 256 and tiled across the
+ * GPU. Both give the same bits.
+ *
  * in[i], out[i]   device pointers, contiguous row-major, 2-byte (bf16) or
  *                 4-byte (f32) aligned; out[i] may equal in[i]; distinct outputs
  *                 must not overlap. Entries of tensors with numel == 0 or

@@ -78,6 +78,9 @@ constexpr int kRowPadBytes = 256;
 // table bytes a call may stage (the pinned staging that ns_noalloc_init makes).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 constexpr size_t kNoAllocTableBytes = size_t(1) << 20;
+// Tables up to this size are read by the staging workgroups straight from the
+// pinned host staging; larger ones are copied to the workspace first.
+constexpr size_t kTablesFromHostMax = size_t(256) << 10;
 
 // Per-matrix descriptor in device memory.
 struct NsProb {
@@ -698,6 +701,10 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
     const float total = red[0];
     __syncthreads();
     if (total_out) *total_out = total;
+    // A sum of squares past fp32 range (||G||_F above about 1.8e19), or an
+    // input holding inf or NaN, gives a NaN scale: every output element is then
+    // NaN, rather than the zeros a zero scale would give.
+    if (!(total <= 3.402823466e38f)) return __builtin_nanf("");
     return 1.0f / (sqrtf(total) + eps);
 }
 
@@ -991,6 +998,28 @@ __global__ __launch_bounds__(Small::THREADS, 2) void ns_small_kernel(
 // the kernels that follow. TI is the input's element type, T the workspace's
 // (fp32 workspaces of bf16 inputs hold the exact values; the sums of squares
 // come out bit-identical to the bf16 workspace's).
+// The per-call tables, pinned host memory -> the workspace head, for calls
+// whose tables are large (the input-staging kernel then reads them from device
+// memory instead of each workgroup reading its descriptors over the bus).
+__global__ __launch_bounds__(256) void ns_table_copy_kernel(const i32x4 *__restrict__ src, i32x4 *__restrict__ dst,
+                                                           int32_t units) {
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < units; u += gridDim.x * 256) dst[u] = src[u];
+}
+
+// Fixed-order sum over the workgroup (kPrepThreads threads): a butterfly within
+// each wavefront, then the wavefronts' sums in wave order. Ends with a barrier.
+__device__ __forceinline__ float block_sum_fixed(float v, float *red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPrepThreads / 64; ++w) t += red[w];
+    return t;
+}
+
 template <typename TI, typename T = TI>
 __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *__restrict__ probs,
                                                                  const TileRef *__restrict__ tiles, int32_t count,
@@ -1074,14 +1103,8 @@ __global__ __launch_bounds__(kPrepThreads) void ns_prepare_kernel(const NsProb *
         }
     }
     // fixed-order block sum of the squares
-    red[threadIdx.x] = ss;
-    __syncthreads();
-#pragma unroll
-    for (int w = kPrepThreads / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) pr.partials[tr.ti * (pr.np / TE) + tr.tj] = red[0];
+    const float tile_ss = block_sum_fixed(ss, red);
+    if (threadIdx.x == 0) pr.partials[tr.ti * (pr.np / TE) + tr.tj] = tile_ss;
     if (!do_trans) return;
 
     // transpose: output row c (tile column), 16 bytes = ET consecutive tile rows
@@ -1555,10 +1578,23 @@ ns_status launch_group(const GroupPlan &g, int32_t steps, float a, float b, floa
     const int32_t npt = g.nptiles;
     {
         TimedScope ts(kTimeNorm, g.norm_bytes);
-        ts.launch(ns_prepare_kernel<TI, T>, dim3((unsigned)npt), dim3(kPrepThreads), st,
-                  reinterpret_cast<const NsProb *>(hdev), reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()),
-                  npt, reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws),
-                  (int32_t)(g.tables.size() / 16), reinterpret_cast<const RowPiece *>(hdev + tsz.o_pieces()));
+        const int32_t units = (int32_t)(g.tables.size() / 16);
+        auto prep = ns_prepare_kernel<TI, T>;
+        if (g.tables.size() <= kTablesFromHostMax) {
+            // small tables: each staging workgroup reads its descriptors from the
+            // pinned staging and together they copy the tables to the workspace
+            ts.launch(prep, dim3((unsigned)npt), dim3(kPrepThreads), st, reinterpret_cast<const NsProb *>(hdev),
+                      reinterpret_cast<const TileRef *>(hdev + tsz.o_ptiles()), npt,
+                      reinterpret_cast<const i32x4 *>(hdev), reinterpret_cast<i32x4 *>(ws), units,
+                      reinterpret_cast<const RowPiece *>(hdev + tsz.o_pieces()));
+        } else {
+            // large tables: one copy first, then staging reads them from device memory
+            const unsigned cgrid = (unsigned)std::min<int64_t>((units + 1023) / 1024, 2048);
+            ts.launch(ns_table_copy_kernel, dim3(cgrid), dim3(256), st, reinterpret_cast<const i32x4 *>(hdev),
+                      reinterpret_cast<i32x4 *>(ws), units);
+            ts.launch(prep, dim3((unsigned)npt), dim3(kPrepThreads), st, d_probs, d_ptiles, npt,
+                      static_cast<const i32x4 *>(nullptr), static_cast<i32x4 *>(nullptr), 0, d_pieces);
+        }
         NSQ_HIP(hipGetLastError());
         if (steps == 0)
             ts.launch(ns_scale_out_kernel<TI>, dim3((unsigned)npt), dim3(kPrepThreads), st, d_probs, d_ptiles, npt,

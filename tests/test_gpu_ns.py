@@ -269,3 +269,27 @@ def test_small_class_many_random_shapes():
         del os.environ["NS_SMALL_MAX"]
     for s, x, y in zip(shapes, tiled, small):
         assert np.array_equal(x, y), s
+
+
+def test_input_range_large_and_tiny_magnitudes():
+    """Inputs of large magnitude within the documented range (||G||_F^2 and
+    G G^T within fp32) match the oracle; past it, every output is NaN rather
+    than zeros. Scale matters only through eps, so a scaled input gives the
+    scaled-input oracle's result."""
+    import torch
+    base = host_matrix(61, 0, (300, 1024), std=1.0, dtype="f32")
+    ok = [base * np.float32(1e15), base * np.float32(1e-15)]   # ||G|| ~ 5.5e17 and 5.5e-13
+    for h in ok:
+        log(f"ns: f32 300x1024 at scale {float(np.abs(h).max()):.1e}")
+        _check([h], "f32", _run_gpu([h], "f32"))
+    big = [base * np.float32(1e18)]                             # ||G||^2 ~ 3e41: past fp32
+    log("ns: f32 300x1024 past the fp32 range of ||G||^2")
+    out = _run_gpu(big, "f32")[0]
+    assert np.all(np.isnan(out))
+    bf = host_matrix(62, 0, (64, 2048), std=1.0)                # bf16 bits of N(0, 1)
+    big_bf = (bf.astype(np.uint32) + (60 << 7)).astype(np.uint16)   # x 2^60 (exponent + 60): ||G||^2 ~ 1.7e41
+    log("ns: bf16 64x2048 past the fp32 range of ||G||^2")
+    got = _run_gpu([big_bf], "bf16")[0]
+    vals = (got.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(vals))
+    del torch
