@@ -56,6 +56,7 @@ PHASES = {
     "bx_final": ("ns_product_kernel<bf16, X' = B' X, last step writes the output>", "ELi2ELb1E", "mfma"),
     "small": ("ns_small_kernel (every step of the matrices with m <= 128)", "ns_small_kernel", "mfma"),
     "norm": ("ns_prepare_kernel (input staging + norm partials)", "ns_prepare_kernel", "hbm"),
+    "tables": ("ns_table_copy_kernel (large per-call tables to device memory)", "ns_table_copy_kernel", "hbm"),
     "route": ("route_copy_kernel (pack / unpack)", "route_copy_kernel", "hbm"),
 }
 WORKLOADS = ["dense-transformer", "routed-square", "many-small"]
@@ -503,7 +504,7 @@ def main():
     ap.add_argument("--shard-dim", type=int, default=0,
                     help="cut every tensor's shards along this dimension (0 = rows; 1 = the TP stage's "
                          "column shards, evenly over the workload's shard count); pack / unpack routing only")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (at least one run "
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (at least one run "
                     "of each sampled matrix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
