@@ -293,3 +293,29 @@ def test_input_range_large_and_tiny_magnitudes():
     vals = (got.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.isnan(vals))
     del torch
+
+
+def test_side_stream_without_workspace_keeps_its_memory():
+    """A call on a side stream with no workspace given: the library's
+    workspace, dropped by the caller at once, is not handed to new work on
+    the current stream while the call may still run there, and the outputs
+    match the oracle. A spin kernel queued ahead on the side stream keeps the
+    call pending while the same-size allocation is made."""
+    import torch
+    hosts = [host_matrix(71, i, (1024, 1536)) for i in range(3)]
+    ins = [to_device(h, "bf16") for h in hosts]
+    outs = [torch.empty_like(x) for x in ins]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    log("ns: bf16 3 x 1024x1536 on a side stream, workspace dropped")
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50_000_000)   # spin (25 ms to 0.5 s, by the counter's clock) ahead of the call
+    ws = nsq.ns_orthogonalize_batched(ins, outs, stream=side)
+    held, nbytes = ws.data_ptr(), ws.numel()
+    del ws
+    other = torch.empty(nbytes, dtype=torch.uint8, device=ins[0].device)
+    assert other.data_ptr() != held, "a block still in use on the side stream was handed out"
+    other.fill_(0xFF)
+    side.synchronize()
+    torch.cuda.synchronize()
+    _check(hosts, "bf16", [to_host(o, "bf16") for o in outs])
