@@ -137,6 +137,18 @@ def _status(fn, *args):
     return e.value.name
 
 
+def test_workspace_size_limits():
+    """Byte offsets inside one padded matrix are 32-bit: the largest accepted
+    n at m = 256 is the last whose padded X^T (n x (256 + row pad)) stays under
+    2^31 bytes; one element more is refused with NS_ERR_OVERFLOW, wide or tall."""
+    for dtype, es, n_max in ((nsq.NS_BF16, 2, 2796032), (nsq.NS_F32, 4, 1677568)):
+        assert n_max * (256 + 256 // es) * es < 2 ** 31 <= (n_max + 256) * (256 + 256 // es) * es
+        for shape in ((256, n_max), (n_max, 256)):
+            nsq.ns_workspace_bytes([shape], dtype)
+        for shape in ((256, n_max + 1), (n_max + 1, 256)):
+            assert _status(nsq.ns_workspace_bytes, [shape], dtype) == "NS_ERR_OVERFLOW"
+
+
 def test_plan_errors():
     assert _status(nsq.ns_plan, [(4, 5)], 5, 2, [[1, 2]]) == "NS_ERR_SPLIT_SUM"
     assert _status(nsq.ns_plan, [(0, 5)], 5, 2, [[0, 0]]) == "NS_ERR_NO_CANDIDATE"

@@ -100,3 +100,39 @@ def test_long_thin_matrix():
     want = oracle_ns(h, "bf16", 5, QUINTIC, DEFAULT_EPS)
     got = (to_host(y, "bf16").astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert float(np.max(np.abs(got - want))) <= TOL["bf16"]
+
+
+def test_largest_accepted_matrix_structured():
+    """The largest bf16 matrix with m = 256 the size limits accept (n =
+    2,796,032; one more padded tile and the kept X^T would reach 2^31 bytes),
+    wide and tall. Its rows are orthogonal with equal norms (a Sylvester-
+    Hadamard block tiled along n, times seeded column signs), so every singular
+    value of X0 is 1/sqrt(m) and the iteration returns kappa * G with
+    kappa = p^5(1/sqrt(m)) / sqrt(n), p the step polynomial on singular values.
+    kappa * sqrt(n) does not depend on n: it is read off the oracle's output for
+    the same structure at n = 2048. Every output element, times sqrt(n) (the
+    unit scale of the other bf16 parity tests), must be within 2e-2 of it."""
+    import torch
+    from workloads import bf16_bits_to_f32, orthogonal_rows_bits
+    m, n, n_small, seed = 256, 2796032, 2048, 91
+    g_small = orthogonal_rows_bits(m, n_small, seed)
+    want = oracle_ns(g_small, "bf16", 5, QUINTIC, DEFAULT_EPS)
+    ratio = want / bf16_bits_to_f32(g_small).astype(np.float64)
+    assert float(ratio.max() - ratio.min()) <= 1e-12 * float(np.abs(ratio).max())   # kappa * G exactly
+    unit = float(ratio.mean()) * np.sqrt(n_small)
+    big = orthogonal_rows_bits(m, n, seed)
+    x = torch.from_numpy(big.view(np.int16)).view(torch.bfloat16).cuda()
+    del big
+    for tall in (False, True):
+        if tall:
+            x = x.t().contiguous()
+        log(f"large: structured {tuple(x.shape)} bf16, the largest accepted size")
+        y = torch.empty_like(x)
+        nsq.ns_orthogonalize_batched([x], [y], steps=5, coeffs=QUINTIC, eps=DEFAULT_EPS)
+        torch.cuda.synchronize()
+        err = float((y.float() * np.sqrt(n) - unit * x.float()).abs().max())
+        log(f"large: max abs err (sqrt(n) scale) {err:.3e}")
+        assert err <= TOL["bf16"], f"{tuple(x.shape)}: {err}"
+        del y
+    del x
+    torch.cuda.empty_cache()

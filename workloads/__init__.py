@@ -90,6 +90,21 @@ def device_matrix(seed: int, index: int, shape, std: float = 0.02, dtype: str = 
 # row splits over S shard buffers
 # ----------------------------------------------------------------------------
 
+def orthogonal_rows_bits(m: int, n: int, seed: int) -> np.ndarray:
+    """bf16 bits (uint16, m x n) of a +-1 matrix whose rows are orthogonal with
+    equal norms sqrt(n): the m x m Sylvester-Hadamard matrix tiled n / m times
+    along the columns, each column then multiplied by a seeded random sign.
+    m must be a power of two and n a multiple of m."""
+    if m & (m - 1) or n % m:
+        raise ValueError("m must be a power of two and n a multiple of m")
+    h = np.ones((1, 1), dtype=np.int8)
+    while h.shape[0] < m:
+        h = np.block([[h, h], [h, -h]])
+    signs = np.where(np.random.default_rng(seed).integers(0, 2, size=n) > 0, 1, -1).astype(np.int8)
+    neg = (np.tile(h, (1, n // m)) * signs[None, :]) < 0
+    return np.where(neg, np.uint16(0xBF80), np.uint16(0x3F80))   # -1.0 / +1.0 in bf16
+
+
 def even_split_rows(rows: int, num_shards: int) -> list[int]:
     """Split ``rows`` over shards the ``torch.tensor_split`` way: the first
     ``rows % S`` shards get one extra row."""
