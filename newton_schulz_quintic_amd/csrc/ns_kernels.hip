@@ -237,6 +237,9 @@ template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
     static_assert(RPW % RPI == 0, "each wave loads whole row groups");
     static_assert(NBUF >= 2 && NBUF <= 5, "ring depth");
 };
+// Build-time alternatives of the 256-tile configuration, kept for measuring
+// (64-byte panel rows in up to 5 ring buffers, or 4 waves across; all
+// measured slower than these defaults).
 #ifndef NSQ_BIG_ROWB
 #define NSQ_BIG_ROWB 128
 #endif
