@@ -870,7 +870,12 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
         char *D = MODE == kSyrkX ? A : MODE == kSyrkA ? B : MODE == kGemmBX ? xn : MODE == kGramG ? pr.g
                 : MODE == kGramQG ? pr.t : MODE == kGramTQ ? A : MODE == kGramAA ? B : qn;   // B0, BQ: next Q
         const int ldd = MODE == kGemmBX ? ldx : ldt;
-        for (int blk = wave; blk < RowChunks<T, BM>::BLOCKS; blk += C::WAVES) {
+        // Fixed trip counts, unrolled by 4: the LDS reads of four iterations
+        // go out before their stores instead of one read-wait-store at a time.
+        static_assert(RowChunks<T, BM>::BLOCKS % C::WAVES == 0, "whole row blocks per wave");
+#pragma unroll 4
+        for (int it = 0; it < RowChunks<T, BM>::BLOCKS / C::WAVES; ++it) {
+            const int blk = wave + it * C::WAVES;
             int r, c;
             i32x4 w = row_chunk<T, BM>(lds, blk, lane, r, c);
             if (mirror_lower && c < r) {   // elements c .. c + 16/es - 1 of row r; those left of r mirrored
@@ -891,7 +896,10 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
             char *qtn = cur ? pr.qt0 : pr.qt1;
             char *E = MODE == kGemmBX ? xtn : MODE == kGramTQ ? pr.at : MODE == kGramB0 || MODE == kGramBQ ? qtn : D;
             const int lde = MODE == kGemmBX ? ldxt : ldt;
-            for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
+            static_assert(COL_CHUNKS % C::THREADS == 0, "whole column chunks per thread");
+#pragma unroll 4
+            for (int it = 0; it < COL_CHUNKS / C::THREADS; ++it) {
+                const int idx = threadIdx.x + it * C::THREADS;
                 int c, r;
                 const i32x4 w = col_chunk<T, BM>(lds, idx, c, r);
                 store16<T>(E, (int64_t)(col0 + c) * lde + row0 + r, w);
@@ -900,14 +908,20 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
     } else {
         const int m = pr.m, n = pr.n;
         const RowPiece *band = pieces + tr.piece;
+        static_assert(RowChunks<TS, BM>::BLOCKS % C::WAVES == 0 && COL_CHUNKS % C::THREADS == 0,
+                      "whole chunks per wave and thread");
         if (!pr.tall) {   // out is m x n: row-major chunks
-            for (int blk = wave; blk < RowChunks<TS, BM>::BLOCKS; blk += C::WAVES) {
+#pragma unroll 4
+            for (int it = 0; it < RowChunks<TS, BM>::BLOCKS / C::WAVES; ++it) {
+                const int blk = wave + it * C::WAVES;
                 int r, c;
                 const i32x4 w = row_chunk<TS, BM>(lds, blk, lane, r, c);
                 store_chunk_checked<TS>(pr, band, tr.npiece, m, n, row0 + r, col0 + c, w);
             }
         } else {          // out is n x m: column-major chunks
-            for (int idx = threadIdx.x; idx < COL_CHUNKS; idx += C::THREADS) {
+#pragma unroll 4
+            for (int it = 0; it < COL_CHUNKS / C::THREADS; ++it) {
+                const int idx = threadIdx.x + it * C::THREADS;
                 int c, r;
                 const i32x4 w = col_chunk<TS, BM>(lds, idx, c, r);
                 store_chunk_checked<TS>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
