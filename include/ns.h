@@ -261,9 +261,19 @@ ns_status ns_orthogonalize_batched(int32_t n, const ns_shape *shapes,
  * ns_noalloc_init: call once per device, with that device current, before
  * the first ns_orthogonalize_batched_noalloc on it and outside any region
  * that may not allocate: it looks up the array's device address and reserves
- * the pinned host staging (8 slots of 1 MiB) that the calls' tables go
- * through. Calling it again is harmless. Errors: HIP, INVALID_ARG (device
- * index >= 64, or the staging busy in another thread's call).
+ * the pinned host staging the calls' tables go through (8 slots of 1 MiB
+ * for calls in stream order, 8 more for calls under stream capture). Calling
+ * it again is harmless. Errors: HIP, INVALID_ARG (device index >= 64, or the
+ * staging busy in another thread's call).
+ *
+ * Stream capture: a call made while its stream is being captured into a HIP
+ * graph (this entry point or any other NS entry point) copies its tables
+ * into one of the 8 capture slots and keeps that slot for the life of the
+ * process, since every replay of the graph reads them. A ninth captured call
+ * fails with NS_ERR_WORKSPACE, and a captured call before any ns_noalloc_init
+ * with NS_ERR_INVALID_ARG, before anything is captured. Replays run like the
+ * call itself: on the scratch array (or the workspace given), in the order
+ * of the stream they are launched on.
  *
  * ns_orthogonalize_batched_noalloc: arguments, results and errors as for
  * ns_orthogonalize_batched (same bits), on the current device's array; it

@@ -49,6 +49,10 @@ void timing_close(int slot, bool ok);
 // staging_reserve) and allocates nothing.
 ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr, bool may_grow = true);
 ns_status staging_reserve(size_t bytes);
+// Calls under stream capture: slots of `bytes` reserved up front, each taken
+// for good by one captured call (its graph's replays read it).
+ns_status staging_reserve_capture(size_t bytes);
+ns_status staging_acquire_capture(size_t bytes, void **ptr, void **dev_ptr);
 ns_status staging_release(int slot, hipStream_t stream, bool used);
 
 // The launches of one timed step of a call: `work` is what they perform

@@ -1788,7 +1788,13 @@ ns_status launch_call(CallPlan &plan, ns_dtype dtype, int32_t steps, float a, fl
     int slot = -1;
     void *staging = nullptr, *staging_dev = nullptr;
     if (total) {
-        ns_status sst = staging_acquire(total, &slot, &staging, &staging_dev, may_grow);
+        // Under stream capture the tables go to a staging slot kept for good:
+        // the graph's replays read them after this call returns.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        NSQ_HIP(hipStreamIsCapturing(hs, &cap));
+        ns_status sst = cap != hipStreamCaptureStatusNone
+                            ? staging_acquire_capture(total, &staging, &staging_dev)
+                            : staging_acquire(total, &slot, &staging, &staging_dev, may_grow);
         if (sst) return sst;
         for (const GroupPlan &g : plan.groups)
             std::memcpy(static_cast<char *>(staging) + g.staging_off, g.tables.data(), g.tables.size());
@@ -1931,7 +1937,9 @@ extern "C" ns_status ns_noalloc_init(void) {
             g_scratch_dev[dev] = p;
         }
     }
-    return staging_reserve(kNoAllocTableBytes);
+    const ns_status st = staging_reserve(kNoAllocTableBytes);
+    if (st) return st;
+    return staging_reserve_capture(kNoAllocTableBytes);
 }
 
 extern "C" ns_status ns_orthogonalize_batched_noalloc(int32_t n, const ns_shape *shapes, const void *const *in,

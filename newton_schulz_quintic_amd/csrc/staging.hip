@@ -129,6 +129,43 @@ ns_status staging_acquire(size_t bytes, int *slot, void **ptr, void **dev_ptr, b
     return NS_OK;
 }
 
+// Calls made while their stream is being captured into a graph: the graph's
+// replays read the tables from the staging long after the call returns, so
+// such a call takes a slot of its own for the life of the process.
+namespace {
+std::vector<Slot> g_capture;
+size_t g_capture_taken = 0;
+constexpr size_t kCaptureSlots = 8;
+}  // namespace
+
+ns_status staging_reserve_capture(size_t bytes) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    while (g_capture.size() < kCaptureSlots) {
+        Slot s;
+        NSQ_HIP(hipHostMalloc(&s.ptr, bytes, hipHostMallocDefault));
+        NSQ_HIP(hipHostGetDevicePointer(&s.dev, s.ptr, 0));
+        s.cap = bytes;
+        g_capture.push_back(s);
+    }
+    return NS_OK;
+}
+
+ns_status staging_acquire_capture(size_t bytes, void **ptr, void **dev_ptr) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_capture.empty())
+        return fail(NS_ERR_INVALID_ARG, "a call under stream capture needs the staging that ns_noalloc_init reserves");
+    if (g_capture_taken >= g_capture.size())
+        return fail(NS_ERR_WORKSPACE, "all %zu table staging slots for calls under stream capture are taken",
+                    g_capture.size());
+    Slot &s = g_capture[g_capture_taken];
+    if (s.cap < bytes)
+        return fail(NS_ERR_WORKSPACE, "the call's tables take %zu bytes, more than a capture slot's %zu", bytes, s.cap);
+    ++g_capture_taken;
+    *ptr = s.ptr;
+    *dev_ptr = s.dev;
+    return NS_OK;
+}
+
 ns_status staging_release(int slot, hipStream_t stream, bool used) {
     std::lock_guard<std::mutex> lk(g_mu);
     Slot &s = g_slots[slot];
