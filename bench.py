@@ -213,6 +213,41 @@ def alg_phase_flops(ms) -> dict:
     return {"syrk_x": fx, "syrk_a": fa, "bx": fb, "bx_final": fb}
 
 
+def tiling_traffic(ms, phase: str):
+    """HBM bytes per launch of the B'X product if every group of 4 x 8 tiles of
+    256 reads each of its operand panels (256 rows x K, K rounded up to a
+    64-element stage) once and writes its tiles (plus X'^T where it is kept,
+    padded m > 1024; the last launch writes the output itself). The measured
+    FETCH_SIZE + WRITE_SIZE of these launches equal it to 0.1 %: the excess
+    over the algorithmic bytes is panels shared by several groups, not
+    re-reads within one. None outside that configuration (other phases, the
+    small size class, too few tiles for the 256-tile configuration)."""
+    if phase not in ("bx", "bx_final"):
+        return None
+    tile, gr, gc, es = 256, 4, 8, 2
+    reads = writes = tiles = 0
+    for s in ms.shapes:
+        m, n = oriented(s)
+        if m == 0:
+            continue
+        if m <= 128:
+            return None
+        mp, np_ = -(-m // tile) * tile, -(-n // tile) * tile
+        tm, tn = mp // tile, np_ // tile
+        k = -(-m // 64) * 64
+        tiles += tm * tn
+        for bi in range(0, tm, gr):
+            for bj in range(0, tn, gc):
+                reads += (min(gr, tm - bi) + min(gc, tn - bj)) * tile * k * es
+        if phase == "bx":
+            writes += tm * tn * tile * tile * es * (2 if mp > 1024 else 1)
+        else:
+            writes += m * n * es
+    if tiles < 256:
+        return None
+    return reads + writes
+
+
 def alg_flops(m: int, n: int, steps: int, c_nonzero: bool = True) -> float:
     """Algorithmic flops of one matrix: per step SYRK(X) m(m+1)n, SYRK(A) m^2(m+1)
     (skipped when c == 0), GEMM(B X) 2 m^2 n; symmetric products counted once."""
@@ -677,6 +712,7 @@ def main():
         out["roofline"] = {"kernel": name, "phase": dom, "bound": bound, "achieved": round(achieved, 2),
                            "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                            "traffic": stored_traffic(args.workload, dom) if not args.shard_dim else None,
+                           "traffic_model": tiling_traffic(ms, dom) if bound == "mfma" else None,
                            "time_share": round(kms / total_ms, 4), "avg_launch_us": round(kms / kn * 1e3, 2),
                            ("alg_flops_per_launch" if bound == "mfma" else "alg_bytes_per_launch"): kwork / kn,
                            "launches": kn}

@@ -102,3 +102,17 @@ def test_cpu_baseline_sample_is_bounded_and_extrapolated():
     assert r["kind"] == "oracle" and r["unit"] == "matrices/s" and r["cores"] >= 1
     assert r["extrapolated"] and r["value"] > 0
     assert r["sample"].startswith("4 matrices (4 frequent shapes")
+
+
+def test_tiling_traffic_model_hand_values():
+    """The once-per-group panel model on the 16 x 1024^2 set: per matrix one
+    4 x 4 group reads 4 + 4 panels of 256 rows x 1024 (bf16) and writes 16
+    tiles of 256^2 (no X'^T at m = 1024); the last launch writes the output."""
+    import bench
+    from workloads import routed_square_batch, many_small
+    ms = routed_square_batch(True)
+    per_reads = 8 * 256 * 1024 * 2
+    assert bench.tiling_traffic(ms, "bx") == 16 * (per_reads + 16 * 256 * 256 * 2)
+    assert bench.tiling_traffic(ms, "bx_final") == 16 * (per_reads + 1024 * 1024 * 2)
+    assert bench.tiling_traffic(ms, "syrk_x") is None
+    assert bench.tiling_traffic(many_small(), "bx") is None      # small size class present
