@@ -24,7 +24,8 @@
 //                                         writes, as K-major loads are slower)
 //    Panels of 128 bytes of K per row go global -> LDS with buffer_load ... lds
 //    into two stage buffers; every wave loads a slice of both panels.
-//    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups).
+//    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups);
+//    bf16 runs v_mfma_f32_16x16x32_bf16, f32 v_mfma_f32_32x32x2f32.
 //  * The symmetric products compute only tiles on or above the diagonal and
 //    store each off-diagonal tile twice (itself and its mirror), so A and B are
 //    exactly symmetric.
@@ -144,16 +145,28 @@ __device__ __forceinline__ const RowPiece &find_piece(const RowPiece *band, int 
 
 template <typename T> struct Mfma;
 
+// The MFMA of each element type and its lane layouts. A K step is KB bytes of
+// k; operand lane l holds row l % BLK of the block and the 16-byte chunk
+// (KB / 16) kg + l / BLK of K step kg; output lane l holds column l % BLK of
+// the BLK x BLK block and, for q < NQ, rows out_row(l, q) .. + 4.
 template <> struct Mfma<__bf16> {
-    typedef bf16x8 frag;  // 8 consecutive k per lane
-    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    // v_mfma_f32_16x16x32_bf16: 32 k per step, 8 consecutive k per lane
+    typedef bf16x8 frag;
+    typedef f32x4 acc;
+    static constexpr int BLK = 16, KB = 64, NQ = 1;
+    static __device__ __forceinline__ int out_row(int lane, int) { return 4 * (lane >> 4); }
+    static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 
 template <> struct Mfma<float> {
-    typedef f32x4 frag;   // 4 consecutive k per lane, one 32x32x2 MFMA per element
-    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    // v_mfma_f32_32x32x2f32: 8 k per step, 4 consecutive k per lane, one MFMA per element
+    typedef f32x4 frag;
+    typedef f32x16 acc;
+    static constexpr int BLK = 32, KB = 32, NQ = 4;
+    static __device__ __forceinline__ int out_row(int lane, int q) { return 8 * q + 4 * (lane >> 5); }
+    static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
@@ -213,30 +226,39 @@ constexpr bool writes_transpose(int mode) {
 }
 
 // Output tile of BM x BM computed by WM x WN waves; each wave owns a
-// (BM/WM) x (BM/WN) sub-tile made of 32x32 MFMA output blocks (rows
-// wm BM/WM .., column blocks col_blk(wn, 0 ..)). K is staged in
+// (BM/WM) x (BM/WN) sub-tile made of the element type's MFMA output blocks
+// (Geo<T>: rows wm BM/WM .., column blocks col_blk(wn, 0 ..)). K is staged in
 // panels of ROWB bytes per row, in a ring of NBUF stage buffers.
 template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
     static constexpr int BM = BM_, WM = WM_, WN = WN_, ROWB = ROWB_, NBUF = NBUF_;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int NBM = BM / WM / 32;    // 32x32 blocks per wave, row direction
-    static constexpr int NBN = BM / WN / 32;    // ... column direction
     static constexpr int PANEL = BM * ROWB;
     static constexpr int STAGE = 2 * PANEL;     // P panel then Q panel
     static constexpr int RING = NBUF * STAGE;
     static constexpr int RPW = BM / WAVES;      // panel rows each wave loads
     static constexpr int RPI = 1024 / ROWB;     // panel rows per 1 KiB wave load
     static constexpr int LOADS = RPW / RPI;     // loads per wave per panel
-    static constexpr int KG = ROWB / 32;        // k-groups (one 32-byte MFMA K step each) per stage
     static_assert(ROWB == 64 || ROWB == 128, "panel row size");
-    // First tile column of the wave's column block j: the blocks of a wave
-    // are WN apart, so a K stage (64 bf16 columns) holds blocks of several
-    // waves and the A A product's seed work of one stage is spread over them.
-    static __device__ __forceinline__ int col_blk(int wn, int j) { return (j * WN + wn) * 32; }
+    // The wave's MFMA blocks for element type T: NBM x NBN blocks of BLK x BLK,
+    // KG K steps (k-groups) per stage. col_blk(wn, j) is the first tile column
+    // of the wave's column block j: the blocks of a wave are WN apart, so a K
+    // stage (64 bf16 columns) holds blocks of several waves and the A A
+    // product's seed work of one stage is spread over them.
+    template <typename T> struct Geo {
+        static constexpr int BLK = Mfma<T>::BLK;
+        static constexpr int NBM = BM / WM / BLK, NBN = BM / WN / BLK;
+        static constexpr int KG = ROWB / Mfma<T>::KB;
+        static_assert(NBM * BLK * WM == BM && NBN * BLK * WN == BM && KG >= 1, "whole blocks");
+        static __device__ __forceinline__ int col_blk(int wn, int j) { return (j * WN + wn) * BLK; }
+    };
     static_assert(RPW % RPI == 0, "each wave loads whole row groups");
     static_assert(NBUF >= 2 && NBUF <= 5, "ring depth");
 };
+// The accumulators of one wave.
+template <typename T, class C>
+using AccTile = typename Mfma<T>::acc[C::template Geo<T>::NBM][C::template Geo<T>::NBN];
+
 // Build-time alternatives of the 256-tile configuration, kept for measuring
 // (64-byte panel rows in up to 5 ring buffers, or 4 waves across; all
 // measured slower than these defaults).
@@ -255,8 +277,8 @@ typedef TileCfg<128, 2, 2, 128, 2> Small;                     // 4 waves, 64 x 6
 // Operand staging. Each stage holds, per operand, ROWB bytes of K for each of
 // the tile's BM rows. Panel row r sits at r * ROWB bytes; its 16-byte chunk c
 // (8 bf16 / 4 f32 consecutive k) sits in slot c ^ swz(r), which makes the
-// fragment reads (32 consecutive rows, one chunk each) hit distinct banks in
-// every 16 lanes:
+// fragment reads (16 or 32 consecutive rows, one chunk each) hit distinct
+// banks in every 16 lanes:
 //   ROWB = 128: swz(r) = (r >> 1) & 7
 //   ROWB = 64:  swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
 // Global -> LDS uses buffer_load ... lds: lane l's 16 bytes land at M0 + 16 l,
@@ -277,13 +299,13 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 // global loads (the ring keeps later stages in flight across it).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// MFMA operand fragment for the 32-row block starting at panel row `blk`,
-// k-group kg of the stage: lane l gets row blk + l%32, chunk 2 kg + l/32.
+// MFMA operand fragment for the block starting at panel row `blk`, k-group
+// kg of the stage: lane l gets row blk + l % BLK, chunk (KB / 16) kg + l / BLK.
 template <typename T, int ROWB>
 __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *region, int lane, int blk, int kg) {
     typedef typename Mfma<T>::frag frag;
-    const int row = blk + (lane & 31);
-    const int c = 2 * kg + (lane >> 5);
+    const int row = blk + lane % Mfma<T>::BLK;
+    const int c = (Mfma<T>::KB / 16) * kg + lane / Mfma<T>::BLK;
     return *reinterpret_cast<const frag *>(region + row * ROWB + ((c ^ swz<ROWB>(row)) << 4));
 }
 
@@ -291,20 +313,22 @@ __device__ __forceinline__ typename Mfma<T>::frag operand_frag(const char *regio
 // along K, e.g. X for X' = B' X): a stage holds KW = ROWB / es rows of K, each
 // the BM tile columns (BM es bytes). The 16-byte unit u of panel row k sits at
 // unit position u ^ swq(k), which puts the rows read together on distinct
-// banks: bf16 fragments come from LDS transpose reads of four consecutive rows
-// (XOR 4 (k % 4) moves their 64-byte pieces to four bank groups), f32
-// fragments from 4-byte reads of rows k and k + 4 (XOR 8 ((k / 4) % 2)).
+// banks: bf16 fragments come from LDS transpose reads, each 16 lanes reading
+// four consecutive rows and 32 lanes rows k0 .. k0 + 3 and k0 + 8 .. k0 + 11
+// of the same 32 bytes (XOR 4 (k % 4) moves the four rows' pieces to four bank
+// groups, XOR 2 ((k / 8) % 2) the second four rows to the other half of each),
+// f32 fragments from 4-byte reads of rows k and k + 4 (XOR 8 ((k / 4) % 2)).
 template <int ES> __device__ __forceinline__ int swq(int k) {
-    if constexpr (ES == 2) return 4 * (k & 3);
+    if constexpr (ES == 2) return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));
     else return 8 * ((k >> 2) & 1);
 }
 
-// MFMA operand fragment of tile columns blk .. blk + 32, k-group kg, from a
-// K-major panel (RB bytes per row): lane l gets column blk + l % 32 and the
+// MFMA operand fragment of tile columns blk .. blk + BLK, k-group kg, from a
+// K-major panel (RB bytes per row): lane l gets column blk + l % BLK and the
 // fragment's consecutive k. bf16: each 16-lane group g takes columns
-// blk + 16 (g % 2) .. + 16, k from 16 kg + 8 (g / 2), four per transpose read
-// (lane t addresses row k0 + t / 4, columns c0 + 4 (t % 4) .. + 4, and
-// receives column c0 + t of rows k0 .. k0 + 3). f32: k = 8 kg + 4 (l / 32) + e.
+// blk .. blk + 16, k from 32 kg + 8 g, four per transpose read (lane t
+// addresses row k0 + t / 4, columns blk + 4 (t % 4) .. + 4, and receives
+// column blk + t of rows k0 .. k0 + 3). f32: k = 8 kg + 4 (l / 32) + e.
 template <typename T, int RB>
 __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region, int lane, int blk, int kg) {
     constexpr int ES = sizeof(T);
@@ -313,8 +337,9 @@ __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region
         return region + k * RB + ((((byte >> 4) ^ swq<ES>(k))) << 4) + (byte & 15);
     };
     if constexpr (ES == 2) {
+        static_assert(Mfma<T>::BLK == 16 && Mfma<T>::KB == 64, "bf16 fragment layout");
         const int t = lane & 15, g = lane >> 4;
-        const int c0 = blk + 16 * (g & 1), k0 = 16 * kg + 8 * (g >> 1);
+        const int c0 = blk, k0 = 32 * kg + 8 * g;
         s16x4 v[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -336,7 +361,7 @@ __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region
 // multiply-add here, separate rounded multiply and add in the epilogue), so
 // that no tile configuration's instruction choice can change a result bit.
 //
-// acc += s * P[r][k0 + c] for the accumulator blocks whose 32 columns lie in
+// acc += s * P[r][k0 + c] for the accumulator blocks whose columns lie in
 // the P stage `sp` (stage columns k0 .. k0 + KW, KW = ROWB / es), where the
 // tile's column c0 + col_blk(wn, j) maps to stage column
 // col_blk(wn, j) % KW when col_blk(wn, j) / KW == rel. Reads four
@@ -345,8 +370,9 @@ __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region
 // .. + 4, and receives column c0 + t, rows r0 .. r0 + 3), f32 by four 4-byte
 // reads.
 template <typename T, class C>
-__device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s, f32x16 (&acc)[C::NBM][C::NBN]) {
-    constexpr int ES = sizeof(T), ROWB = C::ROWB, KW = ROWB / ES;
+__device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s, AccTile<T, C> &acc) {
+    typedef typename C::template Geo<T> G;
+    constexpr int ES = sizeof(T), ROWB = C::ROWB, KW = ROWB / ES, BLK = G::BLK;
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     auto at = [&](int r, int k) -> const char * {   // byte address of P[r][k] in the stage
@@ -354,25 +380,25 @@ __device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s
         return sp + r * ROWB + ((((byte >> 4) ^ swz<ROWB>(r))) << 4) + (byte & 15);
     };
 #pragma unroll
-    for (int j = 0; j < C::NBN; ++j) {
-        const int cj = C::col_blk(wn, j);
+    for (int j = 0; j < G::NBN; ++j) {
+        const int cj = G::col_blk(wn, j);
         if (cj / KW != rel) continue;
         const int kc = cj % KW;
 #pragma unroll
-        for (int i = 0; i < C::NBM; ++i)
+        for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = wm * (C::BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
+            for (int q = 0; q < Mfma<T>::NQ; ++q) {
+                const int rb = wm * (C::BM / C::WM) + i * BLK + Mfma<T>::out_row(lane, q);
                 float old[4];
                 if constexpr (ES == 2) {
-                    const int t = lane & 15, k0 = kc + 16 * ((lane >> 4) & 1);
+                    const int t = lane & 15, k0 = kc + 16 * ((lane >> 4) & (BLK / 16 - 1));
                     const s16x4 w =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), k0 + 4 * (t & 3)));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, kc + (lane & 31)));
+                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, kc + lane % BLK));
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = __builtin_fmaf(s, old[e], acc[i][j][4 * q + e]);
@@ -390,9 +416,10 @@ __device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s
 // adds its part while such a stage is resident (seed_from_stage).
 template <typename T, class C, bool SEED = false, bool QK = false>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
-                                             int extent_q, int nk, char *lds, f32x16 (&acc)[C::NBM][C::NBN],
+                                             int extent_q, int nk, char *lds, AccTile<T, C> &acc,
                                              int seed_kb = 0, float s_seed = 0.f) {
     typedef typename Mfma<T>::frag frag;
+    typedef typename C::template Geo<T> G;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -463,30 +490,30 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
         if (kb + C::NBUF - 1 < nk) issue(kb + C::NBUF - 1);
         const char *sp = lds + (kb % C::NBUF) * C::STAGE, *sq = sp + C::PANEL;
         // fragments for k-group kg + 1 are read while the MFMAs of kg run
-        frag fa[2][C::NBM], fb[2][C::NBN];
+        frag fa[2][G::NBM], fb[2][G::NBN];
 #pragma unroll
-        for (int i = 0; i < C::NBM; ++i) fa[0][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, 0);
+        for (int i = 0; i < G::NBM; ++i) fa[0][i] = operand_frag<T, ROWB>(sp, lane, a_blk + G::BLK * i, 0);
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j)
-            fb[0][j] = QK ? kmajor_frag<T, RB>(sq, lane, C::col_blk(wn, j), 0)
-                          : operand_frag<T, ROWB>(sq, lane, C::col_blk(wn, j), 0);
+        for (int j = 0; j < G::NBN; ++j)
+            fb[0][j] = QK ? kmajor_frag<T, RB>(sq, lane, G::col_blk(wn, j), 0)
+                          : operand_frag<T, ROWB>(sq, lane, G::col_blk(wn, j), 0);
 #pragma unroll
-        for (int kg = 0; kg < C::KG; ++kg) {
+        for (int kg = 0; kg < G::KG; ++kg) {
             const int cb = kg & 1, nb = cb ^ 1;
-            if (kg + 1 < C::KG) {
+            if (kg + 1 < G::KG) {
 #pragma unroll
-                for (int i = 0; i < C::NBM; ++i)
-                    fa[nb][i] = operand_frag<T, ROWB>(sp, lane, a_blk + 32 * i, kg + 1);
+                for (int i = 0; i < G::NBM; ++i)
+                    fa[nb][i] = operand_frag<T, ROWB>(sp, lane, a_blk + G::BLK * i, kg + 1);
 #pragma unroll
-                for (int j = 0; j < C::NBN; ++j)
-                    fb[nb][j] = QK ? kmajor_frag<T, RB>(sq, lane, C::col_blk(wn, j), kg + 1)
-                                   : operand_frag<T, ROWB>(sq, lane, C::col_blk(wn, j), kg + 1);
+                for (int j = 0; j < G::NBN; ++j)
+                    fb[nb][j] = QK ? kmajor_frag<T, RB>(sq, lane, G::col_blk(wn, j), kg + 1)
+                                   : operand_frag<T, ROWB>(sq, lane, G::col_blk(wn, j), kg + 1);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this k-group's MFMAs
 #pragma unroll
-            for (int i = 0; i < C::NBM; ++i)
+            for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
+                for (int j = 0; j < G::NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
         }
         if constexpr (SEED) {
             const int rel = kb - seed_kb;
@@ -499,9 +526,10 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
 // The rounded tile D (BM x BM, D[r][c]) is staged column-major: LDS row c holds
 // D[0..BM)[c] (BM * es bytes), its 16-byte unit u at unit position
 // u ^ swt(c). swt maps 16 consecutive columns to 16 distinct positions, so the
-// staging writes (32 consecutive columns, 8 or 16 bytes each) spread over the
-// banks, and it maps 4 consecutive columns to positions that differ in bits 1-2,
-// so a transpose read (4 columns x 32 bytes) touches 8 distinct positions.
+// staging writes (16 consecutive columns of bf16, 8 bytes each, or 32 of f32,
+// 16 bytes each) spread over the banks, and it maps 4 consecutive columns to
+// positions that differ in bits 1-2, so a transpose read (4 columns x 32
+// bytes) touches 8 distinct positions.
 __device__ __forceinline__ int swt(int c) { return ((c & 3) << 1) | (((c >> 2) & 1) << 3) | ((c >> 3) & 1); }
 
 template <typename T, int BM>
@@ -614,14 +642,15 @@ __device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowP
         if (col + e < cols) p[col + e] = vals[e];
 }
 
-template <class C>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NBM][C::NBN]) {
+template <typename T, class C>
+__device__ __forceinline__ void zero_acc(AccTile<T, C> &acc) {
+    typedef typename C::template Geo<T> G;
 #pragma unroll
-    for (int i = 0; i < C::NBM; ++i)
+    for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j)
+        for (int j = 0; j < G::NBN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            for (int v = 0; v < 4 * Mfma<T>::NQ; ++v) acc[i][j][v] = 0.f;
 }
 
 // acc = s * M[row0 + r][col0 + c] for this wave's accumulator elements, M
@@ -634,8 +663,9 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[C::NBM][C::NBN]) {
 // for f32 with four 4-byte reads. Ends with a barrier: the LDS is free again.
 template <typename T, class C>
 __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int col0, float s, char *lds,
-                                         f32x16 (&acc)[C::NBM][C::NBN]) {
-    constexpr int ES = sizeof(T), RB = C::BM * ES, RPI = 1024 / RB, NI = C::BM / RPI / C::WAVES;
+                                         AccTile<T, C> &acc) {
+    typedef typename C::template Geo<T> G;
+    constexpr int ES = sizeof(T), RB = C::BM * ES, RPI = 1024 / RB, NI = C::BM / RPI / C::WAVES, BLK = G::BLK;
     static_assert(C::BM % (RPI * C::WAVES) == 0, "whole 1 KiB loads per wave");
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -656,16 +686,16 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
         return lds + r * RB + ((((byte >> 4) ^ (2 * (r & 3)))) << 4) + (byte & 15);
     };
 #pragma unroll
-    for (int i = 0; i < C::NBM; ++i)
+    for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j)
+        for (int j = 0; j < G::NBN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = wm * (C::BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
-                const int cb = C::col_blk(wn, j);
+            for (int q = 0; q < Mfma<T>::NQ; ++q) {
+                const int rb = wm * (C::BM / C::WM) + i * BLK + Mfma<T>::out_row(lane, q);
+                const int cb = G::col_blk(wn, j);
                 float old[4];
                 if constexpr (ES == 2) {
-                    const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & 1);
+                    const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & (BLK / 16 - 1));
                     const s16x4 w =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), c0 + 4 * (t & 3)));
 #pragma unroll
@@ -673,7 +703,7 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
                         old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);   // bf16 -> fp32
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, cb + (lane & 31)));
+                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, cb + lane % BLK));
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = s * old[e];
@@ -775,9 +805,10 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
     constexpr bool kTrim = MODE == kSyrkX || MODE == kSyrkA || MODE == kGemmBX;
     const int nk_n = kTrim ? (pr.n + KW - 1) / KW : np / KW;
     const int nk_m = kTrim ? (pr.m + KW - 1) / KW : mp / KW;
-    f32x16 acc[C::NBM][C::NBN];
+    typedef typename C::template Geo<T> G;
+    AccTile<T, C> acc;
     if constexpr (MODE == kSyrkX || MODE == kGramG) {
-        zero_acc<C>(acc);
+        zero_acc<T, C>(acc);
         const int ld = ldx * ES;
         tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                            nk_n, lds, acc);
@@ -790,7 +821,7 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
         if (do_product) {
             // the old tile S[row0.., col0..] passes through the P stages of
             // columns col0 .. col0 + BM: seed s_init S from there
-            zero_acc<C>(acc);
+            zero_acc<T, C>(acc);
             tile_product<T, C, true>(S + (int64_t)row0 * ld, SQ + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
                                      nk_m, lds, acc, col0 / KW, s_init);
         } else {
@@ -799,7 +830,7 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
     } else if constexpr (MODE == kGemmBX || MODE == kGramOut) {
         // B' X, or Q X0 in the Gram space: X read K-major, as stored, or (B' X
         // with a long K) the rows of the stored X^T
-        zero_acc<C>(acc);
+        zero_acc<T, C>(acc);
         char *P = MODE == kGemmBX ? B : qc;
         const int ldp = ldt * ES;
         if (MODE == kGramOut || pr.kmajor) {
@@ -817,15 +848,16 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
         char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
         char *Q = MODE == kGramQG ? pr.g : qtc;   // G symmetric; else the transposes kept for this
         const int ldp = ldt * ES, ldq = ldt * ES;
-        zero_acc<C>(acc);
+        zero_acc<T, C>(acc);
         tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
                            nk_m, lds, acc);
     }
 
     // Epilogue, part 1: scaling, rounding, staging. Accumulator element
-    // (i, j, v) of this lane sits at tile row wm*BM/WM + 32 i + 8 (v/4) + 4 (lane/32)
-    // + v%4 and tile column col_blk(wn, j) + lane%32. The tile is staged in
-    // the type it is stored in: the workspace type, or the output's.
+    // (i, j, 4 q + e) of this lane sits at tile row wm*BM/WM + BLK i +
+    // out_row(lane, q) + e and tile column col_blk(wn, j) + lane % BLK. The
+    // tile is staged in the type it is stored in: the workspace type, or the
+    // output's.
     typedef typename std::conditional<LAST, TO, T>::type TS;
     constexpr int SES = sizeof(TS);
     constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG || MODE == kGramAA;
@@ -833,13 +865,13 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
     const int wm = wave / C::WN, wn = wave % C::WN;
     __syncthreads();   // every wave is done reading operand panels
 #pragma unroll
-    for (int i = 0; i < C::NBM; ++i) {
+    for (int i = 0; i < G::NBM; ++i) {
 #pragma unroll
-        for (int j = 0; j < C::NBN; ++j) {
-            const int c = C::col_blk(wn, j) + (lane & 31);
+        for (int j = 0; j < G::NBN; ++j) {
+            const int c = G::col_blk(wn, j) + lane % G::BLK;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = wm * (BM / C::WM) + i * 32 + 8 * q + 4 * (lane >> 5);
+            for (int q = 0; q < Mfma<T>::NQ; ++q) {
+                const int r = wm * (BM / C::WM) + i * G::BLK + Mfma<T>::out_row(lane, q);
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
