@@ -242,9 +242,7 @@ template <int BM_, int WM_, int WN_, int ROWB_, int NBUF_> struct TileCfg {
     static_assert(ROWB == 64 || ROWB == 128, "panel row size");
     // The wave's MFMA blocks for element type T: NBM x NBN blocks of BLK x BLK,
     // KG K steps (k-groups) per stage. col_blk(wn, j) is the first tile column
-    // of the wave's column block j: the blocks of a wave are WN apart, so a K
-    // stage (64 bf16 columns) holds blocks of several waves and the A A
-    // product's seed work of one stage is spread over them.
+    // of the wave's column block j: the blocks of a wave are WN apart.
     template <typename T> struct Geo {
         static constexpr int BLK = Mfma<T>::BLK;
         static constexpr int NBM = BM / WM / BLK, NBN = BM / WN / BLK;
@@ -357,67 +355,19 @@ __device__ __forceinline__ typename Mfma<T>::frag kmajor_frag(const char *region
     }
 }
 
-// Rounding is spelled out wherever a product meets a sum (an explicit fused
-// multiply-add here, separate rounded multiply and add in the epilogue), so
-// that no tile configuration's instruction choice can change a result bit.
+// Rounding is spelled out wherever a product meets a sum (an explicit
+// multiply before the accumulation, separate rounded multiply and add in the
+// epilogue), so that no tile configuration's instruction choice can change a
+// result bit.
 //
-// acc += s * P[r][k0 + c] for the accumulator blocks whose columns lie in
-// the P stage `sp` (stage columns k0 .. k0 + KW, KW = ROWB / es), where the
-// tile's column c0 + col_blk(wn, j) maps to stage column
-// col_blk(wn, j) % KW when col_blk(wn, j) / KW == rel. Reads four
-// consecutive rows of one column per lane: bf16 by LDS transpose reads (in
-// each 16-lane group lane t addresses row r0 + t / 4, columns c0 + 4 (t % 4)
-// .. + 4, and receives column c0 + t, rows r0 .. r0 + 3), f32 by four 4-byte
-// reads.
-template <typename T, class C>
-__device__ __forceinline__ void seed_from_stage(const char *sp, int rel, float s, AccTile<T, C> &acc) {
-    typedef typename C::template Geo<T> G;
-    constexpr int ES = sizeof(T), ROWB = C::ROWB, KW = ROWB / ES, BLK = G::BLK;
-    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    auto at = [&](int r, int k) -> const char * {   // byte address of P[r][k] in the stage
-        const int byte = k * ES;
-        return sp + r * ROWB + ((((byte >> 4) ^ swz<ROWB>(r))) << 4) + (byte & 15);
-    };
-#pragma unroll
-    for (int j = 0; j < G::NBN; ++j) {
-        const int cj = G::col_blk(wn, j);
-        if (cj / KW != rel) continue;
-        const int kc = cj % KW;
-#pragma unroll
-        for (int i = 0; i < G::NBM; ++i)
-#pragma unroll
-            for (int q = 0; q < Mfma<T>::NQ; ++q) {
-                const int rb = wm * (C::BM / C::WM) + i * BLK + Mfma<T>::out_row(lane, q);
-                float old[4];
-                if constexpr (ES == 2) {
-                    const int t = lane & 15, k0 = kc + 16 * ((lane >> 4) & (BLK / 16 - 1));
-                    const s16x4 w =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), k0 + 4 * (t & 3)));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, kc + lane % BLK));
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = __builtin_fmaf(s, old[e], acc[i][j][4 * q + e]);
-            }
-    }
-}
-
 // acc += P Q^T over nk stages for one BM x BM tile. P, Q point at the tile's
 // first operand row; ldp, ldq are row strides in bytes; `extent_*` is the byte
 // size the buffer resources may address from P and Q. QK: Q is K-major
 // instead, a row-major matrix with K along its rows (C = P Q): Q points at its
-// row 0, tile column 0, and stage kb reads its rows kb KW .. kb KW + KW. SEED: P holds rows
-// row0 .. row0 + BM of a matrix whose tile at (row0, c0) is to be added, times
-// s_seed; stages seed_kb .. seed_kb + BM / KW carry its columns, and each wave
-// adds its part while such a stage is resident (seed_from_stage).
-template <typename T, class C, bool SEED = false, bool QK = false>
+// row 0, tile column 0, and stage kb reads its rows kb KW .. kb KW + KW.
+template <typename T, class C, bool QK = false>
 __device__ __forceinline__ void tile_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
-                                             int extent_q, int nk, char *lds, AccTile<T, C> &acc,
-                                             int seed_kb = 0, float s_seed = 0.f) {
+                                             int extent_q, int nk, char *lds, AccTile<T, C> &acc) {
     typedef typename Mfma<T>::frag frag;
     typedef typename C::template Geo<T> G;
     const int lane = threadIdx.x & 63;
@@ -514,10 +464,6 @@ __device__ __forceinline__ void tile_product(const char *P, const char *Q, int l
             for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
                 for (int j = 0; j < G::NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[cb][i], fb[cb][j], acc[i][j]);
-        }
-        if constexpr (SEED) {
-            const int rel = kb - seed_kb;
-            if (rel >= 0 && rel < C::BM * (int)sizeof(T) / ROWB) seed_from_stage<T, C>(sp, rel, s_seed, acc);
         }
     }
 }
@@ -655,20 +601,18 @@ __device__ __forceinline__ void zero_acc(AccTile<T, C> &acc) {
 
 // acc = s * M[row0 + r][col0 + c] for this wave's accumulator elements, M
 // row-major with row stride ld bytes. The BM x BM tile of M goes global -> LDS
-// first (coalesced, rows of BM * es bytes, the 16-byte unit u of row r at unit
-// position u ^ 2 (r % 4)); each lane then picks its accumulator layout (four
-// consecutive rows of one column) out of it: for bf16 with LDS transpose reads
-// (in each 16-lane group lane t addresses row r0 + t / 4, columns
-// c0 + 4 (t % 4) .. + 4, and receives rows r0 .. r0 + 3 of column c0 + t),
-// for f32 with four 4-byte reads. Ends with a barrier: the LDS is free again.
+// first (load_init_tile: coalesced, rows of BM * es bytes, the 16-byte unit u
+// of row r at unit position u ^ 2 (r % 4)); each lane then picks its
+// accumulator layout (four consecutive rows of one column) out of it
+// (init_quad): for bf16 with LDS transpose reads (in each 16-lane group lane t
+// addresses row r0 + t / 4, columns c0 + 4 (t % 4) .. + 4, and receives rows
+// r0 .. r0 + 3 of column c0 + t), for f32 with four 4-byte reads. Ends with a
+// barrier: the LDS is free again.
 template <typename T, class C>
-__device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int col0, float s, char *lds,
-                                         AccTile<T, C> &acc) {
-    typedef typename C::template Geo<T> G;
-    constexpr int ES = sizeof(T), RB = C::BM * ES, RPI = 1024 / RB, NI = C::BM / RPI / C::WAVES, BLK = G::BLK;
+__device__ __forceinline__ void load_init_tile(const char *M, int ld, int row0, int col0, char *lds) {
+    constexpr int ES = sizeof(T), RB = C::BM * ES, RPI = 1024 / RB, NI = C::BM / RPI / C::WAVES;
     static_assert(C::BM % (RPI * C::WAVES) == 0, "whole 1 KiB loads per wave");
     const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
     const char *base = M + (int64_t)row0 * ld + (int64_t)col0 * ES;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, C::BM * ld, 0x00020000);
@@ -681,34 +625,67 @@ __device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int co
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (NSQ_LDS void *)(lds + blk * 1024), 16, voff, 0, 0, 0);
     }
     __syncthreads();   // waits for this wave's loads, then for every wave's
+}
+
+// s * the staged tile's rows rb .. rb + 3 of this lane's column: cb + lane %
+// BLK (bf16: cb + 16 ((lane / 16) % (BLK / 16)) + lane % 16).
+template <typename T, int BM, int BLK>
+__device__ __forceinline__ void init_quad(const char *lds, int lane, int rb, int cb, float s, float out[4]) {
+    constexpr int ES = sizeof(T), RB = BM * ES;
     auto at = [&](int r, int c) -> const char * {
         const int byte = c * ES;
         return lds + r * RB + ((((byte >> 4) ^ (2 * (r & 3)))) << 4) + (byte & 15);
     };
+    float old[4];
+    if constexpr (ES == 2) {
+        const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & (BLK / 16 - 1));
+        const s16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), c0 + 4 * (t & 3)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);   // bf16 -> fp32
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, cb + lane % BLK));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = s * old[e];
+}
+
+template <typename T, class C>
+__device__ __forceinline__ void init_acc(const char *M, int ld, int row0, int col0, float s, char *lds,
+                                         AccTile<T, C> &acc) {
+    typedef typename C::template Geo<T> G;
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    load_init_tile<T, C>(M, ld, row0, col0, lds);
 #pragma unroll
     for (int i = 0; i < G::NBM; ++i)
 #pragma unroll
         for (int j = 0; j < G::NBN; ++j)
 #pragma unroll
             for (int q = 0; q < Mfma<T>::NQ; ++q) {
-                const int rb = wm * (C::BM / C::WM) + i * BLK + Mfma<T>::out_row(lane, q);
-                const int cb = G::col_blk(wn, j);
-                float old[4];
-                if constexpr (ES == 2) {
-                    const int t = lane & 15, c0 = cb + 16 * ((lane >> 4) & (BLK / 16 - 1));
-                    const s16x4 w =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSQ_LDS s16x4 *)at(rb + (t >> 2), c0 + 4 * (t & 3)));
+                float v[4];
+                init_quad<T, C::BM, G::BLK>(lds, lane, wm * (C::BM / C::WM) + i * G::BLK + Mfma<T>::out_row(lane, q),
+                                            G::col_blk(wn, j), s, v);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        old[e] = __builtin_bit_cast(float, (uint32_t)(uint16_t)w[e] << 16);   // bf16 -> fp32
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) old[e] = *reinterpret_cast<const float *>(at(rb + e, cb + lane % BLK));
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = s * old[e];
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = v[e];
             }
     __syncthreads();   // every wave is done with the staged tile
+}
+
+// Accumulator values -> the values stored (before rounding to the stored
+// type): times s_final (B X: as they are), plus s_diag on the matrix diagonal
+// (rows < m) for the modes that add one. Element e sits at tile row r + e,
+// tile column c of a tile whose first row is row0; diag_tile: ti == tj.
+template <int MODE>
+__device__ __forceinline__ void finish4(float v[4], float s_final, float s_diag, bool diag_tile, int r, int c,
+                                        int row0, int m) {
+    constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG || MODE == kGramAA;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (MODE != kGemmBX) v[e] = __fmul_rn(s_final, v[e]);
+        if constexpr (kDiag)
+            if (diag_tile && r + e == c && row0 + r + e < m) v[e] = __fadd_rn(v[e], s_diag);
+    }
 }
 
 // The normalisation scale 1 / (||G||_F + eps) of one matrix from its partial
@@ -741,6 +718,27 @@ __device__ __forceinline__ float norm_scale(const float *partials, int nparts, f
     return 1.0f / (sqrtf(total) + eps);
 }
 
+// The first step's products fold the normalisation s = 1 / (||G||_F + eps)
+// into their scales (X0 in the workspace holds G unscaled): A0 = s^2 G G^T,
+// B0' scaled by s, and in the Gram space G = s^2 X0 X0^T (ridge times
+// tr(G) / m on the diagonal) and out = s Q X0. `lds` holds kScaleSlots floats
+// of scratch; ends with a barrier.
+template <int MODE>
+__device__ __forceinline__ void fold_norm(const NsProb &pr, float eps, char *lds, float &s_final, float &s_diag) {
+    float total;
+    const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds), &total);
+    if constexpr (MODE == kSyrkX) s_final = sc * sc;
+    else if constexpr (MODE == kSyrkA) {
+        s_final *= sc;
+        s_diag *= sc;
+    } else if constexpr (MODE == kGramG) {
+        s_final = sc * sc;
+        s_diag *= sc * sc * total / (float)pr.m;   // ridge * tr(G) / m, tr(G) = s^2 ||input||^2
+    } else if constexpr (MODE == kGramOut) {
+        s_final = sc;
+    }
+}
+
 // One product launch: MODE picks the operands and epilogue.
 //   kSyrkX : A = X X^T                          P = X, Q = X     upper tiles, mirrored
 //   kSyrkA : B' = s_final (s_init A + A A^T) + s_diag I
@@ -763,133 +761,26 @@ template <typename T, class C> constexpr int tile_lds_bytes() {
     return C::RING > C::BM * C::BM * (int)sizeof(T) ? C::RING : C::BM * C::BM * (int)sizeof(T);
 }
 
-// One BM x BM tile `tr` of matrix `pr` for the product MODE (see Mode). The
-// caller's workgroup runs it whole; `lds` is tile_lds_bytes() of LDS, free on
-// entry and free again on return.
-template <typename T, class C, int MODE, bool LAST, typename TO = T>
-__device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int32_t cur, float s_init,
-                                         float s_final, float s_diag, int32_t do_product, int32_t first,
-                                         float eps, const RowPiece *__restrict__ pieces, char *lds) {
-    static_assert(!LAST || MODE == kGemmBX || MODE == kGramOut, "only B X or the Gram-space output writes out");
-    static_assert(MODE != kGramOut || LAST, "the Gram-space output launch is a last launch");
-    constexpr int BM = C::BM, ES = sizeof(T);
-    const int mp = pr.mp, np = pr.np;
+// Epilogue, part 2, of one BM x BM tile: writes the tile staged in `lds` (in
+// the type it is stored in: the workspace type, or the output's for the last
+// launch) to its destinations. Every wave of the workgroup calls it after the
+// staging barrier.
+template <typename T, class C, int MODE, bool LAST, typename TO>
+__device__ __forceinline__ void write_staged(const NsProb &pr, const TileRef tr, int32_t cur,
+                                             const RowPiece *__restrict__ pieces, const char *lds) {
+    typedef typename std::conditional<LAST, TO, T>::type TS;
+    constexpr int BM = C::BM, ES = sizeof(T), SES = sizeof(TS);
     const int row0 = tr.ti * BM, col0 = tr.tj * BM;
     const int ldx = pr.ldx, ldxt = pr.ldxt, ldt = pr.ldt;
-    char *xc = cur ? pr.x1 : pr.x0;
     char *xn = cur ? pr.x0 : pr.x1;
-    char *xtc = cur ? pr.xt1 : pr.xt0;
     char *xtn = cur ? pr.xt0 : pr.xt1;
-    char *qc = cur ? pr.q1 : pr.q0;
     char *qn = cur ? pr.q0 : pr.q1;
     char *A = pr.a, *B = pr.b;
-    if (first) {
-        float total;
-        const float sc = norm_scale(pr.partials, pr.nparts, eps, reinterpret_cast<float *>(lds), &total);
-        if constexpr (MODE == kSyrkX) s_final = sc * sc;
-        else if constexpr (MODE == kSyrkA) {
-            s_final *= sc;
-            s_diag *= sc;
-        } else if constexpr (MODE == kGramG) {
-            s_final = sc * sc;
-            s_diag *= sc * sc * total / (float)pr.m;   // ridge * tr(G) / m, tr(G) = s^2 ||input||^2
-        } else if constexpr (MODE == kGramOut) {
-            s_final = sc;
-        }
-    }
-
-    // K stages of the NS products: the K extent (n for X X^T, m for A A and
-    // B' X) rounded up to a whole stage; the zero padding past it adds nothing.
-    // The Gram-space products run over the padded extents.
-    constexpr int KW = C::ROWB / ES;
-    constexpr bool kTrim = MODE == kSyrkX || MODE == kSyrkA || MODE == kGemmBX;
-    const int nk_n = kTrim ? (pr.n + KW - 1) / KW : np / KW;
-    const int nk_m = kTrim ? (pr.m + KW - 1) / KW : mp / KW;
-    typedef typename C::template Geo<T> G;
-    AccTile<T, C> acc;
-    if constexpr (MODE == kSyrkX || MODE == kGramG) {
-        zero_acc<T, C>(acc);
-        const int ld = ldx * ES;
-        tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
-                           nk_n, lds, acc);
-    } else if constexpr (MODE == kSyrkA || MODE == kGramB0 || MODE == kGramAA) {
-        // S S with S symmetric (A, G): the Q operand is S's rows; the general
-        // A A of the Gram space reads A^T's rows instead
-        const int ld = ldt * ES;
-        char *S = MODE == kSyrkA ? A : MODE == kGramB0 ? pr.g : A;
-        char *SQ = MODE == kGramAA ? pr.at : S;
-        if (do_product) {
-            // the old tile S[row0.., col0..] passes through the P stages of
-            // columns col0 .. col0 + BM: seed s_init S from there
-            zero_acc<T, C>(acc);
-            tile_product<T, C, true>(S + (int64_t)row0 * ld, SQ + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
-                                     nk_m, lds, acc, col0 / KW, s_init);
-        } else {
-            init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
-        }
-    } else if constexpr (MODE == kGemmBX || MODE == kGramOut) {
-        // B' X, or Q X0 in the Gram space: X read K-major, as stored, or (B' X
-        // with a long K) the rows of the stored X^T
-        zero_acc<T, C>(acc);
-        char *P = MODE == kGemmBX ? B : qc;
-        const int ldp = ldt * ES;
-        if (MODE == kGramOut || pr.kmajor) {
-            char *X = MODE == kGemmBX ? xc : pr.x0;
-            const int ldq = ldx * ES;
-            tile_product<T, C, false, true>(P + (int64_t)row0 * ldp, X + (int64_t)col0 * ES, ldp, ldq, BM * ldp,
-                                            mp * ldq - col0 * ES, nk_m, lds, acc);
-        } else {
-            const int ldq = ldxt * ES;
-            tile_product<T, C>(P + (int64_t)row0 * ldp, xtc + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
-                               nk_m, lds, acc);
-        }
-    } else {   // the other Gram-space products, all with K = mp
-        char *qtc = cur ? pr.qt1 : pr.qt0;
-        char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
-        char *Q = MODE == kGramQG ? pr.g : qtc;   // G symmetric; else the transposes kept for this
-        const int ldp = ldt * ES, ldq = ldt * ES;
-        zero_acc<T, C>(acc);
-        tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
-                           nk_m, lds, acc);
-    }
-
-    // Epilogue, part 1: scaling, rounding, staging. Accumulator element
-    // (i, j, 4 q + e) of this lane sits at tile row wm*BM/WM + BLK i +
-    // out_row(lane, q) + e and tile column col_blk(wn, j) + lane % BLK. The
-    // tile is staged in the type it is stored in: the workspace type, or the
-    // output's.
-    typedef typename std::conditional<LAST, TO, T>::type TS;
-    constexpr int SES = sizeof(TS);
-    constexpr bool kDiag = MODE == kSyrkA || MODE == kGramB0 || MODE == kGramG || MODE == kGramAA;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    __syncthreads();   // every wave is done reading operand panels
-#pragma unroll
-    for (int i = 0; i < G::NBM; ++i) {
-#pragma unroll
-        for (int j = 0; j < G::NBN; ++j) {
-            const int c = G::col_blk(wn, j) + lane % G::BLK;
-#pragma unroll
-            for (int q = 0; q < Mfma<T>::NQ; ++q) {
-                const int r = wm * (BM / C::WM) + i * G::BLK + Mfma<T>::out_row(lane, q);
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = MODE == kGemmBX ? acc[i][j][4 * q + e] : __fmul_rn(s_final, acc[i][j][4 * q + e]);
-                    if constexpr (kDiag)
-                        if (tr.ti == tr.tj && r + e == c && row0 + r + e < pr.m) v[e] = __fadd_rn(v[e], s_diag);
-                }
-                stage4<TS, BM>(lds, r, c, v);
-            }
-        }
-    }
-    __syncthreads();
-    // A diagonal tile of the seeded A A product writes its lower half from its
-    // upper half, so every element (i, j) carries the value computed at
-    // (min(i, j), max(i, j)) whatever the tile size: computed directly, the
-    // lower half would differ in the last bit, as (b / c) A is added at the
-    // stage of the element's column. (X X^T and G need no such step: their
-    // (i, j) and (j, i) sum the same products in the same order.) Row r's
+    // A diagonal tile of the A A product writes its lower half from its upper
+    // half, so the stored B' is symmetric bit for bit whatever order the
+    // matrix cores sum in (elements (i, j) and (j, i) start from the same
+    // s_init A value and add the same products, in the same k order). Row r's
     // elements left of the diagonal are staged column r's, which the row
     // stores below pick up with one extra 16-byte read per chunk.
     const bool mirror_lower = MODE == kSyrkA && tr.ti == tr.tj;
@@ -962,6 +853,105 @@ __device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int
     }
 }
 
+// One BM x BM tile `tr` of matrix `pr` for the product MODE (see Mode). The
+// caller's workgroup runs it whole; `lds` is tile_lds_bytes() of LDS, free on
+// entry and free again on return.
+template <typename T, class C, int MODE, bool LAST, typename TO = T>
+__device__ __forceinline__ void run_tile(const NsProb &pr, const TileRef tr, int32_t cur, float s_init,
+                                         float s_final, float s_diag, int32_t do_product, int32_t first,
+                                         float eps, const RowPiece *__restrict__ pieces, char *lds) {
+    static_assert(!LAST || MODE == kGemmBX || MODE == kGramOut, "only B X or the Gram-space output writes out");
+    static_assert(MODE != kGramOut || LAST, "the Gram-space output launch is a last launch");
+    constexpr int BM = C::BM, ES = sizeof(T);
+    const int mp = pr.mp, np = pr.np;
+    const int row0 = tr.ti * BM, col0 = tr.tj * BM;
+    const int ldx = pr.ldx, ldxt = pr.ldxt, ldt = pr.ldt;
+    char *xc = cur ? pr.x1 : pr.x0;
+    char *xtc = cur ? pr.xt1 : pr.xt0;
+    char *qc = cur ? pr.q1 : pr.q0;
+    char *A = pr.a, *B = pr.b;
+    if (first) fold_norm<MODE>(pr, eps, lds, s_final, s_diag);
+
+    // K stages of the NS products: the K extent (n for X X^T, m for A A and
+    // B' X) rounded up to a whole stage; the zero padding past it adds nothing.
+    // The Gram-space products run over the padded extents.
+    constexpr int KW = C::ROWB / ES;
+    constexpr bool kTrim = MODE == kSyrkX || MODE == kSyrkA || MODE == kGemmBX;
+    const int nk_n = kTrim ? (pr.n + KW - 1) / KW : np / KW;
+    const int nk_m = kTrim ? (pr.m + KW - 1) / KW : mp / KW;
+    typedef typename C::template Geo<T> G;
+    AccTile<T, C> acc;
+    if constexpr (MODE == kSyrkX || MODE == kGramG) {
+        zero_acc<T, C>(acc);
+        const int ld = ldx * ES;
+        tile_product<T, C>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+                           nk_n, lds, acc);
+    } else if constexpr (MODE == kSyrkA || MODE == kGramB0 || MODE == kGramAA) {
+        // S S with S symmetric (A, G): the Q operand is S's rows; the general
+        // A A of the Gram space reads A^T's rows instead
+        const int ld = ldt * ES;
+        char *S = MODE == kSyrkA ? A : MODE == kGramB0 ? pr.g : A;
+        char *SQ = MODE == kGramAA ? pr.at : S;
+        // the accumulators start at s_init times the old tile S[row0.., col0..]
+        init_acc<T, C>(S, ld, row0, col0, s_init, lds, acc);
+        if (do_product)
+            tile_product<T, C>(S + (int64_t)row0 * ld, SQ + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk_m,
+                               lds, acc);
+    } else if constexpr (MODE == kGemmBX || MODE == kGramOut) {
+        // B' X, or Q X0 in the Gram space: X read K-major, as stored, or (B' X
+        // with a long K) the rows of the stored X^T
+        zero_acc<T, C>(acc);
+        char *P = MODE == kGemmBX ? B : qc;
+        const int ldp = ldt * ES;
+        if (MODE == kGramOut || pr.kmajor) {
+            char *X = MODE == kGemmBX ? xc : pr.x0;
+            const int ldq = ldx * ES;
+            tile_product<T, C, true>(P + (int64_t)row0 * ldp, X + (int64_t)col0 * ES, ldp, ldq, BM * ldp,
+                                            mp * ldq - col0 * ES, nk_m, lds, acc);
+        } else {
+            const int ldq = ldxt * ES;
+            tile_product<T, C>(P + (int64_t)row0 * ldp, xtc + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
+                               nk_m, lds, acc);
+        }
+    } else {   // the other Gram-space products, all with K = mp
+        char *qtc = cur ? pr.qt1 : pr.qt0;
+        char *P = MODE == kGramQG ? qc : MODE == kGramTQ ? pr.t : MODE == kGramBQ ? B : qc;
+        char *Q = MODE == kGramQG ? pr.g : qtc;   // G symmetric; else the transposes kept for this
+        const int ldp = ldt * ES, ldq = ldt * ES;
+        zero_acc<T, C>(acc);
+        tile_product<T, C>(P + (int64_t)row0 * ldp, Q + (int64_t)col0 * ldq, ldp, ldq, BM * ldp, BM * ldq,
+                           nk_m, lds, acc);
+    }
+
+    // Epilogue, part 1: scaling, rounding, staging. Accumulator element
+    // (i, j, 4 q + e) of this lane sits at tile row wm*BM/WM + BLK i +
+    // out_row(lane, q) + e and tile column col_blk(wn, j) + lane % BLK. The
+    // tile is staged in the type it is stored in: the workspace type, or the
+    // output's.
+    typedef typename std::conditional<LAST, TO, T>::type TS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    __syncthreads();   // every wave is done reading operand panels
+#pragma unroll
+    for (int i = 0; i < G::NBM; ++i) {
+#pragma unroll
+        for (int j = 0; j < G::NBN; ++j) {
+            const int c = G::col_blk(wn, j) + lane % G::BLK;
+#pragma unroll
+            for (int q = 0; q < Mfma<T>::NQ; ++q) {
+                const int r = wm * (BM / C::WM) + i * G::BLK + Mfma<T>::out_row(lane, q);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                finish4<MODE>(v, s_final, s_diag, tr.ti == tr.tj, r, c, row0, pr.m);
+                stage4<TS, BM>(lds, r, c, v);
+            }
+        }
+    }
+    __syncthreads();
+    write_staged<T, C, MODE, LAST, TO>(pr, tr, cur, pieces, lds);
+}
+
 // One product launch: every tile of `tiles` (hardware workgroup ids remapped
 // so each XCD takes a contiguous range of the list).
 template <typename T, class C, int MODE, bool LAST, typename TO = T>
@@ -977,6 +967,210 @@ __global__ __launch_bounds__(C::THREADS, C::BM == 256 ? 1 : 2) void ns_product_k
                                    pieces, lds);
 }
 
+
+// --- bf16 256-tiles on four waves, accumulators in fixed registers -----------
+// The bf16 256 x 256 tiles of X X^T, A A and B' X run here by default: four
+// waves of 128 x 128 (one per SIMD), the same two stage buffers filled by
+// direct-to-LDS loads as the 8-wave kernel, and each wave's 8 x 8 blocks of
+// 16 x 16 accumulators held in the AGPRs a0..a255 for the whole tile: every
+// MFMA names its block's registers (acc_pinned.h), because the register
+// allocator, left to itself, moves a tile this size between registers inside
+// the K loop. One K stage is an unrolled schedule (pinned_stage.inc): k-group
+// 0's MFMAs in pairs with k-group 1's fragment reads between them, then
+// k-group 1's pairs with, after the first pair, the wait for the next stage
+// and the barrier, and then the loads two stages ahead and the next stage's
+// first fragment reads. Same MFMA, same k order and the same epilogue
+// arithmetic as the 8-wave kernel, so the two give the same bits.
+#include "acc_pinned.h"
+
+typedef TileCfg<256, 2, 2, 128, 2> Quad;   // 4 waves, 128 x 128 per wave, two 64 KiB stages
+
+// Pinned accumulators += P Q^T over nk >= 1 stages of the 256 tile; operands
+// and QK as in tile_product. Wave (wm, wn) = (wave / 2, wave % 2) owns tile
+// rows wm 128 .. + 128 and columns wn 128 .. + 128; its block q = 8 i + j
+// covers rows wm 128 + 16 i .., columns wn 128 + 16 j ... Load n < 8 of a
+// stage brings rows wave 64 + 8 n .. + 8 of the P panel, load 8 + n the same
+// rows of the Q panel (K-major Q: its k-rows wave 16 + 2 n, + 1, the same LDS
+// bytes).
+template <bool QK>
+__device__ __forceinline__ void pinned_product(const char *P, const char *Q, int ldp, int ldq, int extent_p,
+                                               int extent_q, int nk, char *lds) {
+    typedef Quad C;
+    constexpr int ROWB = C::ROWB, PANEL = C::PANEL, STAGE = C::STAGE;
+    constexpr int KW = ROWB / 2, RB = C::BM * 2;   // K-major: KW k-rows of RB bytes per stage
+    static_assert(C::WAVES == 4 && C::LOADS == 8 && C::RPI == 8, "load layout");
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(P), (short)0, extent_p, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Q), (short)0, extent_q, 0x00020000);
+    int voff_p[8], voff_q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = wave * 64 + 8 * i + (lane >> 3);
+        const int chunk = ((lane & 7) ^ swz<ROWB>(row)) << 4;
+        voff_p[i] = row * ldp + chunk;
+        if constexpr (QK) {
+            const int k = wave * 16 + 2 * i + (lane >> 5);
+            voff_q[i] = k * ldq + (((lane & 31) ^ swq<2>(k)) << 4);
+        } else {
+            voff_q[i] = row * ldq + chunk;
+        }
+    }
+    const int q_stage = QK ? KW * ldq : ROWB;   // byte step of Q per stage
+    auto ld = [&](int n, int kb, int buf) {
+        char *dst = lds + buf * STAGE + (n < 8 ? 0 : PANEL) + (wave * 64 + 8 * (n & 7)) * ROWB;
+        if (n < 8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (NSQ_LDS void *)dst, 16, voff_p[n & 7], kb * ROWB, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (NSQ_LDS void *)dst, 16, voff_q[n & 7], kb * q_stage, 0, 0);
+    };
+    // fragment x < 8: P block x (rows wm 128 + 16 x ..); x >= 8: Q block x - 8
+    const int fsw = swz<ROWB>(lane & 15);
+    const int a_off = (wm * 128 + (lane & 15)) * ROWB, b_off = PANEL + (wn * 128 + (lane & 15)) * ROWB;
+    bf16x8 F[2][16];
+    auto rf = [&](int slot, int buf, int kg, int x) {
+        const char *sb = lds + buf * STAGE;
+        if (QK && x >= 8) {
+            F[slot][x] = kmajor_frag<__bf16, RB>(sb + PANEL, lane, wn * 128 + 16 * (x - 8), kg);
+        } else {
+            const int c = ((4 * kg + (lane >> 4)) ^ fsw) << 4;
+            F[slot][x] = *reinterpret_cast<const bf16x8 *>(
+                sb + (x < 8 ? a_off + 16 * x * ROWB : b_off + 16 * (x - 8) * ROWB) + c);
+        }
+    };
+    // stage 0 landed in buffer 0, stage 1 on its way to buffer 1, stage 0's
+    // first fragments read
+#pragma unroll
+    for (int n = 0; n < 16; ++n) ld(n, 0, 0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (nk > 1) {
+#pragma unroll
+        for (int n = 0; n < 16; ++n) ld(n, 1, 1);
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) rf(0, 0, 0, n < 8 ? 8 + n : n - 8);
+    // Stage kb in buffer PAR = kb % 2. W: a stage kb + 1 exists (wait for it,
+    // barrier, read its first fragments); L: a stage kb + 2 exists (load it
+    // into buffer PAR once every wave is past the barrier).
+    auto stage = [&](auto par, auto w, auto l, int kb) {
+        constexpr int PAR = decltype(par)::value;
+        constexpr bool W = decltype(w)::value, L = decltype(l)::value;
+#include "pinned_stage.inc"
+    };
+    typedef std::integral_constant<int, 0> B0;
+    typedef std::integral_constant<int, 1> B1;
+    typedef std::true_type Y;
+    typedef std::false_type N;
+    int kb = 0;
+    for (; kb + 3 < nk; kb += 2) {
+        stage(B0{}, Y{}, Y{}, kb);
+        stage(B1{}, Y{}, Y{}, kb + 1);
+    }
+    if (nk - kb == 3) {
+        stage(B0{}, Y{}, Y{}, kb);
+        stage(B1{}, Y{}, N{}, kb + 1);
+        stage(B0{}, N{}, N{}, kb + 2);
+    } else if (nk - kb == 2) {
+        stage(B0{}, Y{}, N{}, kb);
+        stage(B1{}, N{}, N{}, kb + 1);
+    } else {
+        stage(B0{}, N{}, N{}, kb);
+    }
+    pinned::drain();
+}
+
+// Pinned accumulators = s * M[row0 + r][col0 + c] (the 256 tile of M, row
+// stride ld bytes), through LDS as in init_acc; ends with a barrier.
+__device__ __forceinline__ void pinned_init(const char *M, int ld, int row0, int col0, float s, char *lds) {
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    load_init_tile<__bf16, Quad>(M, ld, row0, col0, lds);
+    pinned::init_each_block([&](auto qc) -> f32x4 {
+        constexpr int q = decltype(qc)::value;
+        float v[4];
+        init_quad<__bf16, 256, 16>(lds, lane, wm * 128 + 16 * (q >> 3) + 4 * (lane >> 4), wn * 128 + 16 * (q & 7), s,
+                                   v);
+        return f32x4{v[0], v[1], v[2], v[3]};
+    });
+    __syncthreads();
+}
+
+// One 256 x 256 tile for MODE in {kSyrkX, kSyrkA, kGemmBX} on four waves:
+// operands, scales and results as run_tile's. The descriptor comes in as a
+// __restrict__ pointer that every mode reads: inlining then tags each other
+// memory access of the tile, the LDS transpose reads included, as not
+// aliasing it, and with such a tag the compiler does not make an LDS read
+// wait for the direct-to-LDS loads in flight (untagged, a transpose read
+// would wait for the next stage's loads; the schedule's own waits order the
+// stages).
+template <int MODE, bool LAST>
+__device__ __forceinline__ void pinned_tile(const NsProb *__restrict__ prp, const TileRef tr, int32_t cur,
+                                            float s_init, float s_final, float s_diag, int32_t do_product,
+                                            int32_t first, float eps, const RowPiece *__restrict__ pieces,
+                                            char *lds) {
+    static_assert(MODE == kSyrkX || MODE == kSyrkA || MODE == kGemmBX, "NS products only");
+    static_assert(!LAST || MODE == kGemmBX, "only B X writes out");
+    typedef __bf16 T;
+    const NsProb &pr = *prp;
+    constexpr int BM = Quad::BM, ES = 2, KW = Quad::ROWB / ES;
+    const int row0 = tr.ti * BM, col0 = tr.tj * BM;
+    char *xc = cur ? pr.x1 : pr.x0;
+    char *xtc = cur ? pr.xt1 : pr.xt0;
+    if (first) fold_norm<MODE>(pr, eps, lds, s_final, s_diag);
+    const int nk_n = (pr.n + KW - 1) / KW, nk_m = (pr.m + KW - 1) / KW;
+    if constexpr (MODE == kSyrkX) {
+        const int ld = pr.ldx * ES;
+        pinned::zero();
+        pinned_product<false>(xc + (int64_t)row0 * ld, xc + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld, nk_n, lds);
+    } else if constexpr (MODE == kSyrkA) {
+        const int ld = pr.ldt * ES;
+        pinned_init(pr.a, ld, row0, col0, s_init, lds);
+        if (do_product)
+            pinned_product<false>(pr.a + (int64_t)row0 * ld, pr.a + (int64_t)col0 * ld, ld, ld, BM * ld, BM * ld,
+                                  nk_m, lds);
+    } else {
+        const int ldp = pr.ldt * ES;
+        pinned::zero();
+        if (pr.kmajor) {
+            const int ldq = pr.ldx * ES;
+            pinned_product<true>(pr.b + (int64_t)row0 * ldp, xc + (int64_t)col0 * ES, ldp, ldq, BM * ldp,
+                                 pr.mp * ldq - col0 * ES, nk_m, lds);
+        } else {
+            const int ldq = pr.ldxt * ES;
+            pinned_product<false>(pr.b + (int64_t)row0 * ldp, xtc + (int64_t)col0 * ldq, ldp, ldq, BM * ldp,
+                                  BM * ldq, nk_m, lds);
+        }
+    }
+    // Epilogue, part 1: block q = 8 i + j's element e of this lane sits at tile
+    // row wm 128 + 16 i + 4 (lane / 16) + e, column wn 128 + 16 j + lane % 16.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    __syncthreads();   // every wave is done reading operand panels
+    pinned::each_block([&](auto qc, f32x4 a) {
+        constexpr int q = decltype(qc)::value;
+        const int r = wm * 128 + 16 * (q >> 3) + 4 * (lane >> 4), c = wn * 128 + 16 * (q & 7) + (lane & 15);
+        float v[4] = {a[0], a[1], a[2], a[3]};
+        finish4<MODE>(v, s_final, s_diag, tr.ti == tr.tj, r, c, row0, pr.m);
+        stage4<T, BM>(lds, r, c, v);
+    });
+    __syncthreads();
+    write_staged<T, Quad, MODE, LAST, T>(pr, tr, cur, pieces, lds);
+}
+
+template <int MODE, bool LAST>
+__global__ __launch_bounds__(Quad::THREADS, 1) void ns_pinned_kernel(
+    const NsProb *__restrict__ probs, const TileRef *__restrict__ tiles, int32_t ntiles, int32_t cur,
+    float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
+    const RowPiece *__restrict__ pieces) {
+    __shared__ __attribute__((aligned(1024))) char lds[tile_lds_bytes<__bf16, Quad>()];
+    const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
+    if (tile_id >= ntiles) return;
+    const TileRef tr = tiles[tile_id];
+    pinned_tile<MODE, LAST>(probs + tr.prob, tr, cur, s_init, s_final, s_diag, do_product, first, eps, pieces, lds);
+}
 
 // Ends a phase of the small-matrix kernel: every thread's global stores of
 // this phase are complete (release at workgroup scope), the workgroup meets,
@@ -1442,6 +1636,32 @@ void launch_product(TimedScope &ts, dim3 grid, hipStream_t st, const NsProb *pro
                   s_final, s_diag, do_product, first, eps, pieces);
 }
 
+void launch_pinned(TimedScope &ts, dim3 grid, hipStream_t st, const NsProb *probs, const TileRef *tiles,
+                   int32_t nt, int32_t mode, int32_t cur, bool last, float s_init, float s_final, float s_diag,
+                   int32_t do_product, int32_t first, float eps, const RowPiece *pieces) {
+    const dim3 block(Quad::THREADS);
+    if (mode == kSyrkX)
+        ts.launch(ns_pinned_kernel<kSyrkX, false>, grid, block, st, probs, tiles, nt, cur, s_init, s_final, s_diag,
+                  do_product, first, eps, pieces);
+    else if (mode == kSyrkA)
+        ts.launch(ns_pinned_kernel<kSyrkA, false>, grid, block, st, probs, tiles, nt, cur, s_init, s_final, s_diag,
+                  do_product, first, eps, pieces);
+    else if (!last)
+        ts.launch(ns_pinned_kernel<kGemmBX, false>, grid, block, st, probs, tiles, nt, cur, s_init, s_final, s_diag,
+                  do_product, first, eps, pieces);
+    else
+        ts.launch(ns_pinned_kernel<kGemmBX, true>, grid, block, st, probs, tiles, nt, cur, s_init, s_final, s_diag,
+                  do_product, first, eps, pieces);
+}
+
+// The bf16 256-tile products run on the 4-wave kernel with fixed accumulator
+// registers; NS_BIG_WAVES=8 selects the 8-wave kernel instead (measuring;
+// both give the same bits).
+bool big_tiles_pinned() {
+    const char *env = getenv("NS_BIG_WAVES");
+    return !(env && atoi(env) == 8);
+}
+
 template <typename T, class C, int MODE, bool LAST = false, typename TO = T>
 void launch_mode(TimedScope &ts, int32_t nt, hipStream_t st, const NsProb *probs, const TileRef *tiles, int32_t cur,
                  float s_init, float s_final, float s_diag, int32_t do_product, int32_t first, float eps,
@@ -1728,8 +1948,12 @@ ns_status launch_group(const GroupPlan &g, int32_t steps, float a, float b, floa
             const int32_t do_product = mode == kSyrkA ? sa_product : 1;
             if constexpr (sizeof(T) == 2) {
                 if (bm == 256) {
-                    launch_product<T, Big>(ts, dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
-                                           s_diag, do_product, s == 0, eps, d_pieces);
+                    if (big_tiles_pinned())
+                        launch_pinned(ts, dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final, s_diag,
+                                      do_product, s == 0, eps, d_pieces);
+                    else
+                        launch_product<T, Big>(ts, dim3(nt), st, d_probs, d_t, nt, mode, cur, last, s_init, s_final,
+                                               s_diag, do_product, s == 0, eps, d_pieces);
                     continue;
                 }
             }

@@ -229,6 +229,34 @@ def test_tile_size_does_not_change_bits(monkeypatch):
         assert np.array_equal(x, y)
 
 
+BIG_TILE_SHAPES = [(1, 300), (70, 300), (150, 400), (250, 600), (300, 700), (700, 500), (1100, 1300),
+                   (1300, 1100), (512, 1536)]
+
+
+@pytest.mark.parametrize("steps,coeffs", [(5, QUINTIC), (3, (2.0, -1.5, 0.0))])
+def test_big_tile_kernels_give_the_same_bits(steps, coeffs, monkeypatch):
+    """The bf16 256-tiles run on four waves with accumulators in fixed
+    registers, or (NS_BIG_WAVES=8) on eight waves: the same MFMA over the same k
+    order and the same epilogue, so the same bits, equal to the 128-tile path's
+    too. Covers 1, 2, 3, 4 and 5 K stages of A A and B X (m = 1, 70, 150, 250,
+    300 with the small class off), K-major and X^T operands of B X, ragged
+    tails, and c = 0 (B' = a I + b A, no A A product)."""
+    hosts = [host_matrix(31, i, s) for i, s in enumerate(BIG_TILE_SHAPES)]
+    log(f"ns: 4-wave vs 8-wave 256 tiles, steps={steps} coeffs={coeffs}")
+    monkeypatch.setenv("NS_SMALL_MAX", "0")
+    monkeypatch.setenv("NS_TILE", "256")
+    four = _run_gpu(hosts, "bf16", steps=steps, coeffs=coeffs)
+    _check(hosts, "bf16", four, steps=steps, coeffs=coeffs)
+    monkeypatch.setenv("NS_BIG_WAVES", "8")
+    eight = _run_gpu(hosts, "bf16", steps=steps, coeffs=coeffs)
+    monkeypatch.delenv("NS_BIG_WAVES")
+    monkeypatch.setenv("NS_TILE", "128")
+    small = _run_gpu(hosts, "bf16", steps=steps, coeffs=coeffs)
+    for s, x, y, z in zip(BIG_TILE_SHAPES, four, eight, small):
+        assert np.array_equal(x, y), s
+        assert np.array_equal(x, z), s
+
+
 SMALL_CLASS = [(1, 7), (7, 1), (5, 3, 4), (64, 64), (100, 1000), (1000, 100), (128, 129), (129, 128),
                (128, 128), (96, 700), (33, 4097), (2, 2), (300, 700), (127, 1025)]
 
