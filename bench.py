@@ -48,16 +48,23 @@ KERNEL_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "ns_kernels
 ROUTE_SRC = os.path.join(ROOT, "newton_schulz_quintic_amd", "csrc", "route.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 TIMING_KINDS = {0: "bx", 1: "route", 2: "norm", 3: "bx_final", 4: "syrk_x", 5: "syrk_a", 6: "small"}
-# What each timing kind is, and the part of its rocprofv3 kernel name that picks it.
+# What each timing kind is, and the parts of its rocprofv3 kernel names that
+# pick it (rocprofv3 gives some names mangled, some demangled). The bf16
+# 256-tiles run on ns_pinned_kernel<mode, last>, the 128-tiles on
+# ns_product_kernel.
 PHASES = {
-    "syrk_x": ("ns_product_kernel<bf16, A = X X^T, upper tiles>", "ELi0ELb0E", "mfma"),
-    "syrk_a": ("ns_product_kernel<bf16, B' = a I + b A + c A A, upper tiles>", "ELi1ELb0E", "mfma"),
-    "bx": ("ns_product_kernel<bf16, X' = B' X>", "ELi2ELb0E", "mfma"),
-    "bx_final": ("ns_product_kernel<bf16, X' = B' X, last step writes the output>", "ELi2ELb1E", "mfma"),
-    "small": ("ns_small_kernel (every step of the matrices with m <= 128)", "ns_small_kernel", "mfma"),
-    "norm": ("ns_prepare_kernel (input staging + norm partials)", "ns_prepare_kernel", "hbm"),
-    "tables": ("ns_table_copy_kernel (large per-call tables to device memory)", "ns_table_copy_kernel", "hbm"),
-    "route": ("route_copy_kernel (pack / unpack)", "route_copy_kernel", "hbm"),
+    "syrk_x": ("ns_pinned_kernel / ns_product_kernel<bf16, A = X X^T, upper tiles>",
+               ("ELi0ELb0E", "ns_pinned_kernel<0, false>", "ns_pinned_kernelILi0ELb0E"), "mfma"),
+    "syrk_a": ("ns_pinned_kernel / ns_product_kernel<bf16, B' = a I + b A + c A A, upper tiles>",
+               ("ELi1ELb0E", "ns_pinned_kernel<1, false>", "ns_pinned_kernelILi1ELb0E"), "mfma"),
+    "bx": ("ns_pinned_kernel / ns_product_kernel<bf16, X' = B' X>",
+           ("ELi2ELb0E", "ns_pinned_kernel<2, false>", "ns_pinned_kernelILi2ELb0E"), "mfma"),
+    "bx_final": ("ns_pinned_kernel / ns_product_kernel<bf16, X' = B' X, last step writes the output>",
+                 ("ELi2ELb1E", "ns_pinned_kernel<2, true>", "ns_pinned_kernelILi2ELb1E"), "mfma"),
+    "small": ("ns_small_kernel (every step of the matrices with m <= 128)", ("ns_small_kernel",), "mfma"),
+    "norm": ("ns_prepare_kernel (input staging + norm partials)", ("ns_prepare_kernel",), "hbm"),
+    "tables": ("ns_table_copy_kernel (large per-call tables to device memory)", ("ns_table_copy_kernel",), "hbm"),
+    "route": ("route_copy_kernel (pack / unpack)", ("route_copy_kernel",), "hbm"),
 }
 WORKLOADS = ["dense-transformer", "routed-square", "many-small"]
 
@@ -94,8 +101,8 @@ def stored_traffic(workload: str, phase: str):
 
 
 def _phase_of(kernel_name: str):
-    for phase, (_, key, _) in PHASES.items():
-        if key in kernel_name:
+    for phase, (_, keys, _) in PHASES.items():
+        if any(k in kernel_name for k in keys):
             return phase
     return None
 
