@@ -223,8 +223,8 @@ def alg_phase_flops(ms) -> dict:
 def tiling_traffic(ms, phase: str):
     """HBM bytes per launch of the B'X product if every group of 4 x 8 tiles of
     256 reads each of its operand panels (256 rows x K, K rounded up to a
-    64-element stage) once and writes its tiles (plus X'^T where it is kept,
-    padded m > 1024; the last launch writes the output itself). The measured
+    64-element stage) once and writes its tiles (bf16 B'X reads X K-major and
+    keeps no X'^T; the last launch writes the output itself). The measured
     FETCH_SIZE + WRITE_SIZE of these launches equal it to 0.1 %: the excess
     over the algorithmic bytes is panels shared by several groups, not
     re-reads within one. None outside that configuration (other phases, the
@@ -247,7 +247,7 @@ def tiling_traffic(ms, phase: str):
             for bj in range(0, tn, gc):
                 reads += (min(gr, tm - bi) + min(gc, tn - bj)) * tile * k * es
         if phase == "bx":
-            writes += tm * tn * tile * tile * es * (2 if mp > 1024 else 1)
+            writes += tm * tn * tile * tile * es
         else:
             writes += m * n * es
     if tiles < 256:

@@ -1436,12 +1436,15 @@ inline size_t xt_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)
 inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(mi.mp * ld_t(mi, es) * es)); }
 
 // B X reads X K-major (through LDS transpose reads) when its K is at most
-// this: the X'^T stores it saves outweigh its slower operand loads only for
-// short main loops. NS_KMAJOR_MAX overrides (tuning; both ways give the same
-// bits). The Gram-space output product always reads X0 K-major.
-int64_t kmajor_max_k() {
+// this; otherwise it reads the rows of a stored X^T, which the input staging
+// and every B X but the last then write too. bf16 always reads K-major: the
+// 4-wave 256-tile loop hides the transpose reads, and the X^T copies it saves
+// cost more. f32 (four 4-byte reads per fragment) keeps X^T past K = 1024.
+// NS_KMAJOR_MAX overrides (tuning; both ways give the same bits). The
+// Gram-space output product always reads X0 K-major.
+int64_t kmajor_max_k(int64_t es) {
     if (const char *env = getenv("NS_KMAJOR_MAX")) return atoll(env);
-    return 1024;
+    return es == 2 ? INT64_MAX : 1024;
 }
 
 // Largest m of the small size class; NS_SMALL_MAX=0 sends every matrix down
@@ -1459,7 +1462,7 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
     if (dtype != NS_BF16 && dtype != NS_F32) return fail(NS_ERR_DTYPE, "dtype %d", (int)dtype);
     const int64_t es = gram ? 4 : dtype == NS_BF16 ? 2 : 4;   // workspace element size
-    const int64_t kmax = kmajor_max_k();
+    const int64_t kmax = kmajor_max_k(es);
     info.assign(n, MatInfo{});
     for (int32_t i = 0; i < n; ++i) {
         MatInfo &mi = info[i];

@@ -187,7 +187,7 @@ def test_routed_equals_unrouted_bitwise():
         assert np.array_equal(to_host(shards[s], "bf16"), np.concatenate(want))
 
 
-# m > 1024: B X reads the stored X^T (the K-major read is kept for short K)
+# m > 1024: f32 B X reads the stored X^T (K-major only for K <= 1024); bf16 reads X K-major
 LONG_K = [(1100, 1300), (1300, 1100), (300, 700)]
 
 
