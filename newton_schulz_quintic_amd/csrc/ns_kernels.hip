@@ -1437,15 +1437,18 @@ inline size_t a_bytes(const MatInfo &mi, int64_t es) { return align256((size_t)(
 
 // B X reads X K-major (through LDS transpose reads) when its K is at most
 // this; otherwise it reads the rows of a stored X^T, which the input staging
-// and every B X but the last then write too. bf16 always reads K-major: the
-// 4-wave 256-tile loop hides the transpose reads, and the X^T copies it saves
-// cost more. f32 (four 4-byte reads per fragment) keeps X^T past K = 1024.
-// NS_KMAJOR_MAX overrides (tuning; both ways give the same bits). The
-// Gram-space output product always reads X0 K-major.
-int64_t kmajor_max_k(int64_t es) {
+// and every B X but the last then write too. A bf16 call that runs 256-tiles
+// (`big`) reads K-major at every K: the 4-wave pinned loop hides the
+// transpose reads, and the X^T copies cost more than they save. The
+// 128-tile loop and f32 (four 4-byte reads per fragment) keep X^T past
+// K = 1024. NS_KMAJOR_MAX overrides (tuning; both ways give the same bits).
+// The Gram-space output product always reads X0 K-major.
+int64_t kmajor_max_k(bool big) {
     if (const char *env = getenv("NS_KMAJOR_MAX")) return atoll(env);
-    return es == 2 ? INT64_MAX : 1024;
+    return big ? INT64_MAX : 1024;
 }
+
+int pick_tile(const std::vector<int32_t> &group, const std::vector<MatInfo> &info, int64_t es);
 
 // Largest m of the small size class; NS_SMALL_MAX=0 sends every matrix down
 // the tiled path (tests compare the two, which give the same bits).
@@ -1462,7 +1465,6 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
     if (n > 0 && !shapes) return fail(NS_ERR_INVALID_ARG, "shapes is NULL");
     if (dtype != NS_BF16 && dtype != NS_F32) return fail(NS_ERR_DTYPE, "dtype %d", (int)dtype);
     const int64_t es = gram ? 4 : dtype == NS_BF16 ? 2 : 4;   // workspace element size
-    const int64_t kmax = kmajor_max_k(es);
     info.assign(n, MatInfo{});
     for (int32_t i = 0; i < n; ++i) {
         MatInfo &mi = info[i];
@@ -1490,6 +1492,14 @@ ns_status describe(int32_t n, const ns_shape *shapes, ns_dtype dtype, std::vecto
         mi.sq_tiles = gram ? tm * tm : 0;
         mi.nparts = (mi.mp / kPrepTile) * (mi.np / kPrepTile);   // one per staging tile
         mi.npieces = 1;
+    }
+    // B X's operand layout is set per call, from the product tile the whole
+    // call would run (a call split into groups keeps it in every group).
+    std::vector<int32_t> all(n);
+    for (int32_t i = 0; i < n; ++i) all[i] = i;
+    const int64_t kmax = kmajor_max_k(!gram && es == 2 && pick_tile(all, info, es) == 256);
+    for (MatInfo &mi : info) {
+        if (!mi.active) continue;
         mi.kmajor = gram || mi.mp <= kmax;
         mi.buf_bytes = gram ? x_bytes(mi, es) + 9 * a_bytes(mi, es)
                             : 2 * x_bytes(mi, es) + (mi.kmajor ? 0 : 2 * xt_bytes(mi, es)) + 2 * a_bytes(mi, es);
