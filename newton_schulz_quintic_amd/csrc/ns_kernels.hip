@@ -9,23 +9,26 @@
 //
 // Design (one GPU, every matrix of a group in flight at once):
 //  * Workspace per matrix, oriented so m <= n, padded to multiples of 256 in
-//    both dims and kept zero in the padding: X (two copies, ping-pong), for
-//    m > 1024 also X^T (two copies), A and B. Padding removes every bounds
-//    check from the product main loop; zero padding stays zero through every
-//    step (products with zero rows/cols).
+//    both dims and kept zero in the padding: X (two copies, ping-pong), A and
+//    B, and X^T (two copies) where B X reads it (below). Padding removes every
+//    bounds check from the product main loop; zero padding stays zero through
+//    every step (products with zero rows/cols).
 //  * All three products run one MFMA main loop over K panels:
 //        A   = X X^T  : P = Q = X        (C = P Q^T, both read along rows)
 //        A A          : P = Q = A        (A A = A A^T, A symmetric)
-//        B X          : P = B, Q = X     (m <= 1024: C = P Q, Q read K-major,
-//                                         stage kb holds 64 rows of X and the
-//                                         MFMA fragments come from LDS
-//                                         transpose reads; longer K: C = P Q^T
-//                                         with Q = X^T, a copy each step
-//                                         writes, as K-major loads are slower)
+//        B X          : P = B, Q = X     (C = P Q, Q read K-major: stage kb
+//                                         holds 64 rows of X and the MFMA
+//                                         fragments come from LDS transpose
+//                                         reads; f32 and 128-tile calls past
+//                                         K = 1024: C = P Q^T with Q = X^T, a
+//                                         copy each step writes)
 //    Panels of 128 bytes of K per row go global -> LDS with buffer_load ... lds
 //    into two stage buffers; every wave loads a slice of both panels.
-//    Tiles are 256 x 256 with 8 waves (128 x 128 with 4 waves for small groups);
-//    bf16 runs v_mfma_f32_16x16x32_bf16, f32 v_mfma_f32_32x32x2f32.
+//    bf16 256 x 256 tiles run on 4 waves of 128 x 128 whose accumulators stay
+//    in fixed AGPRs under a hand-written stage schedule (ns_pinned_kernel);
+//    128 x 128 tiles (small groups, f32) on 4 waves of 64 x 64
+//    (ns_product_kernel). bf16 runs v_mfma_f32_16x16x32_bf16, f32
+//    v_mfma_f32_32x32x2f32.
 //  * The symmetric products compute only tiles on or above the diagonal and
 //    store each off-diagonal tile twice (itself and its mirror), so A and B are
 //    exactly symmetric.
