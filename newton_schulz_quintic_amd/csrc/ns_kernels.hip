@@ -570,13 +570,12 @@ __device__ __forceinline__ void store16_unaligned(char *p, i32x4 w) {
 }
 
 // Bounds-checked store of the 16 / es elements of chunk w at [row][col] of the
-// caller's output (rows x cols as stored, rows spread over pieces).
+// caller's output (rows x cols as stored), row in piece pc.
 template <typename T>
-__device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowPiece *band, int nband,
-                                                    int64_t rows, int64_t cols, int64_t row, int64_t col, i32x4 w) {
+__device__ __forceinline__ void store_chunk_in_piece(const NsProb &pr, const RowPiece &pc, int64_t rows,
+                                                     int64_t cols, int64_t row, int64_t col, i32x4 w) {
     constexpr int E = 16 / (int)sizeof(T);
     if (row >= rows || col >= cols) return;
-    const RowPiece pc = find_piece(band, nband, row);
     char *dst = pc.out + (row - pc.row0) * pc.ld_out * (int64_t)sizeof(T);
     if (col + E <= cols) {
         if (pr.vec_out) store16<T>(dst, col, w);
@@ -589,6 +588,14 @@ __device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowP
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (col + e < cols) p[col + e] = vals[e];
+}
+
+// The same with the row spread over band[0 .. nband) (rows sorted by row0).
+template <typename T>
+__device__ __forceinline__ void store_chunk_checked(const NsProb &pr, const RowPiece *band, int nband,
+                                                    int64_t rows, int64_t cols, int64_t row, int64_t col, i32x4 w) {
+    if (row >= rows || col >= cols) return;
+    store_chunk_in_piece<T>(pr, find_piece(band, nband, row), rows, cols, row, col, w);
 }
 
 template <typename T, class C>
@@ -836,13 +843,23 @@ __device__ __forceinline__ void write_staged(const NsProb &pr, const TileRef tr,
         const RowPiece *band = pieces + tr.piece;
         static_assert(RowChunks<TS, BM>::BLOCKS % C::WAVES == 0 && COL_CHUNKS % C::THREADS == 0,
                       "whole chunks per wave and thread");
+        // A tile whose output rows lie in one piece (the usual case) reads
+        // that piece once: a descriptor load inside the loop would make each
+        // chunk wait for it, and with it for every store issued before
+        // (the same counter tracks both).
+        const bool one = tr.npiece == 1;
+        const RowPiece pc0 = band[0];
+        auto put = [&](int64_t rows, int64_t cols, int64_t row, int64_t col, i32x4 w) {
+            if (one) store_chunk_in_piece<TS>(pr, pc0, rows, cols, row, col, w);
+            else store_chunk_checked<TS>(pr, band, tr.npiece, rows, cols, row, col, w);
+        };
         if (!pr.tall) {   // out is m x n: row-major chunks
 #pragma unroll 4
             for (int it = 0; it < RowChunks<TS, BM>::BLOCKS / C::WAVES; ++it) {
                 const int blk = wave + it * C::WAVES;
                 int r, c;
                 const i32x4 w = row_chunk<TS, BM>(lds, blk, lane, r, c);
-                store_chunk_checked<TS>(pr, band, tr.npiece, m, n, row0 + r, col0 + c, w);
+                put(m, n, row0 + r, col0 + c, w);
             }
         } else {          // out is n x m: column-major chunks
 #pragma unroll 4
@@ -850,7 +867,7 @@ __device__ __forceinline__ void write_staged(const NsProb &pr, const TileRef tr,
                 const int idx = threadIdx.x + it * C::THREADS;
                 int c, r;
                 const i32x4 w = col_chunk<TS, BM>(lds, idx, c, r);
-                store_chunk_checked<TS>(pr, band, tr.npiece, n, m, col0 + c, row0 + r, w);
+                put(n, m, col0 + c, row0 + r, w);
             }
         }
     }

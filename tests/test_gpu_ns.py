@@ -199,14 +199,17 @@ def test_long_k_parity(dtype):
     _check(hosts, dtype, _run_gpu(hosts, dtype))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_b_x_operand_layout_does_not_change_bits(dtype, monkeypatch):
+@pytest.mark.parametrize("dtype,tile", [("bf16", None), ("bf16", "256"), ("f32", None)])
+def test_b_x_operand_layout_does_not_change_bits(dtype, tile, monkeypatch):
     """B X reads X either K-major (LDS transpose reads) or as the stored X^T's
-    rows: the same products in the same order, so the same bits."""
+    rows: the same products in the same order, so the same bits. tile "256"
+    forces the 4-wave 256-tile kernel, whose calls read K-major by default."""
     std = 0.02 if dtype == "bf16" else 1.0
     shapes = [(1100, 1300), (1300, 1100), (700, 500), (64, 64)]
     hosts = [host_matrix(18, i, s, std=std, dtype=dtype) for i, s in enumerate(shapes)]
-    log(f"ns: K-major vs X^T operand {dtype}")
+    log(f"ns: K-major vs X^T operand {dtype} tile {tile}")
+    if tile:
+        monkeypatch.setenv("NS_TILE", tile)
     monkeypatch.setenv("NS_KMAJOR_MAX", "0")
     stored = _run_gpu(hosts, dtype)
     monkeypatch.setenv("NS_KMAJOR_MAX", "100000")
