@@ -28,6 +28,8 @@
  *                        most 128; 0 sends every matrix down the tiled path)
  *   NS_ROUTE_MAX_GRID=W  cap on pack/unpack workgroups (default 2^23, one
  *                        16 KiB chunk each; a lower cap gives each several)
+ *   NS_STAGE_RUN=R       input-staging tiles per workgroup, 1..16 (default:
+ *                        1, or 4 for calls with 32768 staging tiles and more)
  *
  * Pages cited (by title, then section):
  *   [owner_planning] "core.distributed.fsdp.src.megatron_fsdp.experimental.

@@ -163,6 +163,33 @@ def test_many_pieces_per_tile():
     _compare(shapes, split, 64, "bf16", fulls)
 
 
+def test_staging_run_length_same_bits(monkeypatch):
+    """Routed input staging in runs of several tiles (each run's band of rows
+    may span many pieces) gives the bits of one tile per workgroup."""
+    rng = random.Random(11)
+    shapes = [(700, 300), (300, 900), (64, 2000)]
+    split = []
+    for s in shapes:
+        r = [0] * 16
+        left = s[0]
+        for k in range(16):
+            take = min(left, rng.randint(1, 90)) if k < 15 else left
+            r[k] = take
+            left -= take
+        split.append(r)
+    fulls = [host_matrix(12, i, s) for i, s in enumerate(shapes)]
+    shards_host = _shards(fulls, split, 16, "bf16")
+    plan = _plan(shapes, split, 16, "bf16")
+    log("fused route: staging run lengths 1 and 5")
+    monkeypatch.setenv("NS_STAGE_RUN", "1")
+    one = _fused(plan, shards_host, "bf16")
+    _oracle_check(fulls, split, 16, one, "bf16")
+    monkeypatch.setenv("NS_STAGE_RUN", "5")
+    five = _fused(plan, shards_host, "bf16")
+    for s in range(16):
+        assert np.array_equal(one[s].view(np.uint8), five[s].view(np.uint8)), f"shard {s}"
+
+
 def test_in_place_and_zero_steps():
     shapes, split, fulls, home = _ragged_case(32, 3, "bf16")
     shards_host = _shards(fulls, split, 3, "bf16")

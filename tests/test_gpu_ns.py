@@ -350,3 +350,24 @@ def test_side_stream_without_workspace_keeps_its_memory():
     side.synchronize()
     torch.cuda.synchronize()
     _check(hosts, "bf16", [to_host(o, "bf16") for o in outs])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_staging_run_length_does_not_change_bits(dtype, monkeypatch):
+    """Input staging walks runs of tiles per workgroup (one tile for small calls,
+    several for large ones). Each tile's copy and sum of squares is the same
+    work either way, so the run length must not change a bit: wide, tall, 3-D,
+    ragged edges and a single row, with runs of 1, 3 (ragged run tails) and 16
+    tiles, for 5 steps and for 0 (the scale-out path walks the same runs)."""
+    shapes = [(300, 700), (700, 300), (5, 60, 40), (1, 900), (1024, 1024), (129, 1100)]
+    hosts = [host_matrix(41, i, s, dtype=dtype) for i, s in enumerate(shapes)]
+    log(f"ns: staging run lengths, {dtype}")
+    for steps in (5, 0):
+        monkeypatch.setenv("NS_STAGE_RUN", "1")
+        ref = _run_gpu(hosts, dtype, steps=steps)
+        _check(hosts, dtype, ref, steps=steps)
+        for run in ("3", "16"):
+            monkeypatch.setenv("NS_STAGE_RUN", run)
+            got = _run_gpu(hosts, dtype, steps=steps)
+            for h, x, y in zip(hosts, ref, got):
+                assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{h.shape} run {run} steps {steps}"
