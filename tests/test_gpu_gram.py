@@ -73,3 +73,17 @@ def test_steps_and_cubic(dtype):
     _check(hosts, _gram_gpu(hosts, dtype, steps=7, coeffs=CUBIC), dtype, steps=7, coeffs=CUBIC)
     zero = np.zeros((40, 60), dtype=np.uint16 if dtype == "bf16" else np.float32)
     assert not np.any(_gram_gpu([zero], dtype)[0])
+
+
+def test_staging_run_length_same_bits(monkeypatch):
+    """Gram-space staging widens bf16 inputs to fp32 tile by tile; runs of
+    several tiles per workgroup must give the bits of one tile each."""
+    hosts = [host_matrix(52, i, s) for i, s in enumerate(SHAPES)]
+    log("gram: staging run lengths 1 and 3")
+    monkeypatch.setenv("NS_STAGE_RUN", "1")
+    one = _gram_gpu(hosts, "bf16")
+    _check(hosts, one, "bf16")
+    monkeypatch.setenv("NS_STAGE_RUN", "3")
+    three = _gram_gpu(hosts, "bf16")
+    for h, x, y in zip(hosts, one, three):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{h.shape}"
