@@ -40,9 +40,9 @@
 //    caller's output in the input's orientation, shape and dtype.
 //  * Input staging: the input goes unscaled into X0 (tall inputs transposed
 //    through LDS; X0^T too where it is kept) with per-tile fp32 sums of
-//    squares; the products reduce
-//    those in a fixed order (no atomics) and fold the scale into the first
-//    step's epilogues.
+//    squares, each workgroup taking a run of 128 x 128 tiles along one band of
+//    input rows; the products reduce those sums in a fixed order (no atomics)
+//    and fold the scale into the first step's epilogues.
 //  * Workgroup ids are remapped so consecutive tiles land on the same XCD (the
 //    hardware hands workgroups to the 8 XCDs round-robin), sharing its L2, and
 //    tiles are taken in groups of 4 x 8 so a run of tiles reuses operand panels.
